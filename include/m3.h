@@ -1,0 +1,169 @@
+/*
+ * m3.h -- C ABI of the MI355X (gfx950) Mamba-3 SSM mixer core.
+ *
+ * The library computes the selective state-space recurrence of Mamba-3:
+ *
+ *   B_t[r] = RMSNorm_N(Braw_t[r]) * B_normw + B_bias[h, r]     (same for C)
+ *            -- Mamba-3 paper, §3.4: BC normalisation, then a head-specific,
+ *               channel-wise bias
+ *   alpha_t = exp(dt_t A_t), beta_t = (1 - lam_t) dt_t exp(dt_t A_t),
+ *   gamma_t = lam_t dt_t                      -- §3.1.1, Proposition 1
+ *   H_t = R_t (alpha_t H_{t-1} + beta_t sum_r B_{t-1}[r] X_{t-1}[r]^T)
+ *         + gamma_t sum_r B_t[r] X_t[r]^T     -- App. B.3 eq. 25 (real form of the
+ *                                               complex exponential-trapezoidal SSM),
+ *                                               rank-R input of App. C
+ *   y_t[r] = H_t^T C_t[r]                     -- App. C, Y_t = H_t^T C_t
+ *
+ * where R_t rotates every state coordinate pair (i, i + N/2), i < N/2, by the
+ * angle dt_t * theta_t[i] (counter-clockwise: [[cos, -sin], [sin, cos]]; §3.2.1,
+ * Proposition 2, with the state stacked as [real half; imaginary half]). The
+ * prefill evaluates this with the chunked algorithm of §3.3 and the rotary
+ * "RoPE trick" of §3.2.2 (Proposition 4); decode applies one step directly.
+ *
+ * Tensor layouts are dense, row-major, contiguous; b = batch, L = seqlen,
+ * H = nheads, G = ngroups (head h uses group h / (H/G)), P = headdim,
+ * N = dstate, R = rank (1 = SISO):
+ *   x, x-like outputs    [b, L, H, R, P]   io dtype (fp32 or bf16)
+ *   Braw, Craw           [b, L, G, R, N]   io dtype (raw projections, before BCNorm)
+ *   dt, A, lam           [b, L, H]         fp32 (dt > 0 after softplus, A < 0,
+ *                                                lam in [0, 1] after sigmoid)
+ *   theta                [b, L, G, N/2]    fp32 (rotation frequencies; angle = dt*theta)
+ *   B_bias, C_bias       [H, R, N]         fp32
+ *   B_normw, C_normw     [N]               fp32, optional (NULL = ones)
+ *   state h              [b, H, P, N]      fp32 (physical frame)
+ *   x_prev               [b, H, R, P]      io dtype, Braw_prev [b, G, R, N] io dtype
+ *
+ * Ownership: the caller owns every buffer, including the workspace. The library
+ * keeps no state between calls, never allocates, frees or synchronises, and
+ * enqueues its kernels on the caller's stream (a hipStream_t passed as void*;
+ * NULL = the default stream). It is re-entrant.
+ *
+ * Errors: every argument is checked on the host before any HIP call; a failed
+ * check returns a negative status and enqueues nothing. M3_ERR_HIP means a
+ * kernel launch was rejected by the runtime. Faults inside a kernel surface at
+ * the caller's next synchronisation, as HIP errors. No C++ exception crosses
+ * this interface. All device pointers must be 16-byte aligned.
+ */
+#ifndef M3_H
+#define M3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    M3_OK = 0,
+    M3_ERR_INVALID_ARG = -1,         /* NULL where a tensor is required, bad sizes */
+    M3_ERR_UNSUPPORTED = -2,         /* valid shape that no kernel here handles */
+    M3_ERR_MISALIGNED = -3,          /* a device pointer is not 16-byte aligned */
+    M3_ERR_WORKSPACE_TOO_SMALL = -4, /* ws_bytes < m3_scan_workspace_bytes(shape) */
+    M3_ERR_HIP = -5                  /* the HIP runtime rejected a launch */
+} m3_status;
+
+typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
+
+/* flags */
+#define M3_FLAG_FORCE_GENERIC 1u /* use the fp32 vector-ALU chunked kernel even where
+                                    the bf16 matrix-core kernel applies */
+
+typedef struct {
+    int64_t batch;     /* b >= 0 */
+    int64_t seqlen;    /* L >= 0 (decode: ignored) */
+    int64_t nheads;    /* H >= 1 */
+    int64_t ngroups;   /* G >= 1, H % G == 0 */
+    int64_t headdim;   /* P */
+    int64_t dstate;    /* N, even */
+    int64_t rank;      /* R >= 1 */
+    int64_t chunk;     /* tokens per chunk (prefill). The matrix-core kernel needs
+                          chunk * rank == 64 (the pages' rule: 64 / mimo_rank) */
+    int32_t io_dtype;  /* m3_dtype of x, Braw, Craw, x_prev, Braw_prev, y */
+    uint32_t flags;    /* M3_FLAG_* */
+    float eps;         /* BCNorm epsilon (added to the mean square) */
+    int32_t nsegments; /* prefill sequence split: 0 = automatic, 1 = none,
+                          k > 1 = split every sequence into k segments whose end
+                          states are combined in a second pass (state passing) */
+} m3_shape;
+
+/* Prefill (chunked scan) arguments. */
+typedef struct {
+    const void *x;         /* [b,L,H,R,P] io */
+    const void *Braw;      /* [b,L,G,R,N] io */
+    const void *Craw;      /* [b,L,G,R,N] io */
+    const float *dt;       /* [b,L,H] */
+    const float *A;        /* [b,L,H] */
+    const float *lam;      /* [b,L,H] */
+    const float *theta;    /* [b,L,G,N/2] */
+    const float *B_bias;   /* [H,R,N] */
+    const float *C_bias;   /* [H,R,N] */
+    const float *B_normw;  /* [N] or NULL */
+    const float *C_normw;  /* [N] or NULL */
+    const float *h0;       /* [b,H,P,N] initial state or NULL (zero) */
+    const void *x_prev;    /* [b,H,R,P] io: token before position 0, or NULL */
+    const void *Braw_prev; /* [b,G,R,N] io: its raw B, or NULL. Both or neither:
+                              with them, position 0 gets the beta term of the
+                              trapezoid; without, it has none (§3.1.3 unrolling
+                              starts from h_0 = gamma_0 B_0 x_0) */
+    void *y;               /* out [b,L,H,R,P] io */
+    float *h_final;        /* out [b,H,P,N] state after position L-1, or NULL */
+} m3_scan_io;
+
+/* Decode (single token) arguments: the per-token tensors have no L axis. */
+typedef struct {
+    const void *x;         /* [b,H,R,P] io */
+    const void *Braw;      /* [b,G,R,N] io */
+    const void *Craw;      /* [b,G,R,N] io */
+    const float *dt;       /* [b,H] */
+    const float *A;        /* [b,H] */
+    const float *lam;      /* [b,H] */
+    const float *theta;    /* [b,G,N/2] */
+    const float *B_bias;   /* [H,R,N] */
+    const float *C_bias;   /* [H,R,N] */
+    const float *B_normw;  /* [N] or NULL */
+    const float *C_normw;  /* [N] or NULL */
+    const void *x_prev;    /* [b,H,R,P] io, previous token, or NULL (first token) */
+    const void *Braw_prev; /* [b,G,R,N] io, or NULL; both or neither */
+    float *h;              /* in/out [b,H,P,N] state, updated in place */
+    void *y;               /* out [b,H,R,P] io */
+} m3_decode_io;
+
+/* What m3_scan_fwd will launch for a shape (for logs and tests). */
+typedef struct {
+    int32_t kernel;         /* 0 = fp32 vector-ALU chunked kernel, 1 = bf16 matrix-core kernel */
+    int32_t nsegments;      /* segments per sequence (1 = single pass) */
+    int64_t workgroups;     /* workgroups of the main (output) pass */
+    size_t workspace_bytes; /* bytes of caller workspace required */
+} m3_plan;
+
+/* Chunked-scan prefill: y for every position and the final state.
+ * Chunked algorithm of §3.3 (quadratic masked form inside a chunk, §3.1.3 eq. 7
+ * mask; linear state passing between chunks) on B and C rotated by the
+ * cumulative angle (§3.2.2, Proposition 4). Returns M3_OK or a negative status.
+ * workspace may be NULL when m3_scan_workspace_bytes returns 0. */
+m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspace,
+                      size_t ws_bytes, void *stream);
+
+/* Bytes of device workspace m3_scan_fwd needs for this shape (0 if none). */
+size_t m3_scan_workspace_bytes(const m3_shape *shape);
+
+/* Fill *plan with what m3_scan_fwd would launch; validates like m3_scan_fwd
+ * (without the pointer checks). */
+m3_status m3_scan_plan(const m3_shape *shape, m3_plan *plan);
+
+/* One decode step in place: h <- R_t(alpha h + beta B_prev x_prev^T) + gamma B x^T,
+ * y = h^T C (App. B.3 eq. 25 with App. C's rank-R form). Decode requires
+ * N in {16, 32, 64, 128, 256}, P <= 256, R <= 4. */
+m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *m3_status_str(m3_status status);
+
+/* Library ABI version (major * 100 + minor). */
+int m3_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* M3_H */

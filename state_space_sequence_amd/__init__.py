@@ -2,16 +2,10 @@
 
 The compute path is a C-ABI shared library of hand-written HIP kernels for
 gfx950 (``libm3.so``, declared in ``include/m3.h``). ``state_space_sequence_amd.m3``
-is the thin Python binding over it (argument marshalling only); the library is
-loaded on first use and its absence is an error, never a fallback.
+is the thin Python binding over it (argument marshalling only); importing it
+loads the library, and a missing library is an error, never a fallback.
+``state_space_sequence_amd.inputs`` draws the seeded synthetic inputs.
 """
-from . import inputs  # noqa: F401  (seeded synthetic inputs; no method arithmetic)
+from . import inputs  # noqa: F401
 
-__all__ = ["inputs", "m3"]
-
-
-def __getattr__(name):
-    if name == "m3":
-        from . import m3 as _m3
-        return _m3
-    raise AttributeError(name)
+__all__ = ["inputs"]

@@ -1,0 +1,205 @@
+// C ABI of libm3: argument validation, plan selection, launches.
+// Every check runs on the host before any HIP call (see include/m3.h).
+#include <math.h>
+#include <string.h>
+
+#include "m3_internal.h"
+
+namespace m3i {
+namespace {
+
+__global__ void state_copy_kernel(const float *h0, float *hf, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) hf[i] = h0 ? h0[i] : 0.f;
+}
+
+bool aligned16(const void *p) { return p == nullptr || (((uintptr_t)p) & 15u) == 0; }
+
+struct Plan {
+    int kernel;       // 0 generic, 1 matrix-core
+    int nseg;         // segments per sequence
+    int64_t seg_chunks;
+    int64_t workgroups;
+    size_t ws_bytes;
+};
+
+bool mfma_applicable(const m3_shape &s) {
+    return s.io_dtype == M3_BF16 && s.dstate == 128 && s.headdim == 64 && s.chunk * s.rank == 64 &&
+           !(s.flags & M3_FLAG_FORCE_GENERIC) && mfma_kernel_available();
+}
+
+bool generic_applicable(const m3_shape &s) {
+    return s.dstate <= kGenericMaxN && s.headdim <= kGenericMaxP && s.dstate * s.headdim <= kGenericMaxNP &&
+           s.chunk * s.rank <= kGenericMaxRows;
+}
+
+m3_status check_shape(const m3_shape *s) {
+    if (!s) return M3_ERR_INVALID_ARG;
+    if (s->batch < 0 || s->seqlen < 0 || s->nheads < 1 || s->ngroups < 1 || s->headdim < 1 || s->dstate < 2 ||
+        s->rank < 1 || s->chunk < 1)
+        return M3_ERR_INVALID_ARG;
+    if (s->nheads % s->ngroups != 0 || s->dstate % 2 != 0) return M3_ERR_INVALID_ARG;
+    if (s->io_dtype != M3_F32 && s->io_dtype != M3_BF16) return M3_ERR_INVALID_ARG;
+    if (!(s->eps >= 0.f) || !isfinite(s->eps)) return M3_ERR_INVALID_ARG;
+    if (s->nsegments < 0) return M3_ERR_INVALID_ARG;
+    if (s->batch > (1LL << 31) || s->nheads > (1LL << 20) || s->seqlen > (1LL << 40)) return M3_ERR_UNSUPPORTED;
+    return M3_OK;
+}
+
+m3_status make_plan(const m3_shape &s, Plan *pl) {
+    Plan p{};
+    const int64_t nchunks = (s.seqlen + s.chunk - 1) / s.chunk;
+    if (mfma_applicable(s)) {
+        p.kernel = 1;
+        int nseg = s.nsegments;
+        if (nseg == 0) nseg = mfma_auto_segments(s.batch * s.nheads, nchunks);
+        if (nseg < 1) nseg = 1;
+        if (nseg > nchunks && nchunks > 0) nseg = (int)nchunks;
+        if (nchunks == 0) nseg = 1;
+        p.nseg = nseg;
+        p.seg_chunks = nseg > 1 ? (nchunks + nseg - 1) / nseg : nchunks;
+        if (nseg > 1) p.nseg = (int)((nchunks + p.seg_chunks - 1) / p.seg_chunks);
+        p.workgroups = s.batch * s.nheads * p.nseg;
+        p.ws_bytes = p.nseg > 1 ? mfma_workspace_bytes(s.batch * s.nheads, p.nseg, s.headdim, s.dstate) : 0;
+    } else if (generic_applicable(s)) {
+        if (s.nsegments > 1) return M3_ERR_UNSUPPORTED;  // the fp32 kernel runs each chain in one pass
+        p.kernel = 0;
+        p.nseg = 1;
+        p.seg_chunks = nchunks;
+        p.workgroups = s.batch * s.nheads;
+        p.ws_bytes = 0;
+    } else {
+        return M3_ERR_UNSUPPORTED;
+    }
+    *pl = p;
+    return M3_OK;
+}
+
+}  // namespace
+}  // namespace m3i
+
+using namespace m3i;
+
+extern "C" {
+
+const char *m3_status_str(m3_status st) {
+    switch (st) {
+        case M3_OK: return "ok";
+        case M3_ERR_INVALID_ARG: return "invalid argument";
+        case M3_ERR_UNSUPPORTED: return "unsupported shape";
+        case M3_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+        case M3_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case M3_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+int m3_version(void) { return 100; }
+
+m3_status m3_scan_plan(const m3_shape *shape, m3_plan *plan) {
+    m3_status st = check_shape(shape);
+    if (st != M3_OK) return st;
+    if (!plan) return M3_ERR_INVALID_ARG;
+    Plan p;
+    st = make_plan(*shape, &p);
+    if (st != M3_OK) return st;
+    plan->kernel = p.kernel;
+    plan->nsegments = p.nseg;
+    plan->workgroups = p.workgroups;
+    plan->workspace_bytes = p.ws_bytes;
+    return M3_OK;
+}
+
+size_t m3_scan_workspace_bytes(const m3_shape *shape) {
+    if (check_shape(shape) != M3_OK) return 0;
+    Plan p;
+    if (make_plan(*shape, &p) != M3_OK) return 0;
+    return p.ws_bytes;
+}
+
+m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspace, size_t ws_bytes,
+                      void *stream) {
+    m3_status st = check_shape(shape);
+    if (st != M3_OK) return st;
+    if (!io) return M3_ERR_INVALID_ARG;
+    const m3_shape &s = *shape;
+    if ((io->x_prev == nullptr) != (io->Braw_prev == nullptr)) return M3_ERR_INVALID_ARG;
+    const bool work = s.batch * s.seqlen > 0;
+    if (work && (!io->x || !io->Braw || !io->Craw || !io->dt || !io->A || !io->lam || !io->theta ||
+                 !io->B_bias || !io->C_bias || !io->y))
+        return M3_ERR_INVALID_ARG;
+    const void *ptrs[] = {io->x, io->Braw, io->Craw, io->dt, io->A, io->lam, io->theta, io->B_bias,
+                          io->C_bias, io->B_normw, io->C_normw, io->h0, io->x_prev, io->Braw_prev,
+                          io->y, io->h_final, workspace};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return M3_ERR_MISALIGNED;
+    Plan p;
+    st = make_plan(s, &p);
+    if (st != M3_OK) return st;
+    if (p.ws_bytes > 0 && (workspace == nullptr || ws_bytes < p.ws_bytes)) return M3_ERR_WORKSPACE_TOO_SMALL;
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    ScanArgs a{};
+    a.b = s.batch; a.L = s.seqlen; a.H = s.nheads; a.G = s.ngroups; a.P = s.headdim; a.N = s.dstate;
+    a.R = s.rank; a.C = s.chunk; a.eps = s.eps; a.bf16 = (s.io_dtype == M3_BF16);
+    a.has_prev = io->x_prev != nullptr;
+    a.x = io->x; a.Braw = io->Braw; a.Craw = io->Craw; a.dt = io->dt; a.A = io->A; a.lam = io->lam;
+    a.theta = io->theta; a.B_bias = io->B_bias; a.C_bias = io->C_bias; a.B_normw = io->B_normw;
+    a.C_normw = io->C_normw; a.h0 = io->h0; a.x_prev = io->x_prev; a.Braw_prev = io->Braw_prev;
+    a.y = io->y; a.h_final = io->h_final;
+
+    hipError_t e = hipSuccess;
+    if (s.batch * s.nheads == 0) return M3_OK;
+    if (s.seqlen == 0) {
+        if (io->h_final) {
+            const int64_t n = s.batch * s.nheads * s.headdim * s.dstate;
+            hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs, io->h0,
+                               io->h_final, n);
+            e = hipGetLastError();
+        }
+        return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+    }
+    if (p.kernel == 0) {
+        e = launch_scan_generic(a, hs);
+    } else {
+        SplitPlan sp{};
+        sp.nseg = p.nseg;
+        sp.seg_chunks = p.seg_chunks;
+        if (p.nseg > 1) mfma_workspace_carve(workspace, s.batch * s.nheads, p.nseg, s.headdim, s.dstate, &sp);
+        e = launch_scan_mfma(a, sp, hs);
+    }
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *stream) {
+    if (!shape || !io) return M3_ERR_INVALID_ARG;
+    const m3_shape &s = *shape;
+    if (s.batch < 0 || s.nheads < 1 || s.ngroups < 1 || s.headdim < 1 || s.dstate < 2 || s.rank < 1)
+        return M3_ERR_INVALID_ARG;
+    if (s.nheads % s.ngroups != 0 || s.dstate % 2 != 0) return M3_ERR_INVALID_ARG;
+    if (s.io_dtype != M3_F32 && s.io_dtype != M3_BF16) return M3_ERR_INVALID_ARG;
+    if (!(s.eps >= 0.f) || !isfinite(s.eps)) return M3_ERR_INVALID_ARG;
+    if ((io->x_prev == nullptr) != (io->Braw_prev == nullptr)) return M3_ERR_INVALID_ARG;
+    const int64_t N = s.dstate;
+    if (!(N == 16 || N == 32 || N == 64 || N == 128 || N == 256) || s.headdim > kDecodeMaxP ||
+        s.rank > kDecodeMaxR || s.batch > (1LL << 31))
+        return M3_ERR_UNSUPPORTED;
+    if (s.batch > 0 && (!io->x || !io->Braw || !io->Craw || !io->dt || !io->A || !io->lam || !io->theta ||
+                        !io->B_bias || !io->C_bias || !io->h || !io->y))
+        return M3_ERR_INVALID_ARG;
+    const void *ptrs[] = {io->x, io->Braw, io->Craw, io->dt, io->A, io->lam, io->theta, io->B_bias,
+                          io->C_bias, io->B_normw, io->C_normw, io->x_prev, io->Braw_prev, io->h, io->y};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return M3_ERR_MISALIGNED;
+    if (s.batch == 0) return M3_OK;
+    DecodeArgs a{};
+    a.b = s.batch; a.H = s.nheads; a.G = s.ngroups; a.P = s.headdim; a.N = s.dstate; a.R = s.rank;
+    a.eps = s.eps; a.bf16 = (s.io_dtype == M3_BF16); a.has_prev = io->x_prev != nullptr;
+    a.x = io->x; a.Braw = io->Braw; a.Craw = io->Craw; a.dt = io->dt; a.A = io->A; a.lam = io->lam;
+    a.theta = io->theta; a.B_bias = io->B_bias; a.C_bias = io->C_bias; a.B_normw = io->B_normw;
+    a.C_normw = io->C_normw; a.x_prev = io->x_prev; a.Braw_prev = io->Braw_prev; a.h = io->h; a.y = io->y;
+    hipError_t e = launch_decode(a, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+"""Thin Python binding of libm3 (include/m3.h): argument marshalling only.
+
+Every step of the mixer runs in the library's HIP kernels; this module checks
+that tensors are CUDA (HIP) tensors of the right dtype and contiguity, fills the
+C structs and passes raw pointers plus the current stream. If the library is not
+built, importing this module raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libm3.so")
+
+M3_OK = 0
+M3_F32, M3_BF16 = 0, 1
+M3_FLAG_FORCE_GENERIC = 1
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+        ("ngroups", ctypes.c_int64), ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+        ("rank", ctypes.c_int64), ("chunk", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("eps", ctypes.c_float), ("nsegments", ctypes.c_int32),
+    ]
+
+
+class ScanIO(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "Braw", "Craw", "dt", "A", "lam", "theta", "B_bias", "C_bias", "B_normw", "C_normw",
+        "h0", "x_prev", "Braw_prev", "y", "h_final")]
+
+
+class DecodeIO(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "Braw", "Craw", "dt", "A", "lam", "theta", "B_bias", "C_bias", "B_normw", "C_normw",
+        "x_prev", "Braw_prev", "h", "y")]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("nsegments", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libm3.so is not built (%s); run __graft_entry__.build() or "
+                          "python state_space_sequence_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.m3_scan_fwd.restype = ctypes.c_int
+    lib.m3_scan_fwd.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ScanIO), ctypes.c_void_p,
+                                ctypes.c_size_t, ctypes.c_void_p]
+    lib.m3_decode_step.restype = ctypes.c_int
+    lib.m3_decode_step.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(DecodeIO), ctypes.c_void_p]
+    lib.m3_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.m3_scan_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
+    lib.m3_scan_plan.restype = ctypes.c_int
+    lib.m3_scan_plan.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Plan)]
+    lib.m3_status_str.restype = ctypes.c_char_p
+    lib.m3_status_str.argtypes = [ctypes.c_int]
+    lib.m3_version.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+class M3Error(RuntimeError):
+    def __init__(self, code: int):
+        self.code = code
+        super().__init__("libm3: %s (%d)" % (lib.m3_status_str(code).decode(), code))
+
+
+def _check(rc: int):
+    if rc != M3_OK:
+        raise M3Error(rc)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _io_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return M3_BF16
+    if t.dtype == torch.float32:
+        return M3_F32
+    raise TypeError("io tensors must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_shape(batch, seqlen, nheads, ngroups, headdim, dstate, rank, chunk, io_dtype, eps=1e-5,
+               flags=0, nsegments=0) -> Shape:
+    return Shape(batch, seqlen, nheads, ngroups, headdim, dstate, rank, chunk, io_dtype, flags, eps, nsegments)
+
+
+def scan_shape(x, Braw, chunk, eps=1e-5, *, force_generic=False, nsegments=0) -> Shape:
+    b, L, H, R, P = x.shape
+    G, N = Braw.shape[2], Braw.shape[4]
+    return make_shape(b, L, H, G, P, N, R, chunk, _io_dtype(x), eps,
+                      M3_FLAG_FORCE_GENERIC if force_generic else 0, nsegments)
+
+
+def plan(shape: Shape) -> Plan:
+    p = Plan()
+    _check(lib.m3_scan_plan(ctypes.byref(shape), ctypes.byref(p)))
+    return p
+
+
+def workspace_bytes(shape: Shape) -> int:
+    return int(lib.m3_scan_workspace_bytes(ctypes.byref(shape)))
+
+
+def scan_fwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *, chunk=64, eps=1e-5,
+             B_normw=None, C_normw=None, h0=None, x_prev=None, Braw_prev=None,
+             y=None, h_final=None, want_state=True, workspace=None, nsegments=0,
+             force_generic=False, stream=None):
+    """Chunked-scan prefill (m3_scan_fwd). Shapes: x [b,L,H,R,P], Braw/Craw [b,L,G,R,N],
+    dt/A/lam [b,L,H], theta [b,L,G,N/2], biases [H,R,N]. Returns (y, h_final)."""
+    shape = scan_shape(x, Braw, chunk, eps, force_generic=force_generic, nsegments=nsegments)
+    if y is None:
+        y = torch.empty_like(x)
+    if h_final is None and want_state:
+        b, _, H, _, P = x.shape
+        h_final = torch.empty((b, H, P, Braw.shape[4]), dtype=torch.float32, device=x.device)
+    ws = workspace_bytes(shape)
+    if ws and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=x.device)
+    io = ScanIO(_ptr(x), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
+                _ptr(B_bias), _ptr(C_bias), _ptr(B_normw), _ptr(C_normw), _ptr(h0),
+                _ptr(x_prev), _ptr(Braw_prev), _ptr(y), _ptr(h_final))
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.m3_scan_fwd(ctypes.byref(shape), ctypes.byref(io), _ptr(workspace), wsb, _stream(stream)))
+    return y, h_final
+
+
+def decode_step(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, h, *, eps=1e-5,
+                B_normw=None, C_normw=None, x_prev=None, Braw_prev=None, y=None, stream=None):
+    """One decode step (m3_decode_step). x [b,H,R,P], Braw/Craw [b,G,R,N], dt/A/lam [b,H],
+    theta [b,G,N/2], h [b,H,P,N] fp32 updated in place. Returns y [b,H,R,P]."""
+    b, H, R, P = x.shape
+    G, N = Braw.shape[1], Braw.shape[3]
+    shape = make_shape(b, 1, H, G, P, N, R, 1, _io_dtype(x), eps)
+    if y is None:
+        y = torch.empty_like(x)
+    io = DecodeIO(_ptr(x), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
+                  _ptr(B_bias), _ptr(C_bias), _ptr(B_normw), _ptr(C_normw), _ptr(x_prev),
+                  _ptr(Braw_prev), _ptr(h), _ptr(y))
+    _check(lib.m3_decode_step(ctypes.byref(shape), ctypes.byref(io), _stream(stream)))
+    return y
+
+
+# ---------------------------------------------------------------- helpers ---
+def to_device(inp: dict, io: str, device="cuda"):
+    """Move a numpy input dict (from state_space_sequence_amd.inputs) to the GPU:
+    io tensors in bf16 or fp32 (bf16 values are exact), the rest fp32."""
+    io_keys = ("x", "Braw", "Craw", "x_prev", "Braw_prev")
+    out = {}
+    for k, v in inp.items():
+        if v is None:
+            out[k] = None
+            continue
+        t = torch.from_numpy(v).to(device)
+        if k in io_keys and io == "bf16":
+            t = t.to(torch.bfloat16)
+        out[k] = t.contiguous()
+    return out

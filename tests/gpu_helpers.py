@@ -1,0 +1,41 @@
+"""Helpers for the GPU parity tests: run the HIP library through its binding on
+seeded inputs and compare with the oracle by the max-normalised error
+err(T) = max|T_gpu - T_ref| / max|T_ref|."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+TOL_F32 = 1e-4   # fp32 io paths
+TOL_BF16 = 2e-2  # bf16-input paths (y is stored in bf16)
+
+
+def relerr(gpu, ref) -> float:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    if den == 0.0:
+        return float(np.max(np.abs(gpu))) if gpu.size else 0.0
+    return float(np.max(np.abs(gpu - ref)) / den)
+
+
+def gpu_scan(inp, shape, **kw):
+    from state_space_sequence_amd import m3
+    d = m3.to_device(inp, shape.io)
+    y, h = m3.scan_fwd(d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"],
+                       d["B_bias"], d["C_bias"], chunk=shape.chunk, eps=shape.eps,
+                       B_normw=d.get("B_normw"), C_normw=d.get("C_normw"), h0=d.get("h0"),
+                       x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"), **kw)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), h.cpu().numpy().astype(np.float64)
+
+
+def gpu_decode(inp, shape):
+    from state_space_sequence_amd import m3
+    d = m3.to_device(inp, shape.io)
+    h = d["h"].clone()
+    y = m3.decode_step(d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"],
+                       d["B_bias"], d["C_bias"], h, eps=shape.eps, B_normw=d.get("B_normw"),
+                       C_normw=d.get("C_normw"), x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"))
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), h.cpu().numpy().astype(np.float64)

@@ -1,0 +1,133 @@
+"""GPU parity: fused decode kernel and fp32 chunked prefill kernel vs the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from state_space_sequence_amd.inputs import WORKLOADS, Shape, make_decode_inputs, make_scan_inputs
+from tests.gpu_helpers import TOL_BF16, TOL_F32, gpu_decode, gpu_scan, relerr
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ decode --
+DECODE_CASES = [
+    # (b, H, G, P, N, R, io, first_token, normw)
+    (3, 4, 1, 16, 16, 1, "f32", False, False),
+    (2, 4, 2, 64, 64, 2, "f32", False, True),
+    (2, 6, 3, 32, 128, 4, "f32", True, False),
+    (2, 4, 4, 64, 256, 3, "f32", False, False),
+    (4, 8, 1, 64, 128, 1, "bf16", False, False),
+    (4, 8, 1, 64, 64, 4, "bf16", False, True),
+    (1, 2, 1, 200, 32, 2, "bf16", True, False),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES)
+def test_decode_matches_oracle(case):
+    b, H, G, P, N, R, io, first, normw = case
+    shape = Shape(b, 1, H, G, P, N, R, 1, io)
+    say("decode", case)
+    inp = make_decode_inputs(shape, seed=11, first_token=first, with_normw=normw)
+    y, h = gpu_decode(inp, shape)
+    yr, hr = oracle.decode(inp, shape)
+    # the state is fp32 throughout: fp32 bar for h on both io dtypes
+    assert relerr(h, hr) < TOL_F32
+    assert relerr(y, yr) < (TOL_F32 if io == "f32" else TOL_BF16)
+
+
+@pytest.mark.parametrize("name", ["decode_siso_n128", "decode_mimo4_n128", "decode_siso_n64", "decode_mimo4_n64"])
+def test_decode_full_workloads(name):
+    shape = WORKLOADS[name]
+    say("decode workload", name)
+    inp = make_decode_inputs(shape, seed=3)
+    y, h = gpu_decode(inp, shape)
+    yr, hr = oracle.decode(inp, shape)
+    assert relerr(h, hr) < TOL_F32
+    assert relerr(y, yr) < TOL_BF16
+
+
+# ----------------------------------------------------- fp32 chunked prefill --
+def test_tiny_siso_f32_workload():
+    shape = WORKLOADS["tiny_siso_f32"]
+    say("prefill tiny_siso_f32")
+    inp = make_scan_inputs(shape, seed=0)
+    y, h = gpu_scan(inp, shape)
+    yr, hr = oracle.scan(inp, shape)
+    assert relerr(y, yr) < TOL_F32
+    assert relerr(h, hr) < TOL_F32
+
+
+GENERIC_CASES = [
+    # (b, L, H, G, P, N, R, chunk, io, state, prev, normw, slow)
+    (2, 100, 2, 1, 16, 16, 1, 64, "f32", False, False, False, True),     # ragged tail
+    (1, 256, 3, 3, 8, 32, 2, 16, "f32", True, True, True, True),         # MIMO, G = H
+    (2, 77, 4, 2, 32, 64, 4, 16, "f32", True, False, False, False),      # MIMO R=4, ragged
+    (1, 5, 2, 1, 16, 16, 1, 64, "f32", False, True, False, False),       # shorter than a chunk
+    (1, 192, 2, 1, 64, 128, 1, 64, "f32", True, True, False, True),      # 1.5B-like head shape
+    (2, 130, 2, 1, 64, 128, 1, 64, "bf16", False, False, False, True),   # bf16 io, fp32 math
+]
+
+
+@pytest.mark.parametrize("case", GENERIC_CASES)
+def test_generic_prefill_matches_oracle(case):
+    b, L, H, G, P, N, R, C, io, state, prev, normw, slow = case
+    shape = Shape(b, L, H, G, P, N, R, C, io)
+    say("generic prefill", case)
+    inp = make_scan_inputs(shape, seed=5, slow_decay=slow, with_h0=state, with_prev=prev, with_normw=normw)
+    y, h = gpu_scan(inp, shape, force_generic=True)
+    yr, hr = oracle.scan(inp, shape)
+    assert relerr(h, hr) < TOL_F32
+    assert relerr(y, yr) < (TOL_F32 if io == "f32" else TOL_BF16)
+
+
+def test_generic_chunk_size_invariance():
+    """The chunked result does not depend on the chunk length (exact re-association)."""
+    shape = Shape(1, 150, 2, 1, 16, 32, 1, 64, "f32")
+    inp = make_scan_inputs(shape, seed=8, slow_decay=True, with_h0=True, with_prev=True)
+    y64, h64 = gpu_scan(inp, shape, force_generic=True)
+    for c in (1, 7, 16, 50):
+        y, h = gpu_scan(inp, shape.replace(chunk=c), force_generic=True)
+        assert relerr(y, y64) < 1e-5 and relerr(h, h64) < 1e-5, c
+
+
+def test_prefill_then_decode_continues_the_sequence():
+    """prefill(L-1) then one decode step equals prefill(L) at position L-1 (state passing)."""
+    shape = Shape(2, 65, 2, 1, 16, 32, 2, 16, "f32")
+    inp = make_scan_inputs(shape, seed=9, slow_decay=True)
+    y_full, h_full = gpu_scan(inp, shape, force_generic=True)
+    Lm1 = shape.seqlen - 1
+    part = {k: (np.ascontiguousarray(v[:, :Lm1]) if k in ("x", "Braw", "Craw", "dt", "A", "lam", "theta") else v)
+            for k, v in inp.items()}
+    _, h_part = gpu_scan(part, shape.replace(seqlen=Lm1), force_generic=True)
+    dec = {k: (np.ascontiguousarray(inp[k][:, Lm1]) if k in ("x", "Braw", "Craw", "dt", "A", "lam", "theta") else inp[k])
+           for k in inp}
+    dec["h"] = h_part.astype(np.float32)
+    dec["x_prev"] = np.ascontiguousarray(inp["x"][:, Lm1 - 1])
+    dec["Braw_prev"] = np.ascontiguousarray(inp["Braw"][:, Lm1 - 1])
+    yd, hd = gpu_decode(dec, shape)
+    assert relerr(yd, y_full[:, Lm1]) < 1e-5
+    assert relerr(hd, h_full) < 1e-5
+
+
+def test_empty_sequence_copies_state():
+    shape = Shape(2, 0, 2, 1, 16, 16, 1, 64, "f32")
+    inp = make_scan_inputs(shape.replace(seqlen=1), seed=1, with_h0=True)
+    inp = {k: (np.ascontiguousarray(v[:, :0]) if k in ("x", "Braw", "Craw", "dt", "A", "lam", "theta") else v)
+           for k, v in inp.items()}
+    y, h = gpu_scan(inp, shape)
+    assert y.size == 0
+    np.testing.assert_array_equal(h, inp["h0"])
+
+
+def test_generic_is_deterministic():
+    shape = Shape(2, 90, 3, 1, 16, 32, 2, 16, "f32")
+    inp = make_scan_inputs(shape, seed=12)
+    y1, h1 = gpu_scan(inp, shape, force_generic=True)
+    y2, h2 = gpu_scan(inp, shape, force_generic=True)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
