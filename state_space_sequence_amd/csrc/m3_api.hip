@@ -25,6 +25,7 @@ struct Plan {
 
 bool mfma_applicable(const m3_shape &s) {
     return s.io_dtype == M3_BF16 && s.dstate == 128 && s.headdim == 64 && s.chunk * s.rank == 64 &&
+           (s.rank == 1 || s.rank == 2 || s.rank == 4) &&
            !(s.flags & M3_FLAG_FORCE_GENERIC) && mfma_kernel_available();
 }
 

@@ -1,10 +1,700 @@
-// Matrix-core (bf16 MFMA) chunked-scan prefill: placeholder until the kernel lands.
+// Matrix-core chunked-scan prefill of the Mamba-3 SSM core for gfx950.
+//
+// Shape: bf16 io, N = 128 state, P = 64 head dim, 64 rows per chunk where a row
+// is a (token, rank) pair: chunk = 64 / R tokens (the pages' rule "64 / mimo_rank"
+// for bf16; Mamba-3 paper §3.3 "chunked algorithm for MIMO", with the chunk
+// chosen so that the intra-chunk tile stays 64 x 64).
+//
+// Method (see the fp32 kernel for the same algebra written plainly):
+//   rotated frame (§3.2.2 Proposition 4 / App. B.3): B_bar = R(-Phi) B,
+//   C_bar = R(-Phi) C, Phi = cumulative dt*theta from the workgroup's first token;
+//   folded trapezoid weights w_s = lam_s dt_s + (1-lam_{s+1}) dt_{s+1};
+//   per chunk (SSD chunked algorithm, §3.3, mask of §3.1.3 eq. 7):
+//     S^T = B_bar C_bar^T                        (MFMA, K = N)
+//     P^T = S^T o L^T,  L[t,s] = exp(cs_t - cs_s) w_s (s<t), gamma_t (s=t)
+//     Y   = diag(exp(cs_t)) C_bar H~ + P X        (MFMA, K = N and K = rows)
+//     H~ <- exp(cs_end) H~ + B_bar^T diag(exp(cs_end - cs_s) w_s) X   (MFMA, K = rows)
+//   final state H = R(Phi_end) H~.
+//
+// One workgroup (4 waves) owns one (batch, head) chain, or one segment of it
+// when the sequence is split (state passing, App. G.2: pass 1 computes each
+// segment's end state from zero, a combine kernel chains them, pass 2 produces
+// the outputs from the right incoming states). Wave w:
+//   * rotates the 16 rows 16w..16w+15 of the chunk (each lane: one row, 32 of
+//     the 128 state columns, i.e. 16 rotation pairs (i, i+64)), which leaves the
+//     lane holding exactly its MFMA fragments of B_bar and C_bar;
+//   * owns output rows 16w..16w+15 (S^T blocks s <= t, mask, Y);
+//   * owns state columns n in [16w, 16w+16) and [64+16w, 64+16w+16) (so each
+//     rotation pair of the state is held by one lane) for all 64 p.
+// MFMA: v_mfma_f32_16x16x32_bf16. Operand fragments: lane l holds row l%16 and
+// K-slots 8*(l/16)..+7; the accumulator holds rows 4*(l/16)..+3 of column l%16.
+// P^T comes out of the first MFMA already in the A-operand layout of P (K-slots
+// taken in accumulator order), so it never goes through LDS.
+//
+// LDS (bf16 tiles with rows padded by 16 bytes, ~69 KiB, two workgroups
+// per CU): B_bar [row][n], B_bar*scale transposed [n][row], X transposed
+// [p][row], the bf16 copy of the state transposed [p][n] for the Y_off product,
+// and small per-row scalar tables.
 #include "m3_internal.h"
 
 namespace m3i {
-bool mfma_kernel_available() { return false; }
-int mfma_auto_segments(int64_t, int64_t) { return 1; }
-size_t mfma_workspace_bytes(int64_t, int, int64_t, int64_t) { return 0; }
-void mfma_workspace_carve(void *, int64_t, int, int64_t, int64_t, SplitPlan *) {}
-hipError_t launch_scan_mfma(const ScanArgs &, const SplitPlan &, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kN = 128, kP = 64, kRows = 64, kHalf = 64;
+// LDS row strides (elements): 16 bytes of padding per row puts the 8 rows that
+// one 16-byte fragment read touches on 8 different bank groups
+constexpr int kLdN = kN + 8;     // tiles with 128 columns (B_bar, state)
+constexpr int kLdR = kRows + 8;  // tiles with 64 columns (B_bar^T, X^T)
+constexpr int kThreads = 256;
+constexpr int kCUs = 256;  // MI355X compute units: 2 resident workgroups each
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInv2Pi = 0.15915494309189535f;
+
+enum Mode { kFull = 0, kPass1 = 1, kPass2 = 2 };
+
+// A value the compiler cannot see through: lane-derived indices computed from it
+// inside the chunk loop are recomputed each iteration instead of being hoisted
+// out of the loop and kept live (or spilled) across it.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float dpp_row_shr(float v, int k) {
+    // lanes whose source falls outside their 16-lane row read 0
+    int r;
+    switch (k) {
+        case 1: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false); break;
+        case 2: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false); break;
+        case 4: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false); break;
+        default: r = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false); break;
+    }
+    return __int_as_float(r);
+}
+
+__device__ __forceinline__ void sincos_rad(float x, float &s, float &c) {
+    // hardware sine/cosine take revolutions
+    const float rev = __builtin_amdgcn_fractf(x * kInv2Pi);
+    s = __builtin_amdgcn_sinf(rev);
+    c = __builtin_amdgcn_cosf(rev);
+}
+
+struct Smem {
+    __bf16 Bb[kRows * kLdN];  // B_bar [row][n]
+    __bf16 Bt[kN * kLdR];     // B_bar * cst, [n][row]
+    __bf16 Xt[kP * kLdR];     // X, [p][row]
+    __bf16 St[kP * kLdN];     // bf16 state, [p][n]
+    float l2cs[kRows];        // per row: log2(e) * chunk-local cumulative log decay
+    float wgt[kRows];         // per row: folded weight w of the row's token
+    float gam[kRows];         // per row: gamma
+    float eoff[kRows];        // per row: exp(cs) (carried-state output scale)
+    float angtot[4][kHalf];   // per wave: angle total of its rows
+    float carry[kHalf];       // cumulative angle before the current chunk
+    float bias[2][4][kN];     // B / C bias of this head, per rank
+    float normw[2][kN];       // BCNorm gains (ones when absent)
+    float rsp[4];             // 1/rms of the previous token's raw B rows
+};
+
+struct ChainPos {
+    int64_t chain, seg, c_begin, c_end;
+};
+
+__device__ __forceinline__ ChainPos chain_of_block(const ScanArgs &a, const SplitPlan &sp, int mode) {
+    // Blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous range
+    // of (segment, chain) so heads that share B, C, theta share an L2.
+    const int64_t nchains = a.b * a.H;
+    const int64_t nseg = (mode == kFull) ? 1 : sp.nseg;
+    const int64_t total = nchains * nseg;
+    const int64_t id = blockIdx.x;
+    int64_t lin = id;
+    if (total % 8 == 0) lin = (id % 8) * (total / 8) + id / 8;
+    ChainPos cp;
+    cp.seg = lin / nchains;
+    cp.chain = lin % nchains;
+    const int64_t nchunks = (a.L + a.C - 1) / a.C;
+    if (mode == kFull) {
+        cp.c_begin = 0;
+        cp.c_end = nchunks;
+    } else {
+        cp.c_begin = cp.seg * sp.seg_chunks;
+        cp.c_end = cp.c_begin + sp.seg_chunks < nchunks ? cp.c_begin + sp.seg_chunks : nchunks;
+    }
+    return cp;
+}
+
+template <int MODE, int R>
+__global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, SplitPlan sp) {
+    constexpr int C = kRows / R;  // tokens per chunk
+    __shared__ Smem sm;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+    const ChainPos pos = chain_of_block(a, sp, MODE);
+    const int64_t chain = pos.chain;
+    const int64_t bi = chain / a.H, hi = chain % a.H, g = hi / (a.H / a.G);
+    const int64_t L = a.L, H = a.H, G = a.G;
+    const bool has_w = a.B_normw != nullptr || a.C_normw != nullptr;
+
+    // ---------------------------------------------------------------- prologue
+    for (int e = tid; e < 2 * R * kN; e += kThreads) {
+        const int which = e / (R * kN), rem = e % (R * kN);
+        sm.bias[which][rem / kN][rem % kN] = (which == 0 ? a.B_bias : a.C_bias)[(hi * R) * kN + rem];
+    }
+    for (int e = tid; e < 2 * kN; e += kThreads) {
+        const float *src = (e < kN) ? a.B_normw : a.C_normw;
+        sm.normw[e / kN][e % kN] = src ? src[e % kN] : 1.f;
+    }
+    if (tid < kHalf) sm.carry[tid] = 0.f;
+
+    // state fragments: acc[q][pb] holds state[n = 16(w+4q) + 4lg + j][p = 16pb + lr]
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) acc[q][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    {
+        const int l = tid & 63, lr = l & 15, lg = l >> 4;
+        if constexpr (MODE == kFull || MODE == kPass2) {
+            const float *src = nullptr;
+            if (MODE == kFull)
+                src = a.h0 ? a.h0 + chain * (kP * kN) : nullptr;
+            else
+                src = sp.seg_state + (chain * sp.nseg + pos.seg) * (kP * kN);
+            if (src) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) {
+                        const int n0 = 16 * (w + 4 * q) + 4 * lg, p = 16 * pb + lr;
+                        acc[q][pb] = *reinterpret_cast<const f32x4 *>(src + p * kN + n0);
+                    }
+            }
+        }
+        if constexpr (MODE == kFull) {
+            if (a.has_prev && L > 0) {
+                // fold (1 - lam_0) dt_0 B_{-1} x_{-1}^T into the starting state
+                const __bf16 *bp = static_cast<const __bf16 *>(a.Braw_prev) + ((bi * G + g) * R) * kN;
+                const __bf16 *xp = static_cast<const __bf16 *>(a.x_prev) + ((bi * H + hi) * R) * kP;
+                float rsr[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float v0 = (float)bp[r * kN + 2 * l], v1 = (float)bp[r * kN + 2 * l + 1];
+                    rsr[r] = __builtin_amdgcn_rsqf(wave_sum(v0 * v0 + v1 * v1) * (1.f / kN) + a.eps);
+                }
+                const int64_t o0 = (bi * L) * H + hi;
+                const float f = (1.f - a.lam[o0]) * a.dt[o0];
+                const float *bb = a.B_bias + (hi * R) * kN;
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int n = 16 * (w + 4 * q) + 4 * lg + j, p = 16 * pb + lr;
+                            const float wn = a.B_normw ? a.B_normw[n] : 1.f;
+                            float s = 0.f;
+#pragma unroll
+                            for (int r = 0; r < R; ++r)
+                                s += ((float)bp[r * kN + n] * rsr[r] * wn + bb[r * kN + n]) * (float)xp[r * kP + p];
+                            acc[q][pb][j] += f * s;
+                        }
+            }
+        }
+        if constexpr (MODE != kPass1) {
+            // bf16 copy of the state for the first chunk's carried-state output
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    const int n0 = 16 * (w + 4 * q) + 4 * lg, p = 16 * pb + lr;
+                    bf16x4 v = {(__bf16)acc[q][pb][0], (__bf16)acc[q][pb][1], (__bf16)acc[q][pb][2],
+                                (__bf16)acc[q][pb][3]};
+                    *reinterpret_cast<bf16x4 *>(&sm.St[p * kLdN + n0]) = v;
+                }
+        }
+    }
+    __syncthreads();
+
+    float logdecay_total = 0.f;
+    float newcarry = 0.f;
+
+    for (int64_t c = pos.c_begin; c < pos.c_end; ++c) {
+        const int64_t c0 = c * C;
+        const int nv = (int)((L - c0) < C ? (L - c0) : C);
+        // lane-derived indices, recomputed per chunk (see opaque())
+        const int l = opaque(tid & 63);
+        const int lr = l & 15, lg = l >> 4;
+        const int row = 16 * w + lr;  // this lane's row in the rotation stage
+        const int r_row = row % R;
+        const int t_row = row / R;    // its token inside the chunk
+
+        // ---- token scalars: lane = token (every wave computes them)
+        float d = 0.f, av = 0.f, lm = 0.f;
+        if (l < nv) {
+            const int64_t o = (bi * L + c0 + l) * H + hi;
+            d = a.dt[o];
+            av = a.A[o];
+            lm = a.lam[o];
+        }
+        float cs = d * av;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float v = __shfl_up(cs, off, 64);
+            if (l >= off) cs += v;
+        }
+        const float dn = __shfl_down(d, 1, 64), ln = __shfl_down(lm, 1, 64);
+        float look = 0.f;
+        if (l + 1 < nv) {
+            look = (1.f - ln) * dn;
+        } else if (l + 1 == nv && c0 + nv < L) {
+            const int64_t o1 = (bi * L + c0 + nv) * H + hi;
+            look = (1.f - a.lam[o1]) * a.dt[o1];
+        }
+        const float gm = lm * d;
+        const float wt = gm + look;
+        const float cs_end = __shfl(cs, 63, 64);
+        const float cst = __expf(cs_end - cs) * wt;
+
+        // ---- this lane's row: raw B, C, theta, X
+        const bool valid = t_row < nv;
+        const int64_t tok = bi * L + c0 + t_row;
+        bf16x8 rb[4], rc[4];
+        f32x4 th[4];
+        bf16x8 xr[2];
+        if (valid) {
+            const bf16x8 *pb_ = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.Braw) +
+                                                                 ((tok * G + g) * R + r_row) * kN);
+            const bf16x8 *pc_ = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.Craw) +
+                                                                 ((tok * G + g) * R + r_row) * kN);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                rb[ks] = pb_[4 * ks + lg];
+                if constexpr (MODE != kPass1) rc[ks] = pc_[4 * ks + lg];
+            }
+            const f32x4 *pt = reinterpret_cast<const f32x4 *>(a.theta + (tok * G + g) * kHalf);
+            th[0] = pt[2 * lg];
+            th[1] = pt[2 * lg + 1];
+            th[2] = pt[8 + 2 * lg];
+            th[3] = pt[8 + 2 * lg + 1];
+            const bf16x8 *px = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.x) +
+                                                                ((tok * H + hi) * R + r_row) * kP);
+            xr[0] = px[2 * lg];
+            xr[1] = px[2 * lg + 1];
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                rb[ks] = bf16x8{};
+                rc[ks] = bf16x8{};
+                th[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            xr[0] = bf16x8{};
+            xr[1] = bf16x8{};
+        }
+        const float d_row = __shfl(d, t_row, 64);
+        const float cst_row = __shfl(cst, t_row, 64);
+
+        // ---- BCNorm factors of this row (sum over the 4 lanes that hold it)
+        float ssb = 0.f, ssc = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x2 vb = {rb[ks][2 * j], rb[ks][2 * j + 1]};
+                ssb = __builtin_amdgcn_fdot2_f32_bf16(vb, vb, ssb, false);
+                if constexpr (MODE != kPass1) {
+                    const bf16x2 vc = {rc[ks][2 * j], rc[ks][2 * j + 1]};
+                    ssc = __builtin_amdgcn_fdot2_f32_bf16(vc, vc, ssc, false);
+                }
+            }
+        ssb += __shfl_xor(ssb, 16, 64);
+        ssb += __shfl_xor(ssb, 32, 64);
+        const float rsb = __builtin_amdgcn_rsqf(ssb * (1.f / kN) + a.eps);
+        float rsc = 0.f;
+        if constexpr (MODE != kPass1) {
+            ssc += __shfl_xor(ssc, 16, 64);
+            ssc += __shfl_xor(ssc, 32, 64);
+            rsc = __builtin_amdgcn_rsqf(ssc * (1.f / kN) + a.eps);
+        }
+
+        // ---- angles: prefix over the tokens of this wave's rows (16-lane DPP rows)
+        // slot k (0..15) is channel i = 8lg + k (k < 8) or 32 + 8lg + (k - 8)
+        float ph[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            ph[4 * k + 0] = d_row * th[k][0];
+            ph[4 * k + 1] = d_row * th[k][1];
+            ph[4 * k + 2] = d_row * th[k][2];
+            ph[4 * k + 3] = d_row * th[k][3];
+        }
+#pragma unroll
+        for (int sh = R; sh < 16; sh <<= 1)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) ph[k] += dpp_row_shr(ph[k], sh);
+        if (lr == 15) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) sm.angtot[w][(k < 8 ? 8 * lg + k : 32 + 8 * lg + k - 8)] = ph[k];
+        }
+        __syncthreads();  // B1
+
+        // ---- rotate into the frame of the workgroup's first token
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i = (k < 8) ? 8 * lg + k : 32 + 8 * lg + k - 8;
+            float off = sm.carry[i];
+            for (int w2 = 0; w2 < w; ++w2) off += sm.angtot[w2][i];
+            ph[k] += off;
+        }
+        if (w == 0) {
+            // per-row scalar tables for the mask and the carried-state output
+            const int tl = l / R;
+            const float cs_l = __shfl(cs, tl, 64);
+            sm.l2cs[l] = cs_l * kLog2e;
+            sm.wgt[l] = __shfl(wt, tl, 64);
+            sm.gam[l] = __shfl(gm, tl, 64);
+            sm.eoff[l] = __expf(cs_l);
+            newcarry = sm.carry[l] + sm.angtot[0][l] + sm.angtot[1][l] + sm.angtot[2][l] + sm.angtot[3][l];
+        }
+        bf16x8 bfr[4], cfr[4];
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+            for (int jh = 0; jh < 2; ++jh) {
+                const int i0 = 32 * ks2 + 8 * lg + 4 * jh;  // first of 4 channels
+                const f32x4 blo = *reinterpret_cast<const f32x4 *>(&sm.bias[0][r_row][i0]);
+                const f32x4 bhi = *reinterpret_cast<const f32x4 *>(&sm.bias[0][r_row][i0 + 64]);
+                f32x4 wbl = {1.f, 1.f, 1.f, 1.f}, wbh = {1.f, 1.f, 1.f, 1.f};
+                if (has_w) {
+                    wbl = *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0]);
+                    wbh = *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0 + 64]);
+                }
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = 4 * jh + jj;
+                    const int i = i0 + jj;
+                    float sn, cn;
+                    sincos_rad(ph[8 * ks2 + j], sn, cn);
+                    const float bl = (float)rb[ks2][j] * (rsb * wbl[jj]) + blo[jj];
+                    const float bh = (float)rb[ks2 + 2][j] * (rsb * wbh[jj]) + bhi[jj];
+                    float bbl = cn * bl + sn * bh;
+                    float bbh = cn * bh - sn * bl;
+                    if (!valid) { bbl = 0.f; bbh = 0.f; }
+                    bfr[ks2][j] = (__bf16)bbl;
+                    bfr[ks2 + 2][j] = (__bf16)bbh;
+                    // transposed, scaled copy for the state update
+                    sm.Bt[i * kLdR + row] = (__bf16)(bbl * cst_row);
+                    sm.Bt[(i + 64) * kLdR + row] = (__bf16)(bbh * cst_row);
+                    if constexpr (MODE != kPass1) {
+                        const float clo = sm.bias[1][r_row][i], chi = sm.bias[1][r_row][i + 64];
+                        const float wcl = has_w ? sm.normw[1][i] : 1.f, wch = has_w ? sm.normw[1][i + 64] : 1.f;
+                        const float cl = (float)rc[ks2][j] * (rsc * wcl) + clo;
+                        const float ch = (float)rc[ks2 + 2][j] * (rsc * wch) + chi;
+                        float ccl = cn * cl + sn * ch;
+                        float cch = cn * ch - sn * cl;
+                        if (!valid) { ccl = 0.f; cch = 0.f; }
+                        cfr[ks2][j] = (__bf16)ccl;
+                        cfr[ks2 + 2][j] = (__bf16)cch;
+                    }
+                }
+            }
+        }
+        if constexpr (MODE != kPass1) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                *reinterpret_cast<bf16x8 *>(&sm.Bb[row * kLdN + 32 * ks + 8 * lg]) = bfr[ks];
+        }
+        // X transposed: this lane holds X[row][16lg .. 16lg+15]
+#pragma unroll
+        for (int k = 0; k < 16; ++k) sm.Xt[(16 * lg + k) * kLdR + row] = xr[k >> 3][k & 7];
+        __syncthreads();  // B2
+
+        if constexpr (MODE != kPass1) {
+            // ---- S^T blocks (s-block sb <= w) for this wave's t-block
+            f32x4 sT[4];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                sT[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (sb <= w) {
+                    const int srow = 16 * sb + lr;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const bf16x8 av_ = (sb == w) ? bfr[ks]
+                                                     : *reinterpret_cast<const bf16x8 *>(
+                                                           &sm.Bb[srow * kLdN + 32 * ks + 8 * lg]);
+                        sT[sb] = mfma(av_, cfr[ks], sT[sb]);
+                    }
+                }
+            }
+            // ---- mask: lane holds S^T[s = 16sb + 4lg + j][t = 16w + lr]
+            const int ttok = row / R;
+            const float l2t = sm.l2cs[row], gmt = sm.gam[row];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                if (sb <= w) {
+                    const f32x4 l2s = *reinterpret_cast<const f32x4 *>(&sm.l2cs[16 * sb + 4 * lg]);
+                    const f32x4 ws = *reinterpret_cast<const f32x4 *>(&sm.wgt[16 * sb + 4 * lg]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int stok = (16 * sb + 4 * lg + j) / R;
+                        float m = 0.f;
+                        if (stok < ttok)
+                            m = __builtin_amdgcn_exp2f(l2t - l2s[j]) * ws[j];
+                        else if (stok == ttok)
+                            m = gmt;
+                        sT[sb][j] *= m;
+                    }
+                }
+            }
+            bf16x8 pfr[2];
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pfr[m2][j] = (__bf16)sT[2 * m2][j];
+                    pfr[m2][j + 4] = (__bf16)sT[2 * m2 + 1][j];
+                }
+            // ---- Y = diag(exp(cs)) C_bar St + P X
+            f32x4 yacc[4];
+            const f32x4 eo = *reinterpret_cast<const f32x4 *>(&sm.eoff[16 * w + 4 * lg]);
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const int p = 16 * pb + lr;
+                f32x4 yv = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(&sm.St[p * kLdN + 32 * ks + 8 * lg]);
+                    yv = mfma(cfr[ks], bv, yv);
+                }
+                yv[0] *= eo[0];
+                yv[1] *= eo[1];
+                yv[2] *= eo[2];
+                yv[3] *= eo[3];
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    if (2 * m2 <= w) {
+                        const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(&sm.Xt[p * kLdR + 32 * m2 + 4 * lg]);
+                        const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(&sm.Xt[p * kLdR + 32 * m2 + 16 + 4 * lg]);
+                        const bf16x8 bv = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                        yv = mfma(pfr[m2], bv, yv);
+                    }
+                }
+                yacc[pb] = yv;
+            }
+            // ---- store y rows 16w + 4lg + j, column p
+            __bf16 *yp = static_cast<__bf16 *>(a.y);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rrow = 16 * w + 4 * lg + j;
+                const int rt = rrow / R, rr = rrow % R;
+                if (rt < nv) {
+                    const int64_t base = (((bi * L + c0 + rt) * H + hi) * R + rr) * kP;
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) yp[base + 16 * pb + lr] = (__bf16)yacc[pb][j];
+                }
+            }
+            __syncthreads();  // B3: St and Bb reads done
+        }
+
+        // ---- state update: acc[q][pb] = exp(cs_end) acc + Bt-rows x Xt
+        const float dec = __expf(cs_end);
+        logdecay_total += cs_end;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) acc[q][pb] *= dec;
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+            bf16x8 xb[4];
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb)
+                xb[pb] = *reinterpret_cast<const bf16x8 *>(&sm.Xt[(16 * pb + lr) * kLdR + 32 * m2 + 8 * lg]);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int n = 16 * (w + 4 * q) + lr;
+                const bf16x8 bt = *reinterpret_cast<const bf16x8 *>(&sm.Bt[n * kLdR + 32 * m2 + 8 * lg]);
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) acc[q][pb] = mfma(bt, xb[pb], acc[q][pb]);
+            }
+        }
+        if constexpr (MODE != kPass1) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    const int n0 = 16 * (w + 4 * q) + 4 * lg, p = 16 * pb + lr;
+                    bf16x4 v = {(__bf16)acc[q][pb][0], (__bf16)acc[q][pb][1], (__bf16)acc[q][pb][2],
+                                (__bf16)acc[q][pb][3]};
+                    *reinterpret_cast<bf16x4 *>(&sm.St[p * kLdN + n0]) = v;
+                }
+        }
+        // carry was last read before B2 of this chunk; the next read is after B1 of the next
+        if (w == 0) sm.carry[l] = newcarry;
+    }
+    __syncthreads();
+
+    // ------------------------------------------------------------- epilogue
+    const int l = tid & 63, lr = l & 15, lg = l >> 4;
+    const bool last_seg = (MODE == kFull) || (pos.c_end * C >= L);
+    float *dst = nullptr;
+    if (MODE == kPass1)
+        dst = sp.seg_state + (chain * sp.nseg + pos.seg) * (kP * kN);
+    else if (last_seg)
+        dst = a.h_final ? a.h_final + chain * (kP * kN) : nullptr;
+    if (dst) {
+        // back to the physical frame: H = R(Phi) H~ on pairs (n, n + 64)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 16 * w + 4 * lg + j;
+            float sn, cn;
+            sincosf(sm.carry[i], &sn, &cn);
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const float u = acc[0][pb][j], v = acc[1][pb][j];
+                acc[0][pb][j] = cn * u - sn * v;
+                acc[1][pb][j] = sn * u + cn * v;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const int n0 = 16 * (w + 4 * q) + 4 * lg, p = 16 * pb + lr;
+                *reinterpret_cast<f32x4 *>(dst + p * kN + n0) = acc[q][pb];
+            }
+    }
+    if constexpr (MODE == kPass1) {
+        if (tid < kHalf) sp.seg_angle[(chain * sp.nseg + pos.seg) * kHalf + tid] = sm.carry[tid];
+        if (tid == 0) sp.seg_decay[chain * sp.nseg + pos.seg] = logdecay_total;
+    }
+}
+
+// Chain the segment end states: H_in[0] = h0 (+ fold of the previous token);
+// H_in[k+1] = exp(D_k) R(Phi_k) H_in[k] + E_k. Overwrites E_k with H_in[k].
+template <int R>
+__global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan sp) {
+    __shared__ float rsp[4];
+    const int tid = threadIdx.x;
+    const int64_t chain = blockIdx.x;
+    const int64_t bi = chain / a.H, hi = chain % a.H, g = hi / (a.H / a.G);
+    const int i = tid % kHalf;  // this thread's rotation channel
+    float lo[16], hiv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int p = (tid + kThreads * k) / kHalf;
+        lo[k] = a.h0 ? a.h0[(chain * kP + p) * kN + i] : 0.f;
+        hiv[k] = a.h0 ? a.h0[(chain * kP + p) * kN + i + kHalf] : 0.f;
+    }
+    if (a.has_prev && a.L > 0) {
+        const __bf16 *bp = static_cast<const __bf16 *>(a.Braw_prev) + ((bi * a.G + g) * R) * kN;
+        const __bf16 *xp = static_cast<const __bf16 *>(a.x_prev) + ((bi * a.H + hi) * R) * kP;
+        const int wv = tid >> 6, l = tid & 63;
+        if (wv < R) {
+            const float v0 = (float)bp[wv * kN + 2 * l], v1 = (float)bp[wv * kN + 2 * l + 1];
+            const float ss = wave_sum(v0 * v0 + v1 * v1);
+            if (l == 0) rsp[wv] = __builtin_amdgcn_rsqf(ss * (1.f / kN) + a.eps);
+        }
+        __syncthreads();
+        const int64_t o0 = (bi * a.L) * a.H + hi;
+        const float f = (1.f - a.lam[o0]) * a.dt[o0];
+        const float *bb = a.B_bias + (hi * R) * kN;
+        const float wl = a.B_normw ? a.B_normw[i] : 1.f, wh = a.B_normw ? a.B_normw[i + kHalf] : 1.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int p = (tid + kThreads * k) / kHalf;
+            float sl = 0.f, sh = 0.f;
+            for (int r = 0; r < R; ++r) {
+                const float xv = (float)xp[r * kP + p];
+                sl += ((float)bp[r * kN + i] * rsp[r] * wl + bb[r * kN + i]) * xv;
+                sh += ((float)bp[r * kN + i + kHalf] * rsp[r] * wh + bb[r * kN + i + kHalf]) * xv;
+            }
+            lo[k] += f * sl;
+            hiv[k] += f * sh;
+        }
+    }
+    for (int s = 0; s < sp.nseg; ++s) {
+        float *E = sp.seg_state + (chain * sp.nseg + s) * (kP * kN);
+        const float dec = __expf(sp.seg_decay[chain * sp.nseg + s]);
+        float sn, cn;
+        sincosf(sp.seg_angle[(chain * sp.nseg + s) * kHalf + i], &sn, &cn);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int p = (tid + kThreads * k) / kHalf;
+            const float el = E[p * kN + i], eh = E[p * kN + i + kHalf];
+            E[p * kN + i] = lo[k];
+            E[p * kN + i + kHalf] = hiv[k];
+            const float u = lo[k], v = hiv[k];
+            lo[k] = dec * (cn * u - sn * v) + el;
+            hiv[k] = dec * (sn * u + cn * v) + eh;
+        }
+    }
+}
+
+template <int R>
+hipError_t launch_r(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
+    const int64_t chains = a.b * a.H;
+    if (sp.nseg <= 1) {
+        hipLaunchKernelGGL((scan_mfma_kernel<kFull, R>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp);
+        return hipGetLastError();
+    }
+    const unsigned nblk = (unsigned)(chains * sp.nseg);
+    hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((combine_kernel<R>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool mfma_kernel_available() { return true; }
+
+int mfma_auto_segments(int64_t chains, int64_t nchunks) {
+    // one resident wave of workgroups is 2 per CU; split only when the chains
+    // alone leave most of them idle, and keep segments at least 8 chunks long
+    const int64_t slots = 2 * kCUs;
+    if (chains * 4 >= slots * 3) return 1;
+    int64_t nseg = slots / (chains > 0 ? chains : 1);
+    if (nseg > nchunks / 8) nseg = nchunks / 8;
+    return nseg < 1 ? 1 : (int)nseg;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t mfma_workspace_bytes(int64_t chains, int nseg, int64_t P, int64_t N) {
+    return align256(sizeof(float) * chains * nseg * P * N) + align256(sizeof(float) * chains * nseg) +
+           align256(sizeof(float) * chains * nseg * (N / 2));
+}
+
+void mfma_workspace_carve(void *ws, int64_t chains, int nseg, int64_t P, int64_t N, SplitPlan *sp) {
+    char *p = static_cast<char *>(ws);
+    sp->seg_state = reinterpret_cast<float *>(p);
+    p += align256(sizeof(float) * chains * nseg * P * N);
+    sp->seg_decay = reinterpret_cast<float *>(p);
+    p += align256(sizeof(float) * chains * nseg);
+    sp->seg_angle = reinterpret_cast<float *>(p);
+}
+
+hipError_t launch_scan_mfma(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
+    if (a.b * a.H == 0) return hipSuccess;
+    switch (a.R) {
+        case 1: return launch_r<1>(a, sp, s);
+        case 2: return launch_r<2>(a, sp, s);
+        case 4: return launch_r<4>(a, sp, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace m3i
