@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba-3 SSM mixer core on one MI355X.
+
+A step is one chunked-scan prefill (m3_scan_fwd) of the 1.5B-scale SISO layer
+(batch 8, L 4096, 64 heads x P 64, N 128, chunk 64, bf16 io, fp32 state) over
+inputs already resident in HBM; ``value`` is prefill tokens/s. The same JSON
+line carries the roofline of that kernel (HIP events on its stream), the CPU
+oracle timed on a bounded sample, and the other hot-path figures: MIMO rank-4
+prefill, the long-context MIMO prefill (segment split) followed by 256 decode
+steps, and the decode step for N in {128, 64}, SISO and MIMO R=4.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_DENSE_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, TFLOP/s
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_siso_prefill_1p5b.json")
+KERNEL_SRC = os.path.join(ROOT, "state_space_sequence_amd", "csrc", "m3_scan_mfma.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------- algorithmic counts --
+def prefill_bytes(s) -> int:
+    """Bytes a prefill must move at least once: x and y (io dtype), raw B and C,
+    dt/A/lam, theta, biases, the final state (fp32)."""
+    io = 2 if s.io == "bf16" else 4
+    b, L, H, G, P, N, R = s.batch, s.seqlen, s.nheads, s.ngroups, s.headdim, s.dstate, s.rank
+    return (2 * b * L * H * R * P * io          # x in, y out
+            + 2 * b * L * G * R * N * io        # Braw, Craw
+            + 3 * b * L * H * 4                 # dt, A, lam
+            + b * L * G * (N // 2) * 4          # theta
+            + 2 * H * R * N * 4                 # biases
+            + b * H * P * N * 4)                # final state
+
+
+def prefill_flops(s):
+    """Matrix-core flops of the chunked algorithm (dense and causal), per call:
+    per chunk-head 2 T^2 N (C B^T) + 2 T^2 P (masked product with X) with
+    T = chunk * R rows, plus 2 T N P for the chunk state and 2 T N P for the
+    carried-state output."""
+    T = s.chunk * s.rank
+    nch = -(-s.seqlen // s.chunk) * s.batch * s.nheads
+    inter = 4 * T * s.dstate * s.headdim
+    dense = 2 * T * T * (s.dstate + s.headdim) + inter
+    causal_pairs = s.chunk * (s.chunk + 1) // 2 * s.rank * s.rank
+    causal = 2 * causal_pairs * (s.dstate + s.headdim) + inter
+    return nch * dense, nch * causal
+
+
+def decode_bytes(s) -> int:
+    io = 2 if s.io == "bf16" else 4
+    b, H, G, P, N, R = s.batch, s.nheads, s.ngroups, s.headdim, s.dstate, s.rank
+    return (2 * b * H * P * N * 4               # state read + write
+            + 3 * b * H * R * P * io            # x, x_prev, y
+            + 3 * b * G * R * N * io            # Braw, Craw, Braw_prev
+            + 3 * b * H * 4 + b * G * (N // 2) * 4 + 2 * H * R * N * 4)
+
+
+# ----------------------------------------------------------------- helpers --
+def scan_args(d, s):
+    return (d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"], d["B_bias"], d["C_bias"])
+
+
+def time_prefill(m3, torch, d, s, steps, warmup, y, hf, ws):
+    args = scan_args(d, s)
+    for _ in range(warmup):
+        m3.scan_fwd(*args, chunk=s.chunk, eps=s.eps, y=y, h_final=hf, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for k in range(steps):
+        m3.scan_fwd(*args, chunk=s.chunk, eps=s.eps, y=y, h_final=hf, workspace=ws)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]  # ms per launch group
+    return wall, per
+
+
+def src_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_counters(bytes_alg):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(PMC_FILE) as f:
+            pm = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if pm.get("kernel_src_sha256") != src_digest():
+        return None
+    return pm.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, chains_target):
+    """The oracle as it stands, on a bounded sample: whole sequences of a few
+    (batch, head) chains of the same workload, scaled to the workload's tokens/s."""
+    import numpy as np  # noqa: F401
+    import oracle
+    from state_space_sequence_amd.inputs import make_scan_inputs
+    H = shape.nheads
+    nb = max(1, chains_target // H)
+    s = shape.replace(batch=nb)
+    inp = make_scan_inputs(s, seed=99)
+    cores = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.scan(inp, s, nthreads=cores)
+    dt = time.perf_counter() - t0
+    chains = nb * H
+    frac = chains / (shape.batch * shape.nheads)
+    full_time = dt / frac
+    return {
+        "value": shape.batch * shape.seqlen / full_time,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d of %d (batch, head) chains, full L=%d, fp64 C oracle with OpenMP over chains; "
+                  "%.2f s measured, scaled by %d/%d" % (chains, shape.batch * shape.nheads, shape.seqlen, dt,
+                                                         shape.batch * shape.nheads, chains),
+    }
+
+
+# --------------------------------------------------------------------- main --
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="only the headline prefill")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-chains", type=int, default=128)
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="short run for counter collection: one 512 MiB copy, then 2 prefill steps")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on exactly one GPU (the kernels shard over batch and heads, "
+              "but no multi-GPU path is built); got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from state_space_sequence_amd import m3
+    from state_space_sequence_amd.inputs import WORKLOADS, make_decode_inputs, make_scan_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log("device:", props.name, getattr(props, "gcnArchName", ""), "CUs:", props.multi_processor_count)
+
+    name = "siso_prefill_1p5b"
+    s = WORKLOADS[name]
+    log("generating inputs for", name)
+    inp = make_scan_inputs(s, seed=1)
+    d = m3.to_device(inp, s.io)
+    del inp
+    y = torch.empty_like(d["x"])
+    hf = torch.empty((s.batch, s.nheads, s.headdim, s.dstate), dtype=torch.float32, device=dev)
+    shape_c = m3.scan_shape(d["x"], d["Braw"], s.chunk, s.eps)
+    plan = m3.plan(shape_c)
+    wsb = m3.workspace_bytes(shape_c)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+
+    if args.pmc_run:
+        src = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reference copy: reads and writes exactly 512 MiB
+        torch.cuda.synchronize()
+        time_prefill(m3, torch, d, s, 2, 0, y, hf, ws)
+        print(json.dumps({"pmc_run": True, "copy_bytes": 512 * 1024 * 1024,
+                          "prefill_bytes_alg": prefill_bytes(s)}))
+        return
+
+    log("timing %s: %d warmup + %d steps (plan: kernel %d, %d segment(s), %d workgroups)"
+        % (name, args.warmup, args.steps, plan.kernel, plan.nsegments, plan.workgroups))
+    wall, per = time_prefill(m3, torch, d, s, args.steps, args.warmup, y, hf, ws)
+    ms_step = 1e3 * wall / args.steps
+    tokens = s.batch * s.seqlen
+    value = tokens * args.steps / wall
+    kern_ms = sum(per) / len(per)
+    balg = prefill_bytes(s)
+    fl_dense, fl_causal = prefill_flops(s)
+    achieved = balg / (kern_ms * 1e-3) / 1e9
+    traffic = traffic_from_counters(balg)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "scan_mfma_kernel<full, R=1>", "avg_launch_ms": round(kern_ms, 5),
+            "alg_bytes_per_launch": balg,
+            "mfma_frac_dense": round(fl_dense / (kern_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4),
+            "mfma_frac_causal": round(fl_causal / (kern_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4)}
+    log("prefill: %.4f ms/step, %.3e tokens/s, %.0f GB/s (%.1f%% of HBM peak)"
+        % (kern_ms, value, achieved, 100 * achieved / HBM_PEAK_GBS))
+    del d, y, hf
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        # ---- MIMO rank-4 prefill, same shape
+        for nm in ("mimo4_prefill_1p5b", "mimo4_prefill_long"):
+            sm_ = WORKLOADS[nm]
+            log("generating inputs for", nm)
+            inp = make_scan_inputs(sm_, seed=2)
+            dd = m3.to_device(inp, sm_.io)
+            del inp
+            yy = torch.empty_like(dd["x"])
+            hh = torch.empty((sm_.batch, sm_.nheads, sm_.headdim, sm_.dstate), dtype=torch.float32, device=dev)
+            shp = m3.scan_shape(dd["x"], dd["Braw"], sm_.chunk, sm_.eps)
+            pl = m3.plan(shp)
+            w2 = m3.workspace_bytes(shp)
+            wsp = torch.empty(w2, dtype=torch.uint8, device=dev) if w2 else None
+            wl, pr = time_prefill(m3, torch, dd, sm_, 10, 3, yy, hh, wsp)
+            ms = sum(pr) / len(pr)
+            bb = prefill_bytes(sm_)
+            fd, fc = prefill_flops(sm_)
+            ent = {"tokens_per_s": round(sm_.batch * sm_.seqlen / (ms * 1e-3), 1), "ms": round(ms, 4),
+                   "hbm_frac": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "mfma_frac_dense": round(fd / (ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4),
+                   "mfma_frac_causal": round(fc / (ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4),
+                   "segments": pl.nsegments, "workgroups": pl.workgroups}
+            log(nm, ent)
+            if nm == "mimo4_prefill_long":
+                # 256 decode steps continuing from the prefill's final state
+                sd = sm_.replace(seqlen=1)
+                dinp = make_decode_inputs(sd, seed=5)
+                de = m3.to_device(dinp, sd.io)
+                h = hh.clone()
+                xp, bp = dd["x"][:, -1].contiguous(), dd["Braw"][:, -1].contiguous()
+                ydec = torch.empty_like(de["x"])
+                dargs = (de["x"], de["Braw"], de["Craw"], de["dt"], de["A"], de["lam"], de["theta"],
+                         de["B_bias"], de["C_bias"], h)
+                for _ in range(8):
+                    m3.decode_step(*dargs, x_prev=xp, Braw_prev=bp, y=ydec)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(256):
+                    m3.decode_step(*dargs, x_prev=xp, Braw_prev=bp, y=ydec)
+                e1.record()
+                torch.cuda.synchronize()
+                ent["decode_256_steps_us_per_step"] = round(1e3 * e0.elapsed_time(e1) / 256, 3)
+                log("  then 256 decode steps:", ent["decode_256_steps_us_per_step"], "us/step")
+                del de, h
+            extra[nm] = ent
+            del dd, yy, hh, wsp
+            torch.cuda.empty_cache()
+        # ---- decode steps, cycling 4 state buffers so the 256 MB last-level cache
+        # cannot hold the state between steps
+        for nm in ("decode_siso_n128", "decode_mimo4_n128", "decode_siso_n64", "decode_mimo4_n64"):
+            sd = WORKLOADS[nm]
+            dinp = make_decode_inputs(sd, seed=3)
+            de = m3.to_device(dinp, sd.io)
+            states = [de["h"].clone() for _ in range(4)]
+            ydec = torch.empty_like(de["x"])
+            base = (de["x"], de["Braw"], de["Craw"], de["dt"], de["A"], de["lam"], de["theta"],
+                    de["B_bias"], de["C_bias"])
+            for k in range(8):
+                m3.decode_step(*base, states[k % 4], x_prev=de["x_prev"], Braw_prev=de["Braw_prev"], y=ydec)
+            torch.cuda.synchronize()
+            reps = 40
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            evs[0].record()
+            for k in range(reps):
+                m3.decode_step(*base, states[k % 4], x_prev=de["x_prev"], Braw_prev=de["Braw_prev"], y=ydec)
+                evs[k + 1].record()
+            torch.cuda.synchronize()
+            tms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(reps))
+            med = tms[reps // 2]
+            bb = decode_bytes(sd)
+            ent = {"us_per_step": round(1e3 * med, 2), "p10_us": round(1e3 * tms[reps // 10], 2),
+                   "p90_us": round(1e3 * tms[(9 * reps) // 10], 2),
+                   "hbm_frac": round(bb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bb}
+            log(nm, ent)
+            extra[nm] = ent
+            del de, states
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(s, args.cpu_chains)
+        log("cpu oracle:", cpu)
+
+    out = {
+        "metric": "SSM prefill tokens/s (%MFMA peak) + decode us/step (%HBM BW), SISO & MIMO R=4",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": s.batch, "seqlen": s.seqlen, "nheads": s.nheads,
+                   "headdim": s.headdim, "dstate": s.dstate, "rank": s.rank, "chunk": s.chunk,
+                   "io": s.io, "state": "fp32"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
