@@ -10,12 +10,14 @@
 // The step is bound by HBM: the fp32 state is read and written once (arithmetic
 // intensity ~2.5 flop/byte for SISO, ~2.5 R for MIMO; §3.3 "decode arithmetic
 // intensity"). One workgroup owns one (batch, head) state [P, N]. Each thread
-// keeps one quad of state columns n..n+3 and the matching quad of the other
-// half (n + N/2), so a rotation pair never leaves a thread; the per-column
-// B, C, B_prev values of that quad stay in registers while the thread walks the
-// rows p. Rows are streamed as 16-byte loads/stores: 64 lanes cover
-// contiguous N/2-float half-rows. y for a row is reduced across the N/8 lanes
-// that share it.
+// owns V consecutive state columns n..n+V-1 of the first half and the matching
+// columns of the second half (n + N/2), so a rotation pair never leaves a
+// thread; the per-column B, C, B_prev coefficients of those columns stay in
+// registers while the thread walks rows p. A wave covers contiguous half-rows,
+// so every state access is a coalesced V*4-byte vector access. The thread's
+// first batch of state rows is requested before the per-head set-up (BCNorm,
+// sincos), so that set-up overlaps the HBM latency. y for a row is reduced over
+// the N/(2V) lanes that share the row.
 #include "m3_internal.h"
 
 namespace m3i {
@@ -24,16 +26,55 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <bool BF16, int N, int R>
+template <int V>
+struct VecT;
+template <>
+struct VecT<1> {
+    typedef float type;
+};
+template <>
+struct VecT<2> {
+    typedef float2 type;
+};
+template <>
+struct VecT<4> {
+    typedef float4 type;
+};
+
+template <int V>
+__device__ __forceinline__ void unpack(const typename VecT<V>::type &v, float *o) {
+    if constexpr (V == 1) {
+        o[0] = v;
+    } else if constexpr (V == 2) {
+        o[0] = v.x; o[1] = v.y;
+    } else {
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+}
+
+template <int V>
+__device__ __forceinline__ typename VecT<V>::type pack(const float *o) {
+    if constexpr (V == 1)
+        return o[0];
+    else if constexpr (V == 2)
+        return make_float2(o[0], o[1]);
+    else
+        return make_float4(o[0], o[1], o[2], o[3]);
+}
+
+template <bool BF16, int N, int R, int V>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     constexpr int HALF = N / 2;
-    constexpr int NQ = N / 8;  // quads per half row; lanes that share one row p
-    static_assert(NQ >= 2 && NQ <= 32 && (64 % NQ) == 0, "N must be 16..256");
+    constexpr int NQ = HALF / V;            // lanes that share one row p
+    constexpr int ROWS = kThreads / NQ;     // rows covered per pass of the workgroup
+    constexpr int KB = (V == 4) ? 4 : 8;    // passes whose state is held in registers at once
+    static_assert(NQ >= 2 && NQ <= 64 && (64 % NQ) == 0, "unsupported N/V");
+    typedef typename VecT<V>::type vec;
 
     extern __shared__ float sm[];
-    float *sB = sm;              // [R][N]   normalised B_t
-    float *sC = sB + R * N;      // [R][N]   normalised C_t
-    float *sBp = sC + R * N;     // [R][N]   normalised B_{t-1}
+    float *sB = sm;              // [R][N]   raw, then normalised B_t
+    float *sC = sB + R * N;      // [R][N]   C_t
+    float *sBp = sC + R * N;     // [R][N]   B_{t-1}
     float *sx = sBp + R * N;     // [R][P]
     float *sxp = sx + R * a.P;   // [R][P]
     float *scs = sxp + R * a.P;  // [HALF] cos
@@ -45,6 +86,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int64_t bi = bh / a.H, hi = bh % a.H;
     const int64_t g = hi / (a.H / a.G);
     const int P = (int)a.P;
+    const int q = tid % NQ;
+    const int n0 = V * q;
+    const int prow = tid / NQ;
+    const int passes = (P + ROWS - 1) / ROWS;
+    float *hbase = a.h + bh * (int64_t)P * N;
+
+    // ---- first batch of state rows: in flight during the set-up below
+    vec lo[KB], hiv[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        const int p = prow + k * ROWS;
+        if (k < passes && p < P) {
+            lo[k] = *reinterpret_cast<const vec *>(hbase + (int64_t)p * N + n0);
+            hiv[k] = *reinterpret_cast<const vec *>(hbase + (int64_t)p * N + HALF + n0);
+        }
+    }
 
     // ---- raw rows into LDS
     const int64_t rowBC = (bi * a.G + g) * R * N;
@@ -79,16 +136,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     __syncthreads();
 
     const float alpha = expf(d * Av);
-    const float beta = (1.0f - lm) * d * alpha;
+    const float beta = a.has_prev ? (1.0f - lm) * d * alpha : 0.f;
     const float gamma = lm * d;
 
-    // ---- this thread's column quad: n0..n0+3 and HALF+n0..HALF+n0+3
-    const int q = tid % NQ;
-    const int n0 = 4 * q;
-    float bl[R][4], bh_[R][4], cl[R][4], ch[R][4], pl[R][4], ph[R][4];
-    float cs[4], sn[4];
+    // ---- this thread's columns: coefficients in registers
+    float bl[R][V], bhc[R][V], cl[R][V], ch[R][V], pl[R][V], ph[R][V];
+    float cs[V], sn[V];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < V; ++k) {
         cs[k] = scs[n0 + k];
         sn[k] = ssn[n0 + k];
     }
@@ -97,71 +152,81 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const float *bb = a.B_bias + (hi * R + r) * N;
         const float *cb = a.C_bias + (hi * R + r) * N;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < V; ++k) {
             const int nl = n0 + k, nh = HALF + n0 + k;
             const float wbl = a.B_normw ? a.B_normw[nl] : 1.f, wbh = a.B_normw ? a.B_normw[nh] : 1.f;
             const float wcl = a.C_normw ? a.C_normw[nl] : 1.f, wch = a.C_normw ? a.C_normw[nh] : 1.f;
-            bl[r][k] = sB[r * N + nl] * srs[r] * wbl + bb[nl];
-            bh_[r][k] = sB[r * N + nh] * srs[r] * wbh + bb[nh];
+            bl[r][k] = gamma * (sB[r * N + nl] * srs[r] * wbl + bb[nl]);
+            bhc[r][k] = gamma * (sB[r * N + nh] * srs[r] * wbh + bb[nh]);
             cl[r][k] = sC[r * N + nl] * srs[R + r] * wcl + cb[nl];
             ch[r][k] = sC[r * N + nh] * srs[R + r] * wch + cb[nh];
-            pl[r][k] = sBp[r * N + nl] * srs[2 * R + r] * wbl + bb[nl];
-            ph[r][k] = sBp[r * N + nh] * srs[2 * R + r] * wbh + bb[nh];
+            pl[r][k] = beta * (sBp[r * N + nl] * srs[2 * R + r] * wbl + bb[nl]);
+            ph[r][k] = beta * (sBp[r * N + nh] * srs[2 * R + r] * wbh + bb[nh]);
         }
     }
-    const float betae = a.has_prev ? beta : 0.f;
 
     // ---- stream the state rows
-    float *hbase = a.h + bh * (int64_t)P * N;
     const int64_t ybase = rowX;  // y has the x layout
-    for (int e = tid; e < P * NQ; e += kThreads) {
-        const int p = e / NQ;
-        float4 *rowp = reinterpret_cast<float4 *>(hbase + (int64_t)p * N);
-        float4 lo = rowp[q];
-        float4 hi4 = rowp[NQ + q];
-        float xv[R], xpv[R];
+    for (int kb = 0; kb < passes; kb += KB) {
+        if (kb > 0) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            xv[r] = sx[r * P + p];
-            xpv[r] = sxp[r * P + p];
+            for (int k = 0; k < KB; ++k) {
+                const int p = prow + (kb + k) * ROWS;
+                if (kb + k < passes && p < P) {
+                    lo[k] = *reinterpret_cast<const vec *>(hbase + (int64_t)p * N + n0);
+                    hiv[k] = *reinterpret_cast<const vec *>(hbase + (int64_t)p * N + HALF + n0);
+                }
+            }
         }
-        float l[4] = {lo.x, lo.y, lo.z, lo.w};
-        float h[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
-        float yacc[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) yacc[r] = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float u = alpha * l[k], v = alpha * h[k];
-            float su = 0.f, sv = 0.f, gu = 0.f, gv = 0.f;
+        for (int k = 0; k < KB; ++k) {
+            const int p = prow + (kb + k) * ROWS;
+            // rows past P: the whole NQ-lane group is out together, so the
+            // shuffles below stay inside active groups
+            if (kb + k >= passes || p >= P) continue;
+            float xv[R], xpv[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                su += pl[r][k] * xpv[r];
-                sv += ph[r][k] * xpv[r];
-                gu += bl[r][k] * xv[r];
-                gv += bh_[r][k] * xv[r];
+                xv[r] = sx[r * P + p];
+                xpv[r] = sxp[r * P + p];
             }
-            u += betae * su;
-            v += betae * sv;
-            const float nu = cs[k] * u - sn[k] * v + gamma * gu;
-            const float nv = sn[k] * u + cs[k] * v + gamma * gv;
-            l[k] = nu;
-            h[k] = nv;
+            float l[V], h[V];
+            unpack<V>(lo[k], l);
+            unpack<V>(hiv[k], h);
+            float yacc[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) yacc[r] += cl[r][k] * nu + ch[r][k] * nv;
-        }
-        rowp[q] = make_float4(l[0], l[1], l[2], l[3]);
-        rowp[NQ + q] = make_float4(h[0], h[1], h[2], h[3]);
+            for (int r = 0; r < R; ++r) yacc[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float v = yacc[r];
+            for (int c = 0; c < V; ++c) {
+                float u = alpha * l[c], v = alpha * h[c];
+                float gu = 0.f, gv = 0.f;
 #pragma unroll
-            for (int o = NQ / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-            yacc[r] = v;
-        }
-        if (q == 0) {
+                for (int r = 0; r < R; ++r) {
+                    u += pl[r][c] * xpv[r];
+                    v += ph[r][c] * xpv[r];
+                    gu += bl[r][c] * xv[r];
+                    gv += bhc[r][c] * xv[r];
+                }
+                const float nu = cs[c] * u - sn[c] * v + gu;
+                const float nv = sn[c] * u + cs[c] * v + gv;
+                l[c] = nu;
+                h[c] = nv;
 #pragma unroll
-            for (int r = 0; r < R; ++r) st_io<BF16>(a.y, ybase + r * P + p, yacc[r]);
+                for (int r = 0; r < R; ++r) yacc[r] += cl[r][c] * nu + ch[r][c] * nv;
+            }
+            *reinterpret_cast<vec *>(hbase + (int64_t)p * N + n0) = pack<V>(l);
+            *reinterpret_cast<vec *>(hbase + (int64_t)p * N + HALF + n0) = pack<V>(h);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float v = yacc[r];
+#pragma unroll
+                for (int o = NQ / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+                yacc[r] = v;
+            }
+            if (q == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) st_io<BF16>(a.y, ybase + r * P + p, yacc[r]);
+            }
         }
     }
 }
@@ -171,17 +236,11 @@ hipError_t launch_n(const DecodeArgs &a, hipStream_t s) {
     const size_t smem = sizeof(float) * (3 * a.R * N + 2 * a.R * a.P + N + 3 * a.R);
     dim3 grid((unsigned)(a.b * a.H)), block(kThreads);
     switch (a.R) {
-#define M3_CASE_R(RR)                                                                     \
-    case RR:                                                                             \
-        hipLaunchKernelGGL((decode_kernel<BF16, N, RR>), grid, block, smem, s, a);      \
-        break;
-        M3_CASE_R(1)
-        M3_CASE_R(2)
-        M3_CASE_R(3)
-        M3_CASE_R(4)
-#undef M3_CASE_R
-        default:
-            return hipErrorInvalidValue;
+        case 1: hipLaunchKernelGGL((decode_kernel<BF16, N, 1, 4>), grid, block, smem, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<BF16, N, 2, 2>), grid, block, smem, s, a); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<BF16, N, 3, 2>), grid, block, smem, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<BF16, N, 4, 2>), grid, block, smem, s, a); break;
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

@@ -89,20 +89,19 @@ __device__ __forceinline__ void sincos_rad(float x, float &s, float &c) {
     c = __builtin_amdgcn_cosf(rev);
 }
 
-struct Smem {
-    __bf16 Bb[kRows * kLdN];  // B_bar [row][n]
-    __bf16 Bt[kN * kLdR];     // B_bar * cst, [n][row]
-    __bf16 Xt[kP * kLdR];     // X, [p][row]
-    __bf16 St[kP * kLdN];     // bf16 state, [p][n]
-    float l2cs[kRows];        // per row: log2(e) * chunk-local cumulative log decay
-    float wgt[kRows];         // per row: folded weight w of the row's token
-    float gam[kRows];         // per row: gamma
-    float eoff[kRows];        // per row: exp(cs) (carried-state output scale)
-    float angtot[4][kHalf];   // per wave: angle total of its rows
-    float carry[kHalf];       // cumulative angle before the current chunk
-    float bias[2][4][kN];     // B / C bias of this head, per rank
-    float normw[2][kN];       // BCNorm gains (ones when absent)
-    float rsp[4];             // 1/rms of the previous token's raw B rows
+struct alignas(16) Smem {
+    alignas(16) __bf16 Bb[kRows * kLdN];  // B_bar [row][n]
+    alignas(16) __bf16 Bt[kN * kLdR];     // B_bar * cst, [n][row]
+    alignas(16) __bf16 Xt[kP * kLdR];     // X, [p][row]
+    alignas(16) __bf16 St[kP * kLdN];     // bf16 state, [p][n]
+    alignas(16) float l2cs[kRows];        // per row: log2(e) * chunk-local cumulative log decay
+    alignas(16) float wgt[kRows];         // per row: folded weight w of the row's token
+    alignas(16) float gam[kRows];         // per row: gamma
+    alignas(16) float eoff[kRows];        // per row: exp(cs) (carried-state output scale)
+    alignas(16) float angtot[4][kHalf];   // per wave: angle total of its rows
+    alignas(16) float carry[kHalf];       // cumulative angle before the current chunk
+    alignas(16) float bias[2][4][kN];     // B / C bias of this head, per rank
+    alignas(16) float normw[2][kN];       // BCNorm gains (ones when absent)
 };
 
 struct ChainPos {
@@ -247,6 +246,40 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             av = a.A[o];
             lm = a.lam[o];
         }
+        // ---- this lane's row: raw B, C, theta, X (MFMA fragment layout)
+        const bool valid = t_row < nv;
+        const int64_t tok = bi * L + c0 + t_row;
+        bf16x8 rb[4], rc[4], xf[2];
+        f32x4 th[4];
+        if (valid) {
+            const bf16x8 *pb_ = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.Braw) +
+                                                                 ((tok * G + g) * R + r_row) * kN);
+            const bf16x8 *pc_ = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.Craw) +
+                                                                 ((tok * G + g) * R + r_row) * kN);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                rb[ks] = pb_[4 * ks + lg];
+                if constexpr (MODE != kPass1) rc[ks] = pc_[4 * ks + lg];
+            }
+            const f32x4 *pt = reinterpret_cast<const f32x4 *>(a.theta + (tok * G + g) * kHalf);
+            th[0] = pt[2 * lg];
+            th[1] = pt[2 * lg + 1];
+            th[2] = pt[8 + 2 * lg];
+            th[3] = pt[8 + 2 * lg + 1];
+            const bf16x8 *px = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.x) +
+                                                                ((tok * H + hi) * R + r_row) * kP);
+            xf[0] = px[lg];
+            xf[1] = px[4 + lg];
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                rb[ks] = bf16x8{};
+                rc[ks] = bf16x8{};
+                th[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            xf[0] = bf16x8{};
+            xf[1] = bf16x8{};
+        }
         float cs = d * av;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -265,42 +298,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         const float wt = gm + look;
         const float cs_end = __shfl(cs, 63, 64);
         const float cst = __expf(cs_end - cs) * wt;
-
-        // ---- this lane's row: raw B, C, theta, X
-        const bool valid = t_row < nv;
-        const int64_t tok = bi * L + c0 + t_row;
-        bf16x8 rb[4], rc[4];
-        f32x4 th[4];
-        bf16x8 xr[2];
-        if (valid) {
-            const bf16x8 *pb_ = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.Braw) +
-                                                                 ((tok * G + g) * R + r_row) * kN);
-            const bf16x8 *pc_ = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.Craw) +
-                                                                 ((tok * G + g) * R + r_row) * kN);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                rb[ks] = pb_[4 * ks + lg];
-                if constexpr (MODE != kPass1) rc[ks] = pc_[4 * ks + lg];
-            }
-            const f32x4 *pt = reinterpret_cast<const f32x4 *>(a.theta + (tok * G + g) * kHalf);
-            th[0] = pt[2 * lg];
-            th[1] = pt[2 * lg + 1];
-            th[2] = pt[8 + 2 * lg];
-            th[3] = pt[8 + 2 * lg + 1];
-            const bf16x8 *px = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.x) +
-                                                                ((tok * H + hi) * R + r_row) * kP);
-            xr[0] = px[2 * lg];
-            xr[1] = px[2 * lg + 1];
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                rb[ks] = bf16x8{};
-                rc[ks] = bf16x8{};
-                th[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            xr[0] = bf16x8{};
-            xr[1] = bf16x8{};
-        }
         const float d_row = __shfl(d, t_row, 64);
         const float cst_row = __shfl(cst, t_row, 64);
 
@@ -343,18 +340,28 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             for (int k = 0; k < 16; ++k) ph[k] += dpp_row_shr(ph[k], sh);
         if (lr == 15) {
 #pragma unroll
-            for (int k = 0; k < 16; ++k) sm.angtot[w][(k < 8 ? 8 * lg + k : 32 + 8 * lg + k - 8)] = ph[k];
+            for (int h2 = 0; h2 < 2; ++h2) {
+                *reinterpret_cast<f32x4 *>(&sm.angtot[w][32 * h2 + 8 * lg]) =
+                    f32x4{ph[8 * h2 + 0], ph[8 * h2 + 1], ph[8 * h2 + 2], ph[8 * h2 + 3]};
+                *reinterpret_cast<f32x4 *>(&sm.angtot[w][32 * h2 + 8 * lg + 4]) =
+                    f32x4{ph[8 * h2 + 4], ph[8 * h2 + 5], ph[8 * h2 + 6], ph[8 * h2 + 7]};
+            }
         }
         __syncthreads();  // B1
 
         // ---- rotate into the frame of the workgroup's first token
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int i = (k < 8) ? 8 * lg + k : 32 + 8 * lg + k - 8;
-            float off = sm.carry[i];
-            for (int w2 = 0; w2 < w; ++w2) off += sm.angtot[w2][i];
-            ph[k] += off;
-        }
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int q4 = 0; q4 < 2; ++q4) {
+                const int i0 = 32 * h2 + 8 * lg + 4 * q4;
+                f32x4 off = *reinterpret_cast<const f32x4 *>(&sm.carry[i0]);
+                if (w > 0) off += *reinterpret_cast<const f32x4 *>(&sm.angtot[0][i0]);
+                if (w > 1) off += *reinterpret_cast<const f32x4 *>(&sm.angtot[1][i0]);
+                if (w > 2) off += *reinterpret_cast<const f32x4 *>(&sm.angtot[2][i0]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ph[8 * h2 + 4 * q4 + k] += off[k];
+            }
         if (w == 0) {
             // per-row scalar tables for the mask and the carried-state output
             const int tl = l / R;
@@ -365,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             sm.eoff[l] = __expf(cs_l);
             newcarry = sm.carry[l] + sm.angtot[0][l] + sm.angtot[1][l] + sm.angtot[2][l] + sm.angtot[3][l];
         }
-        bf16x8 bfr[4], cfr[4];
+        bf16x8 bfr[4], cfr[4], bsc[4];
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
@@ -373,35 +380,38 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 const int i0 = 32 * ks2 + 8 * lg + 4 * jh;  // first of 4 channels
                 const f32x4 blo = *reinterpret_cast<const f32x4 *>(&sm.bias[0][r_row][i0]);
                 const f32x4 bhi = *reinterpret_cast<const f32x4 *>(&sm.bias[0][r_row][i0 + 64]);
-                f32x4 wbl = {1.f, 1.f, 1.f, 1.f}, wbh = {1.f, 1.f, 1.f, 1.f};
+                f32x4 clo = {0.f, 0.f, 0.f, 0.f}, chi = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (MODE != kPass1) {
+                    clo = *reinterpret_cast<const f32x4 *>(&sm.bias[1][r_row][i0]);
+                    chi = *reinterpret_cast<const f32x4 *>(&sm.bias[1][r_row][i0 + 64]);
+                }
+                f32x4 abl = {rsb, rsb, rsb, rsb}, abh = abl, acl = {rsc, rsc, rsc, rsc}, ach = acl;
                 if (has_w) {
-                    wbl = *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0]);
-                    wbh = *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0 + 64]);
+                    abl *= *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0]);
+                    abh *= *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0 + 64]);
+                    acl *= *reinterpret_cast<const f32x4 *>(&sm.normw[1][i0]);
+                    ach *= *reinterpret_cast<const f32x4 *>(&sm.normw[1][i0 + 64]);
                 }
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int j = 4 * jh + jj;
-                    const int i = i0 + jj;
                     float sn, cn;
                     sincos_rad(ph[8 * ks2 + j], sn, cn);
-                    const float bl = (float)rb[ks2][j] * (rsb * wbl[jj]) + blo[jj];
-                    const float bh = (float)rb[ks2 + 2][j] * (rsb * wbh[jj]) + bhi[jj];
-                    float bbl = cn * bl + sn * bh;
-                    float bbh = cn * bh - sn * bl;
-                    if (!valid) { bbl = 0.f; bbh = 0.f; }
+                    const float bl = (float)rb[ks2][j] * abl[jj] + blo[jj];
+                    const float bh = (float)rb[ks2 + 2][j] * abh[jj] + bhi[jj];
+                    // rows past the end of the sequence need no zeroing: their
+                    // weights w, gamma and cst are 0 and their outputs are not stored
+                    const float bbl = cn * bl + sn * bh;
+                    const float bbh = cn * bh - sn * bl;
                     bfr[ks2][j] = (__bf16)bbl;
                     bfr[ks2 + 2][j] = (__bf16)bbh;
-                    // transposed, scaled copy for the state update
-                    sm.Bt[i * kLdR + row] = (__bf16)(bbl * cst_row);
-                    sm.Bt[(i + 64) * kLdR + row] = (__bf16)(bbh * cst_row);
+                    bsc[ks2][j] = (__bf16)(bbl * cst_row);
+                    bsc[ks2 + 2][j] = (__bf16)(bbh * cst_row);
                     if constexpr (MODE != kPass1) {
-                        const float clo = sm.bias[1][r_row][i], chi = sm.bias[1][r_row][i + 64];
-                        const float wcl = has_w ? sm.normw[1][i] : 1.f, wch = has_w ? sm.normw[1][i + 64] : 1.f;
-                        const float cl = (float)rc[ks2][j] * (rsc * wcl) + clo;
-                        const float ch = (float)rc[ks2 + 2][j] * (rsc * wch) + chi;
-                        float ccl = cn * cl + sn * ch;
-                        float cch = cn * ch - sn * cl;
-                        if (!valid) { ccl = 0.f; cch = 0.f; }
+                        const float cl = (float)rc[ks2][j] * acl[jj] + clo[jj];
+                        const float ch = (float)rc[ks2 + 2][j] * ach[jj] + chi[jj];
+                        const float ccl = cn * cl + sn * ch;
+                        const float cch = cn * ch - sn * cl;
                         cfr[ks2][j] = (__bf16)ccl;
                         cfr[ks2 + 2][j] = (__bf16)cch;
                     }
@@ -413,9 +423,29 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             for (int ks = 0; ks < 4; ++ks)
                 *reinterpret_cast<bf16x8 *>(&sm.Bb[row * kLdN + 32 * ks + 8 * lg]) = bfr[ks];
         }
-        // X transposed: this lane holds X[row][16lg .. 16lg+15]
+        // ---- transposed copies through the matrix core: T = frag x selection,
+        // exact for bf16 operands. Output lane holds rows 16w + 4lg..+3 of column lr.
+        {
+            // selection fragments: E_h[k][c] = 1 when k == 16h + c (k = 8lg + j)
+            bf16x8 e0, e1;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) sm.Xt[(16 * lg + k) * kLdR + row] = xr[k >> 3][k & 7];
+            for (int j = 0; j < 8; ++j) {
+                e0[j] = (__bf16)((8 * lg + j == lr) ? 1.f : 0.f);
+                e1[j] = (__bf16)((8 * lg + j == 16 + lr) ? 1.f : 0.f);
+            }
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const f32x4 t = mfma(bsc[nb >> 1], (nb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f});
+                const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
+                *reinterpret_cast<bf16x4 *>(&sm.Bt[(16 * nb + lr) * kLdR + 16 * w + 4 * lg]) = v;
+            }
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const f32x4 t = mfma(xf[pb >> 1], (pb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f});
+                const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
+                *reinterpret_cast<bf16x4 *>(&sm.Xt[(16 * pb + lr) * kLdR + 16 * w + 4 * lg]) = v;
+            }
+        }
         __syncthreads();  // B2
 
         if constexpr (MODE != kPass1) {
@@ -440,17 +470,20 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             const float l2t = sm.l2cs[row], gmt = sm.gam[row];
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
-                if (sb <= w) {
+                if (sb < w) {
+                    // every s token precedes every t token
+                    const f32x4 l2s = *reinterpret_cast<const f32x4 *>(&sm.l2cs[16 * sb + 4 * lg]);
+                    const f32x4 ws = *reinterpret_cast<const f32x4 *>(&sm.wgt[16 * sb + 4 * lg]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sT[sb][j] *= __builtin_amdgcn_exp2f(l2t - l2s[j]) * ws[j];
+                } else if (sb == w) {
                     const f32x4 l2s = *reinterpret_cast<const f32x4 *>(&sm.l2cs[16 * sb + 4 * lg]);
                     const f32x4 ws = *reinterpret_cast<const f32x4 *>(&sm.wgt[16 * sb + 4 * lg]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int stok = (16 * sb + 4 * lg + j) / R;
-                        float m = 0.f;
-                        if (stok < ttok)
-                            m = __builtin_amdgcn_exp2f(l2t - l2s[j]) * ws[j];
-                        else if (stok == ttok)
-                            m = gmt;
+                        const float e = __builtin_amdgcn_exp2f(fminf(l2t - l2s[j], 0.f)) * ws[j];
+                        const float m = (stok < ttok) ? e : ((stok == ttok) ? gmt : 0.f);
                         sT[sb][j] *= m;
                     }
                 }
@@ -463,43 +496,32 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     pfr[m2][j] = (__bf16)sT[2 * m2][j];
                     pfr[m2][j + 4] = (__bf16)sT[2 * m2 + 1][j];
                 }
-            // ---- Y = diag(exp(cs)) C_bar St + P X
-            f32x4 yacc[4];
-            const f32x4 eo = *reinterpret_cast<const f32x4 *>(&sm.eoff[16 * w + 4 * lg]);
+            // ---- Y^T = (St C_bar^T) diag(exp(cs)) + X^T P^T ; lane: column t = row, rows p
+            const float eo = sm.eoff[row];
+            __bf16 *yp = static_cast<__bf16 *>(a.y);
+            const int64_t ybase = (((bi * L + c0 + t_row) * H + hi) * R + r_row) * kP;
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) {
                 const int p = 16 * pb + lr;
                 f32x4 yv = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(&sm.St[p * kLdN + 32 * ks + 8 * lg]);
-                    yv = mfma(cfr[ks], bv, yv);
+                    const bf16x8 sv = *reinterpret_cast<const bf16x8 *>(&sm.St[p * kLdN + 32 * ks + 8 * lg]);
+                    yv = mfma(sv, cfr[ks], yv);
                 }
-                yv[0] *= eo[0];
-                yv[1] *= eo[1];
-                yv[2] *= eo[2];
-                yv[3] *= eo[3];
+                yv *= eo;
 #pragma unroll
                 for (int m2 = 0; m2 < 2; ++m2) {
                     if (2 * m2 <= w) {
                         const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(&sm.Xt[p * kLdR + 32 * m2 + 4 * lg]);
                         const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(&sm.Xt[p * kLdR + 32 * m2 + 16 + 4 * lg]);
-                        const bf16x8 bv = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-                        yv = mfma(pfr[m2], bv, yv);
+                        const bf16x8 xv = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                        yv = mfma(xv, pfr[m2], yv);
                     }
                 }
-                yacc[pb] = yv;
-            }
-            // ---- store y rows 16w + 4lg + j, column p
-            __bf16 *yp = static_cast<__bf16 *>(a.y);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rrow = 16 * w + 4 * lg + j;
-                const int rt = rrow / R, rr = rrow % R;
-                if (rt < nv) {
-                    const int64_t base = (((bi * L + c0 + rt) * H + hi) * R + rr) * kP;
-#pragma unroll
-                    for (int pb = 0; pb < 4; ++pb) yp[base + 16 * pb + lr] = (__bf16)yacc[pb][j];
+                if (valid) {
+                    const bf16x4 o = {(__bf16)yv[0], (__bf16)yv[1], (__bf16)yv[2], (__bf16)yv[3]};
+                    *reinterpret_cast<bf16x4 *>(yp + ybase + 16 * pb + 4 * lg) = o;
                 }
             }
             __syncthreads();  // B3: St and Bb reads done
