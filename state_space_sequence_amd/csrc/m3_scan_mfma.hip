@@ -131,6 +131,109 @@ __device__ __forceinline__ ChainPos chain_of_block(const ScanArgs &a, const Spli
     return cp;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: Hillis-Steele
+// inside each 16-lane row, then the row totals carried by row broadcasts.
+__device__ __forceinline__ float wave_incl_scan(float v) {
+    v += dpp_row_shr(v, 1);
+    v += dpp_row_shr(v, 2);
+    v += dpp_row_shr(v, 4);
+    v += dpp_row_shr(v, 8);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));  // row_bcast:15
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return v;
+}
+
+// Per-lane constants of the chunk loop (fixed for the workgroup's lifetime).
+struct Lane {
+    int l, lr, lg, row, r_row, t_row;
+    int offBC;  // element offset of this lane's slice of a chunk's raw B/C block
+    int offTh;  // element offset of this lane's theta row in a chunk's theta block
+    int offX;   // element offset of this lane's row in a chunk's x (and y) block
+};
+
+template <int R>
+__device__ __forceinline__ Lane make_lane(int l, int w, int64_t G, int64_t H) {
+    Lane ln;
+    ln.l = l;
+    ln.lr = l & 15;
+    ln.lg = l >> 4;
+    ln.row = 16 * w + ln.lr;
+    ln.r_row = ln.row % R;
+    ln.t_row = ln.row / R;
+    ln.offBC = (ln.t_row * (int)G * R + ln.r_row) * kN + 8 * ln.lg;
+    ln.offTh = ln.t_row * (int)G * kHalf;
+    ln.offX = (ln.t_row * (int)H * R + ln.r_row) * kP;
+    return ln;
+}
+
+// Uniform (per workgroup and chunk) bases of a chunk's blocks.
+struct ChunkBase {
+    const __bf16 *B, *Cr, *x;
+    const float *th;
+    const float *dt, *A, *lam;
+    __bf16 *y;
+};
+
+template <int R>
+__device__ __forceinline__ ChunkBase chunk_base(const ScanArgs &a, int64_t bi, int64_t hi, int64_t g, int64_t c0) {
+    ChunkBase cb;
+    const int64_t t0 = bi * a.L + c0;  // first token of the chunk
+    cb.B = static_cast<const __bf16 *>(a.Braw) + (t0 * a.G + g) * R * kN;
+    cb.Cr = static_cast<const __bf16 *>(a.Craw) + (t0 * a.G + g) * R * kN;
+    cb.th = a.theta + (t0 * a.G + g) * kHalf;
+    cb.x = static_cast<const __bf16 *>(a.x) + (t0 * a.H + hi) * R * kP;
+    cb.y = static_cast<__bf16 *>(a.y) + (t0 * a.H + hi) * R * kP;
+    cb.dt = a.dt + t0 * a.H + hi;
+    cb.A = a.A + t0 * a.H + hi;
+    cb.lam = a.lam + t0 * a.H + hi;
+    return cb;
+}
+
+// Global inputs of one chunk for one lane: its row of raw B and C (MFMA fragment
+// layout) and, in lanes 0..C-1, the token scalars.
+struct ChunkRegs {
+    bf16x8 rb[4], rc[4];
+    float d, av, lm;
+};
+
+template <int MODE>
+__device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, int nv, int64_t H,
+                                           ChunkRegs &cr) {
+    cr.d = 0.f;
+    cr.av = 0.f;
+    cr.lm = 0.f;
+    if (ln.l < nv) {
+        const int o = ln.l * (int)H;
+        cr.d = cb.dt[o];
+        cr.av = cb.A[o];
+        cr.lm = cb.lam[o];
+    }
+    if (ln.t_row < nv) {
+        const bf16x8 *pb = reinterpret_cast<const bf16x8 *>(cb.B + ln.offBC);
+        const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + ln.offBC);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            cr.rb[ks] = pb[4 * ks];
+            if constexpr (MODE != kPass1) cr.rc[ks] = pc[4 * ks];
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            cr.rb[ks] = bf16x8{};
+            cr.rc[ks] = bf16x8{};
+        }
+    }
+}
+
+// bf16x8 fragment with a single 1.0 at slot j (none when j is outside 0..7)
+__device__ __forceinline__ bf16x8 unit_fragment(int j) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) u[k] = (j == 2 * k ? 0x3F80u : 0u) | (j == 2 * k + 1 ? 0x3F800000u : 0u);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
 template <int MODE, int R>
 __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, SplitPlan sp) {
     constexpr int C = kRows / R;  // tokens per chunk
@@ -143,6 +246,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
     const int64_t bi = chain / a.H, hi = chain % a.H, g = hi / (a.H / a.G);
     const int64_t L = a.L, H = a.H, G = a.G;
     const bool has_w = a.B_normw != nullptr || a.C_normw != nullptr;
+
+    const int l = tid & 63, lr = l & 15, lg = l >> 4;
 
     // ---------------------------------------------------------------- prologue
     for (int e = tid; e < 2 * R * kN; e += kThreads) {
@@ -162,67 +267,67 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) acc[q][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    {
-        const int l = tid & 63, lr = l & 15, lg = l >> 4;
-        if constexpr (MODE == kFull || MODE == kPass2) {
-            const float *src = nullptr;
-            if (MODE == kFull)
-                src = a.h0 ? a.h0 + chain * (kP * kN) : nullptr;
-            else
-                src = sp.seg_state + (chain * sp.nseg + pos.seg) * (kP * kN);
-            if (src) {
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int pb = 0; pb < 4; ++pb) {
-                        const int n0 = 16 * (w + 4 * q) + 4 * lg, p = 16 * pb + lr;
-                        acc[q][pb] = *reinterpret_cast<const f32x4 *>(src + p * kN + n0);
-                    }
-            }
-        }
-        if constexpr (MODE == kFull) {
-            if (a.has_prev && L > 0) {
-                // fold (1 - lam_0) dt_0 B_{-1} x_{-1}^T into the starting state
-                const __bf16 *bp = static_cast<const __bf16 *>(a.Braw_prev) + ((bi * G + g) * R) * kN;
-                const __bf16 *xp = static_cast<const __bf16 *>(a.x_prev) + ((bi * H + hi) * R) * kP;
-                float rsr[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const float v0 = (float)bp[r * kN + 2 * l], v1 = (float)bp[r * kN + 2 * l + 1];
-                    rsr[r] = __builtin_amdgcn_rsqf(wave_sum(v0 * v0 + v1 * v1) * (1.f / kN) + a.eps);
-                }
-                const int64_t o0 = (bi * L) * H + hi;
-                const float f = (1.f - a.lam[o0]) * a.dt[o0];
-                const float *bb = a.B_bias + (hi * R) * kN;
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int pb = 0; pb < 4; ++pb)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int n = 16 * (w + 4 * q) + 4 * lg + j, p = 16 * pb + lr;
-                            const float wn = a.B_normw ? a.B_normw[n] : 1.f;
-                            float s = 0.f;
-#pragma unroll
-                            for (int r = 0; r < R; ++r)
-                                s += ((float)bp[r * kN + n] * rsr[r] * wn + bb[r * kN + n]) * (float)xp[r * kP + p];
-                            acc[q][pb][j] += f * s;
-                        }
-            }
-        }
-        if constexpr (MODE != kPass1) {
-            // bf16 copy of the state for the first chunk's carried-state output
+    if constexpr (MODE == kFull || MODE == kPass2) {
+        const float *src = nullptr;
+        if (MODE == kFull)
+            src = a.h0 ? a.h0 + chain * (kP * kN) : nullptr;
+        else
+            src = sp.seg_state + (chain * sp.nseg + pos.seg) * (kP * kN);
+        if (src) {
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
                 for (int pb = 0; pb < 4; ++pb) {
                     const int n0 = 16 * (w + 4 * q) + 4 * lg, p = 16 * pb + lr;
-                    bf16x4 v = {(__bf16)acc[q][pb][0], (__bf16)acc[q][pb][1], (__bf16)acc[q][pb][2],
-                                (__bf16)acc[q][pb][3]};
-                    *reinterpret_cast<bf16x4 *>(&sm.St[p * kLdN + n0]) = v;
+                    acc[q][pb] = *reinterpret_cast<const f32x4 *>(src + p * kN + n0);
                 }
         }
     }
+    if constexpr (MODE == kFull) {
+        if (a.has_prev && L > 0) {
+            // fold (1 - lam_0) dt_0 B_{-1} x_{-1}^T into the starting state
+            const __bf16 *bp = static_cast<const __bf16 *>(a.Braw_prev) + ((bi * G + g) * R) * kN;
+            const __bf16 *xp = static_cast<const __bf16 *>(a.x_prev) + ((bi * H + hi) * R) * kP;
+            float rsr[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float v0 = (float)bp[r * kN + 2 * l], v1 = (float)bp[r * kN + 2 * l + 1];
+                rsr[r] = __builtin_amdgcn_rsqf(wave_sum(v0 * v0 + v1 * v1) * (1.f / kN) + a.eps);
+            }
+            const int64_t o0 = (bi * L) * H + hi;
+            const float f = (1.f - a.lam[o0]) * a.dt[o0];
+            const float *bb = a.B_bias + (hi * R) * kN;
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int n = 16 * (w + 4 * q) + 4 * lg + j, p = 16 * pb + lr;
+                        const float wn = a.B_normw ? a.B_normw[n] : 1.f;
+                        float s = 0.f;
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            s += ((float)bp[r * kN + n] * rsr[r] * wn + bb[r * kN + n]) * (float)xp[r * kP + p];
+                        acc[q][pb][j] += f * s;
+                    }
+        }
+    }
+    if constexpr (MODE != kPass1) {
+        // bf16 copy of the state for the first chunk's carried-state output
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+                const int n0 = 16 * (w + 4 * q) + 4 * lg, p = 16 * pb + lr;
+                bf16x4 v = {(__bf16)acc[q][pb][0], (__bf16)acc[q][pb][1], (__bf16)acc[q][pb][2],
+                            (__bf16)acc[q][pb][3]};
+                *reinterpret_cast<bf16x4 *>(&sm.St[p * kLdN + n0]) = v;
+            }
+    }
+    // selection fragments for the transposes: E_h[k][c] = 1 when k == 16h + c,
+    // with k = 8lg + slot and c = lr
+    const bf16x8 e0 = unit_fragment(lr - 8 * lg), e1 = unit_fragment(16 + lr - 8 * lg);
     __syncthreads();
 
     float logdecay_total = 0.f;
@@ -231,75 +336,63 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
     for (int64_t c = pos.c_begin; c < pos.c_end; ++c) {
         const int64_t c0 = c * C;
         const int nv = (int)((L - c0) < C ? (L - c0) : C);
+        const ChunkBase cb = chunk_base<R>(a, bi, hi, g, c0);
         // lane-derived indices, recomputed per chunk (see opaque())
-        const int l = opaque(tid & 63);
-        const int lr = l & 15, lg = l >> 4;
-        const int row = 16 * w + lr;  // this lane's row in the rotation stage
-        const int r_row = row % R;
-        const int t_row = row / R;    // its token inside the chunk
+        const Lane ln = make_lane<R>(opaque(tid & 63), w, G, H);
+        const int l = ln.l, lr = ln.lr, lg = ln.lg, row = ln.row, r_row = ln.r_row, t_row = ln.t_row;
+        ChunkRegs cr;
+        load_chunk<MODE>(cb, ln, nv, H, cr);
 
-        // ---- token scalars: lane = token (every wave computes them)
-        float d = 0.f, av = 0.f, lm = 0.f;
-        if (l < nv) {
-            const int64_t o = (bi * L + c0 + l) * H + hi;
-            d = a.dt[o];
-            av = a.A[o];
-            lm = a.lam[o];
-        }
-        // ---- this lane's row: raw B, C, theta, X (MFMA fragment layout)
+        // ---- this chunk's inputs: raw B, C and the token scalars first, then
+        // theta and X, which are used last
         const bool valid = t_row < nv;
-        const int64_t tok = bi * L + c0 + t_row;
+        const float d = cr.d, av = cr.av, lm = cr.lm;
         bf16x8 rb[4], rc[4], xf[2];
         f32x4 th[4];
-        if (valid) {
-            const bf16x8 *pb_ = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.Braw) +
-                                                                 ((tok * G + g) * R + r_row) * kN);
-            const bf16x8 *pc_ = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.Craw) +
-                                                                 ((tok * G + g) * R + r_row) * kN);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                rb[ks] = pb_[4 * ks + lg];
-                if constexpr (MODE != kPass1) rc[ks] = pc_[4 * ks + lg];
-            }
-            const f32x4 *pt = reinterpret_cast<const f32x4 *>(a.theta + (tok * G + g) * kHalf);
+        for (int k = 0; k < 4; ++k) {
+            rb[k] = cr.rb[k];
+            rc[k] = cr.rc[k];
+        }
+        if (valid) {
+            const f32x4 *pt = reinterpret_cast<const f32x4 *>(cb.th + ln.offTh);
             th[0] = pt[2 * lg];
             th[1] = pt[2 * lg + 1];
             th[2] = pt[8 + 2 * lg];
             th[3] = pt[8 + 2 * lg + 1];
-            const bf16x8 *px = reinterpret_cast<const bf16x8 *>(static_cast<const __bf16 *>(a.x) +
-                                                                ((tok * H + hi) * R + r_row) * kP);
+            const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + ln.offX);
             xf[0] = px[lg];
             xf[1] = px[4 + lg];
         } else {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                rb[ks] = bf16x8{};
-                rc[ks] = bf16x8{};
-                th[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            for (int k = 0; k < 4; ++k) th[k] = f32x4{0.f, 0.f, 0.f, 0.f};
             xf[0] = bf16x8{};
             xf[1] = bf16x8{};
         }
-        float cs = d * av;
+        // ---- X^T through the matrix core: T = X-fragment x selection, exact for
+        // bf16 operands; the output lane holds rows 16w + 4lg..+3 of column lr
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float v = __shfl_up(cs, off, 64);
-            if (l >= off) cs += v;
+        for (int pb = 0; pb < 4; ++pb) {
+            const f32x4 t = mfma(xf[pb >> 1], (pb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f});
+            const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
+            *reinterpret_cast<bf16x4 *>(&sm.Xt[(16 * pb + lr) * kLdR + 16 * w + 4 * lg]) = v;
         }
-        const float dn = __shfl_down(d, 1, 64), ln = __shfl_down(lm, 1, 64);
+
+        // ---- token scalars (lane = token): decay prefix, folded weights
+        const float cs = wave_incl_scan(d * av);
+        const float dn = __shfl_down(d, 1, 64), lnx = __shfl_down(lm, 1, 64);
         float look = 0.f;
         if (l + 1 < nv) {
-            look = (1.f - ln) * dn;
+            look = (1.f - lnx) * dn;
         } else if (l + 1 == nv && c0 + nv < L) {
-            const int64_t o1 = (bi * L + c0 + nv) * H + hi;
-            look = (1.f - a.lam[o1]) * a.dt[o1];
+            const int o1 = nv * (int)H;
+            look = (1.f - cb.lam[o1]) * cb.dt[o1];
         }
         const float gm = lm * d;
         const float wt = gm + look;
-        const float cs_end = __shfl(cs, 63, 64);
+        const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
         const float cst = __expf(cs_end - cs) * wt;
         const float d_row = __shfl(d, t_row, 64);
-        const float cst_row = __shfl(cst, t_row, 64);
 
         // ---- BCNorm factors of this row (sum over the 4 lanes that hold it)
         float ssb = 0.f, ssc = 0.f;
@@ -372,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             sm.eoff[l] = __expf(cs_l);
             newcarry = sm.carry[l] + sm.angtot[0][l] + sm.angtot[1][l] + sm.angtot[2][l] + sm.angtot[3][l];
         }
-        bf16x8 bfr[4], cfr[4], bsc[4];
+        bf16x8 bfr[4], cfr[4];
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
@@ -405,8 +498,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     const float bbh = cn * bh - sn * bl;
                     bfr[ks2][j] = (__bf16)bbl;
                     bfr[ks2 + 2][j] = (__bf16)bbh;
-                    bsc[ks2][j] = (__bf16)(bbl * cst_row);
-                    bsc[ks2 + 2][j] = (__bf16)(bbh * cst_row);
                     if constexpr (MODE != kPass1) {
                         const float cl = (float)rc[ks2][j] * acl[jj] + clo[jj];
                         const float ch = (float)rc[ks2 + 2][j] * ach[jj] + chi[jj];
@@ -423,27 +514,17 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             for (int ks = 0; ks < 4; ++ks)
                 *reinterpret_cast<bf16x8 *>(&sm.Bb[row * kLdN + 32 * ks + 8 * lg]) = bfr[ks];
         }
-        // ---- transposed copies through the matrix core: T = frag x selection,
-        // exact for bf16 operands. Output lane holds rows 16w + 4lg..+3 of column lr.
+        // ---- B_bar^T scaled by cst through the matrix core; the scale belongs to
+        // the output rows 16w + 4lg + j
         {
-            // selection fragments: E_h[k][c] = 1 when k == 16h + c (k = 8lg + j)
-            bf16x8 e0, e1;
+            f32x4 cs4;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                e0[j] = (__bf16)((8 * lg + j == lr) ? 1.f : 0.f);
-                e1[j] = (__bf16)((8 * lg + j == 16 + lr) ? 1.f : 0.f);
-            }
+            for (int j = 0; j < 4; ++j) cs4[j] = __shfl(cst, (16 * w + 4 * lg + j) / R, 64);
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
-                const f32x4 t = mfma(bsc[nb >> 1], (nb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 t = mfma(bfr[nb >> 1], (nb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f}) * cs4;
                 const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
                 *reinterpret_cast<bf16x4 *>(&sm.Bt[(16 * nb + lr) * kLdR + 16 * w + 4 * lg]) = v;
-            }
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) {
-                const f32x4 t = mfma(xf[pb >> 1], (pb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f});
-                const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
-                *reinterpret_cast<bf16x4 *>(&sm.Xt[(16 * pb + lr) * kLdR + 16 * w + 4 * lg]) = v;
             }
         }
         __syncthreads();  // B2
@@ -458,9 +539,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     const int srow = 16 * sb + lr;
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
-                        const bf16x8 av_ = (sb == w) ? bfr[ks]
-                                                     : *reinterpret_cast<const bf16x8 *>(
-                                                           &sm.Bb[srow * kLdN + 32 * ks + 8 * lg]);
+                        const bf16x8 av_ = *reinterpret_cast<const bf16x8 *>(&sm.Bb[srow * kLdN + 32 * ks + 8 * lg]);
                         sT[sb] = mfma(av_, cfr[ks], sT[sb]);
                     }
                 }
@@ -498,8 +577,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 }
             // ---- Y^T = (St C_bar^T) diag(exp(cs)) + X^T P^T ; lane: column t = row, rows p
             const float eo = sm.eoff[row];
-            __bf16 *yp = static_cast<__bf16 *>(a.y);
-            const int64_t ybase = (((bi * L + c0 + t_row) * H + hi) * R + r_row) * kP;
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) {
                 const int p = 16 * pb + lr;
@@ -521,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 }
                 if (valid) {
                     const bf16x4 o = {(__bf16)yv[0], (__bf16)yv[1], (__bf16)yv[2], (__bf16)yv[3]};
-                    *reinterpret_cast<bf16x4 *>(yp + ybase + 16 * pb + 4 * lg) = o;
+                    *reinterpret_cast<bf16x4 *>(cb.y + ln.offX + 16 * pb + 4 * lg) = o;
                 }
             }
             __syncthreads();  // B3: St and Bb reads done
@@ -565,7 +642,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
     __syncthreads();
 
     // ------------------------------------------------------------- epilogue
-    const int l = tid & 63, lr = l & 15, lg = l >> 4;
     const bool last_seg = (MODE == kFull) || (pos.c_end * C >= L);
     float *dst = nullptr;
     if (MODE == kPass1)
