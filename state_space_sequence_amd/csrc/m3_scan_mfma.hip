@@ -189,10 +189,12 @@ __device__ __forceinline__ ChunkBase chunk_base(const ScanArgs &a, int64_t bi, i
     return cb;
 }
 
-// Global inputs of one chunk for one lane: its row of raw B and C (MFMA fragment
-// layout) and, in lanes 0..C-1, the token scalars.
+// Global inputs of one chunk for one lane: its row of raw B, C, theta and X (MFMA
+// fragment layout) and, in lanes 0..C-1, the token scalars. Loaded one chunk ahead
+// so the loads are in flight while the previous chunk is computed.
 struct ChunkRegs {
-    bf16x8 rb[4], rc[4];
+    bf16x8 rb[4], rc[4], xf[2];
+    f32x4 th[4];
     float d, av, lm;
 };
 
@@ -216,12 +218,23 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
             cr.rb[ks] = pb[4 * ks];
             if constexpr (MODE != kPass1) cr.rc[ks] = pc[4 * ks];
         }
+        const f32x4 *pt = reinterpret_cast<const f32x4 *>(cb.th + ln.offTh);
+        cr.th[0] = pt[2 * ln.lg];
+        cr.th[1] = pt[2 * ln.lg + 1];
+        cr.th[2] = pt[8 + 2 * ln.lg];
+        cr.th[3] = pt[8 + 2 * ln.lg + 1];
+        const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + ln.offX);
+        cr.xf[0] = px[ln.lg];
+        cr.xf[1] = px[4 + ln.lg];
     } else {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             cr.rb[ks] = bf16x8{};
             cr.rc[ks] = bf16x8{};
+            cr.th[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        cr.xf[0] = bf16x8{};
+        cr.xf[1] = bf16x8{};
     }
 }
 
@@ -234,7 +247,7 @@ __device__ __forceinline__ bf16x8 unit_fragment(int j) {
     return __builtin_bit_cast(bf16x8, u);
 }
 
-template <int MODE, int R>
+template <int MODE, int R, bool HAS_W>
 __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, SplitPlan sp) {
     constexpr int C = kRows / R;  // tokens per chunk
     __shared__ Smem sm;
@@ -245,7 +258,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
     const int64_t chain = pos.chain;
     const int64_t bi = chain / a.H, hi = chain % a.H, g = hi / (a.H / a.G);
     const int64_t L = a.L, H = a.H, G = a.G;
-    const bool has_w = a.B_normw != nullptr || a.C_normw != nullptr;
 
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
 
@@ -333,6 +345,13 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
     float logdecay_total = 0.f;
     float newcarry = 0.f;
 
+    ChunkRegs cr;
+    if (pos.c_begin < pos.c_end) {
+        const int64_t c0 = pos.c_begin * C;
+        const int nv = (int)((L - c0) < C ? (L - c0) : C);
+        load_chunk<MODE>(chunk_base<R>(a, bi, hi, g, c0), make_lane<R>(tid & 63, w, G, H), nv, H, cr);
+    }
+
     for (int64_t c = pos.c_begin; c < pos.c_end; ++c) {
         const int64_t c0 = c * C;
         const int nv = (int)((L - c0) < C ? (L - c0) : C);
@@ -340,11 +359,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         // lane-derived indices, recomputed per chunk (see opaque())
         const Lane ln = make_lane<R>(opaque(tid & 63), w, G, H);
         const int l = ln.l, lr = ln.lr, lg = ln.lg, row = ln.row, r_row = ln.r_row, t_row = ln.t_row;
-        ChunkRegs cr;
-        load_chunk<MODE>(cb, ln, nv, H, cr);
 
-        // ---- this chunk's inputs: raw B, C and the token scalars first, then
-        // theta and X, which are used last
+        // ---- this chunk's inputs, loaded during the previous chunk
         const bool valid = t_row < nv;
         const float d = cr.d, av = cr.av, lm = cr.lm;
         bf16x8 rb[4], rc[4], xf[2];
@@ -353,22 +369,10 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         for (int k = 0; k < 4; ++k) {
             rb[k] = cr.rb[k];
             rc[k] = cr.rc[k];
+            th[k] = cr.th[k];
         }
-        if (valid) {
-            const f32x4 *pt = reinterpret_cast<const f32x4 *>(cb.th + ln.offTh);
-            th[0] = pt[2 * lg];
-            th[1] = pt[2 * lg + 1];
-            th[2] = pt[8 + 2 * lg];
-            th[3] = pt[8 + 2 * lg + 1];
-            const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + ln.offX);
-            xf[0] = px[lg];
-            xf[1] = px[4 + lg];
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) th[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            xf[0] = bf16x8{};
-            xf[1] = bf16x8{};
-        }
+        xf[0] = cr.xf[0];
+        xf[1] = cr.xf[1];
         // ---- X^T through the matrix core: T = X-fragment x selection, exact for
         // bf16 operands; the output lane holds rows 16w + 4lg..+3 of column lr
 #pragma unroll
@@ -478,20 +482,21 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     clo = *reinterpret_cast<const f32x4 *>(&sm.bias[1][r_row][i0]);
                     chi = *reinterpret_cast<const f32x4 *>(&sm.bias[1][r_row][i0 + 64]);
                 }
-                f32x4 abl = {rsb, rsb, rsb, rsb}, abh = abl, acl = {rsc, rsc, rsc, rsc}, ach = acl;
-                if (has_w) {
-                    abl *= *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0]);
-                    abh *= *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0 + 64]);
-                    acl *= *reinterpret_cast<const f32x4 *>(&sm.normw[1][i0]);
-                    ach *= *reinterpret_cast<const f32x4 *>(&sm.normw[1][i0 + 64]);
+                // BCNorm scale per channel: 1/rms, times the gain when there is one
+                f32x4 abl, abh, acl, ach;
+                if constexpr (HAS_W) {
+                    abl = rsb * *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0]);
+                    abh = rsb * *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0 + 64]);
+                    acl = rsc * *reinterpret_cast<const f32x4 *>(&sm.normw[1][i0]);
+                    ach = rsc * *reinterpret_cast<const f32x4 *>(&sm.normw[1][i0 + 64]);
                 }
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int j = 4 * jh + jj;
                     float sn, cn;
                     sincos_rad(ph[8 * ks2 + j], sn, cn);
-                    const float bl = (float)rb[ks2][j] * abl[jj] + blo[jj];
-                    const float bh = (float)rb[ks2 + 2][j] * abh[jj] + bhi[jj];
+                    const float bl = (float)rb[ks2][j] * (HAS_W ? abl[jj] : rsb) + blo[jj];
+                    const float bh = (float)rb[ks2 + 2][j] * (HAS_W ? abh[jj] : rsb) + bhi[jj];
                     // rows past the end of the sequence need no zeroing: their
                     // weights w, gamma and cst are 0 and their outputs are not stored
                     const float bbl = cn * bl + sn * bh;
@@ -499,8 +504,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     bfr[ks2][j] = (__bf16)bbl;
                     bfr[ks2 + 2][j] = (__bf16)bbh;
                     if constexpr (MODE != kPass1) {
-                        const float cl = (float)rc[ks2][j] * acl[jj] + clo[jj];
-                        const float ch = (float)rc[ks2 + 2][j] * ach[jj] + chi[jj];
+                        const float cl = (float)rc[ks2][j] * (HAS_W ? acl[jj] : rsc) + clo[jj];
+                        const float ch = (float)rc[ks2 + 2][j] * (HAS_W ? ach[jj] : rsc) + chi[jj];
                         const float ccl = cn * cl + sn * ch;
                         const float cch = cn * ch - sn * cl;
                         cfr[ks2][j] = (__bf16)ccl;
@@ -528,6 +533,13 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             }
         }
         __syncthreads();  // B2
+
+        // ---- next chunk's inputs: in flight during this chunk's matrix work
+        if (c + 1 < pos.c_end) {
+            const int64_t c1 = c0 + C;
+            const int nv1 = (int)((L - c1) < C ? (L - c1) : C);
+            load_chunk<MODE>(chunk_base<R>(a, bi, hi, g, c1), ln, nv1, H, cr);
+        }
 
         if constexpr (MODE != kPass1) {
             // ---- S^T blocks (s-block sb <= w) for this wave's t-block
@@ -737,22 +749,28 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
     }
 }
 
-template <int R>
-hipError_t launch_r(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
+template <int R, bool HAS_W>
+hipError_t launch_rw(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
     const int64_t chains = a.b * a.H;
     if (sp.nseg <= 1) {
-        hipLaunchKernelGGL((scan_mfma_kernel<kFull, R>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp);
+        hipLaunchKernelGGL((scan_mfma_kernel<kFull, R, HAS_W>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp);
         return hipGetLastError();
     }
     const unsigned nblk = (unsigned)(chains * sp.nseg);
-    hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
+    hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R, HAS_W>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((combine_kernel<R>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
+    hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R, HAS_W>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
     return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_r(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
+    if (a.B_normw || a.C_normw) return launch_rw<R, true>(a, sp, s);
+    return launch_rw<R, false>(a, sp, s);
 }
 
 }  // namespace
