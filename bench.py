@@ -214,6 +214,23 @@ def main():
     torch.cuda.empty_cache()
 
     extra = {}
+    # achievable HBM bandwidth for a plain device copy (read + write), beside the spec peak
+    src = torch.empty(256 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    extra["hbm_copy_probe"] = {"GB_per_s": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+                               "bytes": "256 MiB read + 256 MiB written per copy"}
+    log("copy probe: %.0f GB/s" % copy_gbs)
+    del src, dst
     if not args.no_extra:
         # ---- MIMO rank-4 prefill, same shape
         for nm in ("mimo4_prefill_1p5b", "mimo4_prefill_long"):

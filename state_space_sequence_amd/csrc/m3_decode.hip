@@ -16,7 +16,9 @@
 // registers while the thread walks rows p. A wave covers contiguous half-rows,
 // so every state access is a coalesced V*4-byte vector access. The thread's
 // first batch of state rows is requested before the per-head set-up (BCNorm,
-// sincos), so that set-up overlaps the HBM latency. y for a row is reduced over
+// sincos), so that set-up overlaps the HBM latency. The per-column coefficients
+// are formed once per workgroup in LDS. State rows are streamed with
+// non-temporal accesses (read once, written once). y for a row is reduced over
 // the N/(2V) lanes that share the row.
 #include "m3_internal.h"
 
@@ -34,52 +36,59 @@ struct VecT<1> {
 };
 template <>
 struct VecT<2> {
-    typedef float2 type;
+    typedef float type __attribute__((ext_vector_type(2)));
 };
 template <>
 struct VecT<4> {
-    typedef float4 type;
+    typedef float type __attribute__((ext_vector_type(4)));
 };
 
 template <int V>
 __device__ __forceinline__ void unpack(const typename VecT<V>::type &v, float *o) {
     if constexpr (V == 1) {
         o[0] = v;
-    } else if constexpr (V == 2) {
-        o[0] = v.x; o[1] = v.y;
     } else {
-        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+#pragma unroll
+        for (int k = 0; k < V; ++k) o[k] = v[k];
     }
 }
 
 template <int V>
 __device__ __forceinline__ typename VecT<V>::type pack(const float *o) {
-    if constexpr (V == 1)
+    if constexpr (V == 1) {
         return o[0];
-    else if constexpr (V == 2)
-        return make_float2(o[0], o[1]);
-    else
-        return make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+        typename VecT<V>::type v;
+#pragma unroll
+        for (int k = 0; k < V; ++k) v[k] = o[k];
+        return v;
+    }
 }
 
-template <bool BF16, int N, int R, int V>
+template <bool BF16, int N, int R, int V, int KBATCH>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     constexpr int HALF = N / 2;
     constexpr int NQ = HALF / V;            // lanes that share one row p
     constexpr int ROWS = kThreads / NQ;     // rows covered per pass of the workgroup
-    constexpr int KB = (V == 4) ? 4 : 8;    // passes whose state is held in registers at once
+    constexpr int KB = KBATCH;              // passes whose state is held in registers at once
     static_assert(NQ >= 2 && NQ <= 64 && (64 % NQ) == 0, "unsupported N/V");
     typedef typename VecT<V>::type vec;
 
     extern __shared__ float sm[];
-    float *sB = sm;              // [R][N]   raw, then normalised B_t
-    float *sC = sB + R * N;      // [R][N]   C_t
-    float *sBp = sC + R * N;     // [R][N]   B_{t-1}
-    float *sx = sBp + R * N;     // [R][P]
-    float *sxp = sx + R * a.P;   // [R][P]
-    float *scs = sxp + R * a.P;  // [HALF] cos
-    float *ssn = scs + HALF;     // [HALF] sin
-    float *srs = ssn + HALF;     // [3R]  1/rms per row
+    // every array below starts on a 16-byte boundary (sizes are multiples of 4
+    // floats) except the last two, which are only read as scalars
+    float *sB = sm;              // [R][N]   raw, then gamma * normalised B_t
+    float *sC = sB + R * N;      // [R][N]   raw, then normalised C_t
+    float *sBp = sC + R * N;     // [R][N]   raw, then beta * normalised B_{t-1}
+    float *sbb = sBp + R * N;    // [R][N]   B bias of this head
+    float *scb = sbb + R * N;    // [R][N]   C bias
+    float *swb = scb + R * N;    // [N]      B gain (ones when absent)
+    float *swc = swb + N;        // [N]      C gain
+    float *scs = swc + N;        // [HALF]   cos
+    float *ssn = scs + HALF;     // [HALF]   sin
+    float *srs = ssn + HALF;     // [4R]     1/rms per row
+    float *sx = srs + 4 * R;     // [P][R]
+    float *sxp = sx + R * a.P;   // [P][R]
 
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x;
@@ -98,8 +107,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int k = 0; k < KB; ++k) {
         const int p = prow + k * ROWS;
         if (k < passes && p < P) {
-            lo[k] = *reinterpret_cast<const vec *>(hbase + (int64_t)p * N + n0);
-            hiv[k] = *reinterpret_cast<const vec *>(hbase + (int64_t)p * N + HALF + n0);
+            lo[k] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(hbase + (int64_t)p * N + n0));
+            hiv[k] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(hbase + (int64_t)p * N + HALF + n0));
         }
     }
 
@@ -112,8 +121,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
     const int64_t rowX = (bi * a.H + hi) * R * P;
     for (int e = tid; e < R * P; e += kThreads) {
-        sx[e] = ld_io<BF16>(a.x, rowX + e);
-        sxp[e] = a.has_prev ? ld_io<BF16>(a.x_prev, rowX + e) : 0.f;
+        // stored rank-minor, [p][r], so one row's ranks are adjacent
+        const int r = e / P, p = e % P;
+        sx[p * R + r] = ld_io<BF16>(a.x, rowX + e);
+        sxp[p * R + r] = a.has_prev ? ld_io<BF16>(a.x_prev, rowX + e) : 0.f;
+    }
+    for (int e = tid; e < R * N; e += kThreads) {
+        sbb[e] = a.B_bias[hi * R * N + e];
+        scb[e] = a.C_bias[hi * R * N + e];
+    }
+    for (int e = tid; e < N; e += kThreads) {
+        swb[e] = a.B_normw ? a.B_normw[e] : 1.f;
+        swc[e] = a.C_normw ? a.C_normw[e] : 1.f;
     }
     const float d = a.dt[bh], Av = a.A[bh], lm = a.lam[bh];
     for (int i = tid; i < HALF; i += kThreads) {
@@ -139,30 +158,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const float beta = a.has_prev ? (1.0f - lm) * d * alpha : 0.f;
     const float gamma = lm * d;
 
+    // ---- per-column coefficients, once per workgroup, in place in LDS:
+    // sB <- gamma * B_t, sBp <- beta * B_{t-1}, sC <- C_t (all normalised + bias)
+    for (int e = tid; e < R * N; e += kThreads) {
+        const int r = e / N, n = e % N;
+        sB[e] = gamma * (sB[e] * srs[r] * swb[n] + sbb[e]);
+        sC[e] = sC[e] * srs[R + r] * swc[n] + scb[e];
+        sBp[e] = beta * (sBp[e] * srs[2 * R + r] * swb[n] + sbb[e]);
+    }
+    __syncthreads();
+
     // ---- this thread's columns: coefficients in registers
     float bl[R][V], bhc[R][V], cl[R][V], ch[R][V], pl[R][V], ph[R][V];
     float cs[V], sn[V];
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-        cs[k] = scs[n0 + k];
-        sn[k] = ssn[n0 + k];
-    }
+    unpack<V>(*reinterpret_cast<const vec *>(scs + n0), cs);
+    unpack<V>(*reinterpret_cast<const vec *>(ssn + n0), sn);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const float *bb = a.B_bias + (hi * R + r) * N;
-        const float *cb = a.C_bias + (hi * R + r) * N;
-#pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const int nl = n0 + k, nh = HALF + n0 + k;
-            const float wbl = a.B_normw ? a.B_normw[nl] : 1.f, wbh = a.B_normw ? a.B_normw[nh] : 1.f;
-            const float wcl = a.C_normw ? a.C_normw[nl] : 1.f, wch = a.C_normw ? a.C_normw[nh] : 1.f;
-            bl[r][k] = gamma * (sB[r * N + nl] * srs[r] * wbl + bb[nl]);
-            bhc[r][k] = gamma * (sB[r * N + nh] * srs[r] * wbh + bb[nh]);
-            cl[r][k] = sC[r * N + nl] * srs[R + r] * wcl + cb[nl];
-            ch[r][k] = sC[r * N + nh] * srs[R + r] * wch + cb[nh];
-            pl[r][k] = beta * (sBp[r * N + nl] * srs[2 * R + r] * wbl + bb[nl]);
-            ph[r][k] = beta * (sBp[r * N + nh] * srs[2 * R + r] * wbh + bb[nh]);
-        }
+        unpack<V>(*reinterpret_cast<const vec *>(sB + r * N + n0), bl[r]);
+        unpack<V>(*reinterpret_cast<const vec *>(sB + r * N + HALF + n0), bhc[r]);
+        unpack<V>(*reinterpret_cast<const vec *>(sC + r * N + n0), cl[r]);
+        unpack<V>(*reinterpret_cast<const vec *>(sC + r * N + HALF + n0), ch[r]);
+        unpack<V>(*reinterpret_cast<const vec *>(sBp + r * N + n0), pl[r]);
+        unpack<V>(*reinterpret_cast<const vec *>(sBp + r * N + HALF + n0), ph[r]);
     }
 
     // ---- stream the state rows
@@ -173,8 +191,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             for (int k = 0; k < KB; ++k) {
                 const int p = prow + (kb + k) * ROWS;
                 if (kb + k < passes && p < P) {
-                    lo[k] = *reinterpret_cast<const vec *>(hbase + (int64_t)p * N + n0);
-                    hiv[k] = *reinterpret_cast<const vec *>(hbase + (int64_t)p * N + HALF + n0);
+                    lo[k] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(hbase + (int64_t)p * N + n0));
+                    hiv[k] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(hbase + (int64_t)p * N + HALF + n0));
                 }
             }
         }
@@ -187,8 +205,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             float xv[R], xpv[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                xv[r] = sx[r * P + p];
-                xpv[r] = sxp[r * P + p];
+                xv[r] = sx[p * R + r];
+                xpv[r] = sxp[p * R + r];
             }
             float l[V], h[V];
             unpack<V>(lo[k], l);
@@ -214,18 +232,48 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) yacc[r] += cl[r][c] * nu + ch[r][c] * nv;
             }
-            *reinterpret_cast<vec *>(hbase + (int64_t)p * N + n0) = pack<V>(l);
-            *reinterpret_cast<vec *>(hbase + (int64_t)p * N + HALF + n0) = pack<V>(h);
+            __builtin_nontemporal_store(pack<V>(l), reinterpret_cast<vec *>(hbase + (int64_t)p * N + n0));
+            __builtin_nontemporal_store(pack<V>(h), reinterpret_cast<vec *>(hbase + (int64_t)p * N + HALF + n0));
+            if constexpr (R == 2 || R == 4) {
+                // reduce-scatter over the NQ lanes of the row: at each of the first
+                // log2(R) steps a lane keeps half of its partial sums and adds the
+                // partner's matching half, so R sums cost log2(NQ) + R - 1 shuffles
+                constexpr int LR = (R == 2) ? 1 : 2;
+                float vals[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                float v = yacc[r];
+                for (int r = 0; r < R; ++r) vals[r] = yacc[r];
+                int cnt = R;
 #pragma unroll
-                for (int o = NQ / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-                yacc[r] = v;
-            }
-            if (q == 0) {
+                for (int st = 0; st < LR; ++st) {
+                    const int o = NQ >> (st + 1);
+                    const bool up = (q & o) != 0;
+                    const int half = cnt / 2;
 #pragma unroll
-                for (int r = 0; r < R; ++r) st_io<BF16>(a.y, ybase + r * P + p, yacc[r]);
+                    for (int i = 0; i < R / 2; ++i) {
+                        if (i < half) {
+                            const float send = up ? vals[i] : vals[i + half];
+                            const float keep = up ? vals[i + half] : vals[i];
+                            vals[i] = keep + __shfl_xor(send, o, 64);
+                        }
+                    }
+                    cnt = half;
+                }
+                float v = vals[0];
+#pragma unroll
+                for (int o = NQ / (2 * R); o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+                if (q % (NQ / R) == 0) st_io<BF16>(a.y, ybase + (q / (NQ / R)) * P + p, v);
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float v = yacc[r];
+#pragma unroll
+                    for (int o = NQ / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+                    yacc[r] = v;
+                }
+                if (q == 0) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r) st_io<BF16>(a.y, ybase + r * P + p, yacc[r]);
+                }
             }
         }
     }
@@ -233,13 +281,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
 template <bool BF16, int N>
 hipError_t launch_n(const DecodeArgs &a, hipStream_t s) {
-    const size_t smem = sizeof(float) * (3 * a.R * N + 2 * a.R * a.P + N + 3 * a.R);
+    const size_t smem = sizeof(float) * (5 * a.R * N + 3 * N + 4 * a.R + 2 * a.R * a.P);
     dim3 grid((unsigned)(a.b * a.H)), block(kThreads);
     switch (a.R) {
-        case 1: hipLaunchKernelGGL((decode_kernel<BF16, N, 1, 4>), grid, block, smem, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<BF16, N, 2, 2>), grid, block, smem, s, a); break;
-        case 3: hipLaunchKernelGGL((decode_kernel<BF16, N, 3, 2>), grid, block, smem, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<BF16, N, 4, 2>), grid, block, smem, s, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<BF16, N, 1, 4, 2>), grid, block, smem, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<BF16, N, 2, 2, 4>), grid, block, smem, s, a); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<BF16, N, 3, 2, 4>), grid, block, smem, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<BF16, N, 4, 2, 4>), grid, block, smem, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
