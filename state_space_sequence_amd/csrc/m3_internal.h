@@ -42,7 +42,7 @@ struct SplitPlan {
     int64_t seg_chunks;  // chunks per segment (last one may be shorter)
     float *seg_state;  // [b,H,nseg,P,N]: pass-1 end states, then incoming states
     float *seg_decay;  // [b,H,nseg]     total log-decay of each segment
-    float *seg_angle;  // [b,H,nseg,N/2] total rotation angle of each segment
+    float *seg_angle;  // [b,H,nseg,N/2] total rotation angle of each segment, in revolutions mod 1
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);

@@ -82,11 +82,26 @@ __device__ __forceinline__ float dpp_row_shr(float v, int k) {
     return __int_as_float(r);
 }
 
-__device__ __forceinline__ void sincos_rad(float x, float &s, float &c) {
-    // hardware sine/cosine take revolutions
-    const float rev = __builtin_amdgcn_fractf(x * kInv2Pi);
+// Angles are kept in revolutions (turns): the hardware sine/cosine take them
+// directly, and the running total can be reduced mod 1 without changing any
+// rotation, which keeps its fp32 resolution over long sequences.
+__device__ __forceinline__ void sincos_rev(float x, float &s, float &c) {
+    const float rev = __builtin_amdgcn_fractf(x);
     s = __builtin_amdgcn_sinf(rev);
     c = __builtin_amdgcn_cosf(rev);
+}
+
+// x summed over lanes l, l^16, l^32, l^48 (the four 16-lane rows of the wave),
+// through the gfx950 row swaps instead of an LDS round trip
+__device__ __forceinline__ float sum_over_rows(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
 struct alignas(16) Smem {
@@ -98,8 +113,11 @@ struct alignas(16) Smem {
     alignas(16) float wgt[kRows];         // per row: folded weight w of the row's token
     alignas(16) float gam[kRows];         // per row: gamma
     alignas(16) float eoff[kRows];        // per row: exp(cs) (carried-state output scale)
-    alignas(16) float angtot[4][kHalf];   // per wave: angle total of its rows
-    alignas(16) float carry[kHalf];       // cumulative angle before the current chunk
+    alignas(16) float cstt[kRows];        // per row: exp(cs_end - cs) w (state-input weight)
+    alignas(16) float ftab[kRows];        // per row t >= 16: exp(cs_t - cs_ref), ref = last row of the block before t's
+    alignas(16) float tw[3][kRows];       // [w-1][s]: exp(cs_ref(w) - cs_s) w_s for s < 16w, else 0
+    alignas(16) float angtot[4][kHalf];   // per wave: angle total of its rows (revolutions)
+    alignas(16) float carry[kHalf];       // cumulative angle before the current chunk, mod 1 revolution
     alignas(16) float bias[2][4][kN];     // B / C bias of this head, per rank
     alignas(16) float normw[2][kN];       // BCNorm gains (ones when absent)
 };
@@ -146,13 +164,11 @@ __device__ __forceinline__ float wave_incl_scan(float v) {
 // Per-lane constants of the chunk loop (fixed for the workgroup's lifetime).
 struct Lane {
     int l, lr, lg, row, r_row, t_row;
-    int offBC;  // element offset of this lane's slice of a chunk's raw B/C block
-    int offTh;  // element offset of this lane's theta row in a chunk's theta block
-    int offX;   // element offset of this lane's row in a chunk's x (and y) block
+    int offX;  // element offset of this lane's row in a chunk's x (and y) block
 };
 
 template <int R>
-__device__ __forceinline__ Lane make_lane(int l, int w, int64_t G, int64_t H) {
+__device__ __forceinline__ Lane make_lane(int l, int w, int64_t H) {
     Lane ln;
     ln.l = l;
     ln.lr = l & 15;
@@ -160,8 +176,6 @@ __device__ __forceinline__ Lane make_lane(int l, int w, int64_t G, int64_t H) {
     ln.row = 16 * w + ln.lr;
     ln.r_row = ln.row % R;
     ln.t_row = ln.row / R;
-    ln.offBC = (ln.t_row * (int)G * R + ln.r_row) * kN + 8 * ln.lg;
-    ln.offTh = ln.t_row * (int)G * kHalf;
     ln.offX = (ln.t_row * (int)H * R + ln.r_row) * kP;
     return ln;
 }
@@ -195,47 +209,56 @@ __device__ __forceinline__ ChunkBase chunk_base(const ScanArgs &a, int64_t bi, i
 struct ChunkRegs {
     bf16x8 rb[4], rc[4], xf[2];
     f32x4 th[4];
-    float d, av, lm;
+    float d, av, lm;  // dt, A, lambda of the token of row l (lane l holds row l)
+    float dn, lmn;    // dt and lambda of the token after it (0 past the end)
+    float drow;       // dt of the token of this lane's fragment row (0 past the end)
 };
 
-template <int MODE>
-__device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, int nv, int64_t H,
-                                           ChunkRegs &cr) {
+// nv: tokens of the chunk; avail: tokens from the chunk's first one to the end
+// of the sequence (capped at C + 1).
+template <int MODE, int R>
+__device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, int nv, int avail, int64_t G,
+                                           int64_t H, ChunkRegs &cr) {
+    // token scalars in row layout: lane l holds row l, i.e. token l / R
+    const int ts = ln.l / R;
     cr.d = 0.f;
     cr.av = 0.f;
     cr.lm = 0.f;
-    if (ln.l < nv) {
-        const int o = ln.l * (int)H;
+    cr.dn = 0.f;
+    cr.lmn = 0.f;
+    if (ts < nv) {
+        const int o = ts * (int)H;
         cr.d = cb.dt[o];
         cr.av = cb.A[o];
         cr.lm = cb.lam[o];
-    }
-    if (ln.t_row < nv) {
-        const bf16x8 *pb = reinterpret_cast<const bf16x8 *>(cb.B + ln.offBC);
-        const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + ln.offBC);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            cr.rb[ks] = pb[4 * ks];
-            if constexpr (MODE != kPass1) cr.rc[ks] = pc[4 * ks];
+        if (ts + 1 < avail) {
+            cr.dn = cb.dt[o + (int)H];
+            cr.lmn = cb.lam[o + (int)H];
         }
-        const f32x4 *pt = reinterpret_cast<const f32x4 *>(cb.th + ln.offTh);
-        cr.th[0] = pt[2 * ln.lg];
-        cr.th[1] = pt[2 * ln.lg + 1];
-        cr.th[2] = pt[8 + 2 * ln.lg];
-        cr.th[3] = pt[8 + 2 * ln.lg + 1];
-        const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + ln.offX);
-        cr.xf[0] = px[ln.lg];
-        cr.xf[1] = px[4 + ln.lg];
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            cr.rb[ks] = bf16x8{};
-            cr.rc[ks] = bf16x8{};
-            cr.th[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        cr.xf[0] = bf16x8{};
-        cr.xf[1] = bf16x8{};
     }
+    // fragment rows past the end read the last token's data instead of zeros:
+    // finite values whose weights, gamma, state weight and angle increment are
+    // all zero, and whose outputs are not stored
+    const bool valid = ln.t_row < nv;
+    const int tr = valid ? ln.t_row : nv - 1;
+    const float dr = cb.dt[tr * (int)H];
+    cr.drow = valid ? dr : 0.f;
+    const int offBC = (tr * (int)G * R + ln.r_row) * kN + 8 * ln.lg;
+    const bf16x8 *pb = reinterpret_cast<const bf16x8 *>(cb.B + offBC);
+    const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + offBC);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        cr.rb[ks] = pb[4 * ks];
+        if constexpr (MODE != kPass1) cr.rc[ks] = pc[4 * ks];
+    }
+    const f32x4 *pt = reinterpret_cast<const f32x4 *>(cb.th + tr * (int)G * kHalf);
+    cr.th[0] = pt[2 * ln.lg];
+    cr.th[1] = pt[2 * ln.lg + 1];
+    cr.th[2] = pt[8 + 2 * ln.lg];
+    cr.th[3] = pt[8 + 2 * ln.lg + 1];
+    const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + (tr * (int)H * R + ln.r_row) * kP);
+    cr.xf[0] = px[ln.lg];
+    cr.xf[1] = px[4 + ln.lg];
 }
 
 // bf16x8 fragment with a single 1.0 at slot j (none when j is outside 0..7)
@@ -349,7 +372,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
     if (pos.c_begin < pos.c_end) {
         const int64_t c0 = pos.c_begin * C;
         const int nv = (int)((L - c0) < C ? (L - c0) : C);
-        load_chunk<MODE>(chunk_base<R>(a, bi, hi, g, c0), make_lane<R>(tid & 63, w, G, H), nv, H, cr);
+        const int avail = (int)((L - c0) < C + 1 ? (L - c0) : C + 1);
+        load_chunk<MODE, R>(chunk_base<R>(a, bi, hi, g, c0), make_lane<R>(tid & 63, w, H), nv, avail, G, H, cr);
     }
 
     for (int64_t c = pos.c_begin; c < pos.c_end; ++c) {
@@ -357,12 +381,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         const int nv = (int)((L - c0) < C ? (L - c0) : C);
         const ChunkBase cb = chunk_base<R>(a, bi, hi, g, c0);
         // lane-derived indices, recomputed per chunk (see opaque())
-        const Lane ln = make_lane<R>(opaque(tid & 63), w, G, H);
+        const Lane ln = make_lane<R>(opaque(tid & 63), w, H);
         const int l = ln.l, lr = ln.lr, lg = ln.lg, row = ln.row, r_row = ln.r_row, t_row = ln.t_row;
 
         // ---- this chunk's inputs, loaded during the previous chunk
         const bool valid = t_row < nv;
-        const float d = cr.d, av = cr.av, lm = cr.lm;
+        const float d = cr.d, av = cr.av, lm = cr.lm, dn = cr.dn, lmn = cr.lmn, drow = cr.drow;
         bf16x8 rb[4], rc[4], xf[2];
         f32x4 th[4];
 #pragma unroll
@@ -382,21 +406,37 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             *reinterpret_cast<bf16x4 *>(&sm.Xt[(16 * pb + lr) * kLdR + 16 * w + 4 * lg]) = v;
         }
 
-        // ---- token scalars (lane = token): decay prefix, folded weights
-        const float cs = wave_incl_scan(d * av);
-        const float dn = __shfl_down(d, 1, 64), lnx = __shfl_down(lm, 1, 64);
-        float look = 0.f;
-        if (l + 1 < nv) {
-            look = (1.f - lnx) * dn;
-        } else if (l + 1 == nv && c0 + nv < L) {
-            const int o1 = nv * (int)H;
-            look = (1.f - cb.lam[o1]) * cb.dt[o1];
-        }
+        // ---- token scalars in row layout (lane l = row l, token l / R): decay
+        // prefix over the tokens (one term per token), folded weights
+        const float cs = wave_incl_scan((l % R == 0) ? d * av : 0.f);
         const float gm = lm * d;
-        const float wt = gm + look;
-        const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
-        const float cst = __expf(cs_end - cs) * wt;
-        const float d_row = __shfl(d, t_row, 64);
+        const float wt = gm + (1.f - lmn) * dn;
+        const float cs_end = lane_value(cs, 63);
+        // per-row tables; the previous chunk's reads of them ended before its last barrier
+        {
+            const float l2c = cs * kLog2e;
+            if (w == 0) {
+                sm.l2cs[l] = l2c;
+                sm.wgt[l] = wt;
+                sm.gam[l] = gm;
+                sm.eoff[l] = __expf(cs);
+            } else if (w == 1) {
+                sm.cstt[l] = __expf(cs_end - cs) * wt;
+                // factor of row t against the last row of the block before its own
+                const float ref = (l < 32) ? lane_value(l2c, 15) : ((l < 48) ? lane_value(l2c, 31) : lane_value(l2c, 47));
+                sm.ftab[l] = __builtin_amdgcn_exp2f(fminf(l2c - ref, 0.f));
+            } else {
+                // decay from row s to the last row of block wb-1, times w_s (rows s < 16wb)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int wb = (w == 2) ? 1 + k : 3;
+                    if (w == 2 || k == 0) {
+                        const float ref = lane_value(l2c, 16 * wb - 1);
+                        sm.tw[wb - 1][l] = (l < 16 * wb) ? __builtin_amdgcn_exp2f(fminf(ref - l2c, 0.f)) * wt : 0.f;
+                    }
+                }
+            }
+        }
 
         // ---- BCNorm factors of this row (sum over the 4 lanes that hold it)
         float ssb = 0.f, ssc = 0.f;
@@ -411,25 +451,21 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     ssc = __builtin_amdgcn_fdot2_f32_bf16(vc, vc, ssc, false);
                 }
             }
-        ssb += __shfl_xor(ssb, 16, 64);
-        ssb += __shfl_xor(ssb, 32, 64);
-        const float rsb = __builtin_amdgcn_rsqf(ssb * (1.f / kN) + a.eps);
+        const float rsb = __builtin_amdgcn_rsqf(sum_over_rows(ssb) * (1.f / kN) + a.eps);
         float rsc = 0.f;
-        if constexpr (MODE != kPass1) {
-            ssc += __shfl_xor(ssc, 16, 64);
-            ssc += __shfl_xor(ssc, 32, 64);
-            rsc = __builtin_amdgcn_rsqf(ssc * (1.f / kN) + a.eps);
-        }
+        if constexpr (MODE != kPass1) rsc = __builtin_amdgcn_rsqf(sum_over_rows(ssc) * (1.f / kN) + a.eps);
 
         // ---- angles: prefix over the tokens of this wave's rows (16-lane DPP rows)
         // slot k (0..15) is channel i = 8lg + k (k < 8) or 32 + 8lg + (k - 8)
+        // (in revolutions: dt theta / 2 pi)
+        const float drev = drow * kInv2Pi;
         float ph[16];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            ph[4 * k + 0] = d_row * th[k][0];
-            ph[4 * k + 1] = d_row * th[k][1];
-            ph[4 * k + 2] = d_row * th[k][2];
-            ph[4 * k + 3] = d_row * th[k][3];
+            ph[4 * k + 0] = drev * th[k][0];
+            ph[4 * k + 1] = drev * th[k][1];
+            ph[4 * k + 2] = drev * th[k][2];
+            ph[4 * k + 3] = drev * th[k][3];
         }
 #pragma unroll
         for (int sh = R; sh < 16; sh <<= 1)
@@ -459,16 +495,9 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 #pragma unroll
                 for (int k = 0; k < 4; ++k) ph[8 * h2 + 4 * q4 + k] += off[k];
             }
-        if (w == 0) {
-            // per-row scalar tables for the mask and the carried-state output
-            const int tl = l / R;
-            const float cs_l = __shfl(cs, tl, 64);
-            sm.l2cs[l] = cs_l * kLog2e;
-            sm.wgt[l] = __shfl(wt, tl, 64);
-            sm.gam[l] = __shfl(gm, tl, 64);
-            sm.eoff[l] = __expf(cs_l);
-            newcarry = sm.carry[l] + sm.angtot[0][l] + sm.angtot[1][l] + sm.angtot[2][l] + sm.angtot[3][l];
-        }
+        if (w == 0)
+            newcarry = __builtin_amdgcn_fractf(sm.carry[l] + sm.angtot[0][l] + sm.angtot[1][l] + sm.angtot[2][l] +
+                                               sm.angtot[3][l]);
         bf16x8 bfr[4], cfr[4];
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2) {
@@ -494,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 for (int jj = 0; jj < 4; ++jj) {
                     const int j = 4 * jh + jj;
                     float sn, cn;
-                    sincos_rad(ph[8 * ks2 + j], sn, cn);
+                    sincos_rev(ph[8 * ks2 + j], sn, cn);
                     const float bl = (float)rb[ks2][j] * (HAS_W ? abl[jj] : rsb) + blo[jj];
                     const float bh = (float)rb[ks2 + 2][j] * (HAS_W ? abh[jj] : rsb) + bhi[jj];
                     // rows past the end of the sequence need no zeroing: their
@@ -522,9 +551,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         // ---- B_bar^T scaled by cst through the matrix core; the scale belongs to
         // the output rows 16w + 4lg + j
         {
-            f32x4 cs4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) cs4[j] = __shfl(cst, (16 * w + 4 * lg + j) / R, 64);
+            const f32x4 cs4 = *reinterpret_cast<const f32x4 *>(&sm.cstt[16 * w + 4 * lg]);
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
                 const f32x4 t = mfma(bfr[nb >> 1], (nb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f}) * cs4;
@@ -538,7 +565,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         if (c + 1 < pos.c_end) {
             const int64_t c1 = c0 + C;
             const int nv1 = (int)((L - c1) < C ? (L - c1) : C);
-            load_chunk<MODE>(chunk_base<R>(a, bi, hi, g, c1), ln, nv1, H, cr);
+            const int avail1 = (int)((L - c1) < C + 1 ? (L - c1) : C + 1);
+            load_chunk<MODE, R>(chunk_base<R>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
         }
 
         if constexpr (MODE != kPass1) {
@@ -558,15 +586,16 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             }
             // ---- mask: lane holds S^T[s = 16sb + 4lg + j][t = 16w + lr]
             const int ttok = row / R;
-            const float l2t = sm.l2cs[row], gmt = sm.gam[row];
+            const float l2t = sm.l2cs[row], gmt = sm.gam[row], ft = sm.ftab[row];
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
                 if (sb < w) {
-                    // every s token precedes every t token
-                    const f32x4 l2s = *reinterpret_cast<const f32x4 *>(&sm.l2cs[16 * sb + 4 * lg]);
-                    const f32x4 ws = *reinterpret_cast<const f32x4 *>(&sm.wgt[16 * sb + 4 * lg]);
+                    // every s token precedes every t token: the decay splits at the
+                    // last row of block w-1, exp(cs_t - cs_ref) exp(cs_ref - cs_s),
+                    // both factors at most 1
+                    const f32x4 tws = *reinterpret_cast<const f32x4 *>(&sm.tw[w - 1][16 * sb + 4 * lg]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sT[sb][j] *= __builtin_amdgcn_exp2f(l2t - l2s[j]) * ws[j];
+                    for (int j = 0; j < 4; ++j) sT[sb][j] *= tws[j] * ft;
                 } else if (sb == w) {
                     const f32x4 l2s = *reinterpret_cast<const f32x4 *>(&sm.l2cs[16 * sb + 4 * lg]);
                     const f32x4 ws = *reinterpret_cast<const f32x4 *>(&sm.wgt[16 * sb + 4 * lg]);
@@ -666,7 +695,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         for (int j = 0; j < 4; ++j) {
             const int i = 16 * w + 4 * lg + j;
             float sn, cn;
-            sincosf(sm.carry[i], &sn, &cn);
+            sincos_rev(sm.carry[i], sn, cn);
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) {
                 const float u = acc[0][pb][j], v = acc[1][pb][j];
@@ -735,7 +764,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
         float *E = sp.seg_state + (chain * sp.nseg + s) * (kP * kN);
         const float dec = __expf(sp.seg_decay[chain * sp.nseg + s]);
         float sn, cn;
-        sincosf(sp.seg_angle[(chain * sp.nseg + s) * kHalf + i], &sn, &cn);
+        sincos_rev(sp.seg_angle[(chain * sp.nseg + s) * kHalf + i], sn, cn);
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int p = (tid + kThreads * k) / kHalf;
