@@ -482,19 +482,30 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         }
         __syncthreads();  // B1
 
-        // ---- rotate into the frame of the workgroup's first token
+        // ---- rotate into the frame of the workgroup's first token: add the carry
+        // and the totals of the earlier waves' rows. Branch-free (uniform 0/1
+        // weights), so that all the LDS reads are issued before the first wait.
+        {
+            const float f0 = (w > 0) ? 1.f : 0.f, f1 = (w > 1) ? 1.f : 0.f, f2 = (w > 2) ? 1.f : 0.f;
+            f32x4 cy[4], a0[4], a1[4], a2[4];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int q4 = 0; q4 < 2; ++q4) {
-                const int i0 = 32 * h2 + 8 * lg + 4 * q4;
-                f32x4 off = *reinterpret_cast<const f32x4 *>(&sm.carry[i0]);
-                if (w > 0) off += *reinterpret_cast<const f32x4 *>(&sm.angtot[0][i0]);
-                if (w > 1) off += *reinterpret_cast<const f32x4 *>(&sm.angtot[1][i0]);
-                if (w > 2) off += *reinterpret_cast<const f32x4 *>(&sm.angtot[2][i0]);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) ph[8 * h2 + 4 * q4 + k] += off[k];
+            for (int q = 0; q < 4; ++q) {
+                const int i0 = 32 * (q >> 1) + 8 * lg + 4 * (q & 1);
+                cy[q] = *reinterpret_cast<const f32x4 *>(&sm.carry[i0]);
+                a0[q] = *reinterpret_cast<const f32x4 *>(&sm.angtot[0][i0]);
+                a1[q] = *reinterpret_cast<const f32x4 *>(&sm.angtot[1][i0]);
+                a2[q] = *reinterpret_cast<const f32x4 *>(&sm.angtot[2][i0]);
             }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    float v = ph[4 * q + k] + cy[q][k];
+                    v = __builtin_fmaf(f0, a0[q][k], v);
+                    v = __builtin_fmaf(f1, a1[q][k], v);
+                    ph[4 * q + k] = __builtin_fmaf(f2, a2[q][k], v);
+                }
+        }
         if (w == 0)
             newcarry = __builtin_amdgcn_fractf(sm.carry[l] + sm.angtot[0][l] + sm.angtot[1][l] + sm.angtot[2][l] +
                                                sm.angtot[3][l]);
@@ -585,27 +596,34 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 }
             }
             // ---- mask: lane holds S^T[s = 16sb + 4lg + j][t = 16w + lr]
+            // (all table reads first, no LDS wait inside the uniform branches below)
             const int ttok = row / R;
             const float l2t = sm.l2cs[row], gmt = sm.gam[row], ft = sm.ftab[row];
+            const f32x4 l2s = *reinterpret_cast<const f32x4 *>(&sm.l2cs[16 * w + 4 * lg]);
+            const f32x4 ws = *reinterpret_cast<const f32x4 *>(&sm.wgt[16 * w + 4 * lg]);
+            f32x4 tws[3];
+#pragma unroll
+            for (int sb = 0; sb < 3; ++sb)
+                tws[sb] = *reinterpret_cast<const f32x4 *>(&sm.tw[w > 0 ? w - 1 : 0][16 * sb + 4 * lg]);
+            // diagonal block w: exp(cs_t - cs_s) w_s below the diagonal, gamma on it
+            f32x4 mdiag;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int stok = (16 * w + 4 * lg + j) / R;
+                const float e = __builtin_amdgcn_exp2f(fminf(l2t - l2s[j], 0.f)) * ws[j];
+                const float before = (stok < ttok) ? 1.f : 0.f, same = (stok == ttok) ? 1.f : 0.f;
+                mdiag[j] = before * e + same * gmt;
+            }
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
                 if (sb < w) {
                     // every s token precedes every t token: the decay splits at the
                     // last row of block w-1, exp(cs_t - cs_ref) exp(cs_ref - cs_s),
                     // both factors at most 1
-                    const f32x4 tws = *reinterpret_cast<const f32x4 *>(&sm.tw[w - 1][16 * sb + 4 * lg]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sT[sb][j] *= tws[j] * ft;
+                    for (int j = 0; j < 4; ++j) sT[sb][j] *= tws[sb < 3 ? sb : 2][j] * ft;
                 } else if (sb == w) {
-                    const f32x4 l2s = *reinterpret_cast<const f32x4 *>(&sm.l2cs[16 * sb + 4 * lg]);
-                    const f32x4 ws = *reinterpret_cast<const f32x4 *>(&sm.wgt[16 * sb + 4 * lg]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int stok = (16 * sb + 4 * lg + j) / R;
-                        const float e = __builtin_amdgcn_exp2f(fminf(l2t - l2s[j], 0.f)) * ws[j];
-                        const float m = (stok < ttok) ? e : ((stok == ttok) ? gmt : 0.f);
-                        sT[sb][j] *= m;
-                    }
+                    sT[sb] *= mdiag;
                 }
             }
             bf16x8 pfr[2];
