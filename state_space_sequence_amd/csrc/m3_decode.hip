@@ -65,8 +65,44 @@ __device__ __forceinline__ typename VecT<V>::type pack(const float *o) {
     }
 }
 
+// One reduce-scatter step at lane bit B over the first 2*HALF of vals: the lower
+// lane of each pair keeps vals[0..HALF) plus the partner's, the upper lane keeps
+// vals[HALF..2HALF) plus the partner's (stored back into vals[0..HALF)).
+template <int B, int HALF, int R>
+__device__ __forceinline__ void scatter_step(float (&vals)[R], int q) {
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+        if constexpr (B >= 4) {
+            float f, s;
+            row_swap<B>(vals[i], vals[i + HALF], f, s);
+            vals[i] = f + s;
+        } else {
+            const bool up = (q >> B) & 1;
+            const float send = up ? vals[i] : vals[i + HALF];
+            const float keep = up ? vals[i + HALF] : vals[i];
+            vals[i] = keep + lane_partner<B>(send);
+        }
+    }
+}
+
+// sum over the low LB bits of the lane group
+template <int LB>
+__device__ __forceinline__ float tree_sum_low(float x) {
+    if constexpr (LB >= 1) x += lane_partner<0>(x);
+    if constexpr (LB >= 2) x += lane_partner<1>(x);
+    if constexpr (LB >= 3) x += lane_partner<2>(x);
+    if constexpr (LB >= 4) x += lane_partner<3>(x);
+    if constexpr (LB >= 5) {
+        float f, s;
+        row_swap<4>(x, x, f, s);
+        x = f + s;
+    }
+    static_assert(LB <= 5, "at most 32 lanes below the scatter bits");
+    return x;
+}
+
 template <bool BF16, int N, int R, int V, int KBATCH>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(DecodeArgs a) {
     constexpr int HALF = N / 2;
     constexpr int NQ = HALF / V;            // lanes that share one row p
     constexpr int ROWS = kThreads / NQ;     // rows covered per pass of the workgroup
@@ -235,41 +271,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             __builtin_nontemporal_store(pack<V>(l), reinterpret_cast<vec *>(hbase + (int64_t)p * N + n0));
             __builtin_nontemporal_store(pack<V>(h), reinterpret_cast<vec *>(hbase + (int64_t)p * N + HALF + n0));
             if constexpr (R == 2 || R == 4) {
-                // reduce-scatter over the NQ lanes of the row: at each of the first
-                // log2(R) steps a lane keeps half of its partial sums and adds the
-                // partner's matching half, so R sums cost log2(NQ) + R - 1 shuffles
+                // reduce-scatter over the NQ lanes of the row: at the top log2(R)
+                // bits of the lane group a lane keeps half of its partial sums and
+                // adds the partner's matching half; the low bits then sum one value.
+                // A lane with group index q ends with the sum of rank
+                // q / (NQ / R).
+                constexpr int LNQ = (NQ >= 64) ? 6 : (NQ >= 32) ? 5 : (NQ >= 16) ? 4 : (NQ >= 8) ? 3 : (NQ >= 4) ? 2 : 1;
                 constexpr int LR = (R == 2) ? 1 : 2;
+                static_assert(LNQ >= LR, "the row needs at least R lanes");
                 float vals[R];
 #pragma unroll
                 for (int r = 0; r < R; ++r) vals[r] = yacc[r];
-                int cnt = R;
-#pragma unroll
-                for (int st = 0; st < LR; ++st) {
-                    const int o = NQ >> (st + 1);
-                    const bool up = (q & o) != 0;
-                    const int half = cnt / 2;
-#pragma unroll
-                    for (int i = 0; i < R / 2; ++i) {
-                        if (i < half) {
-                            const float send = up ? vals[i] : vals[i + half];
-                            const float keep = up ? vals[i + half] : vals[i];
-                            vals[i] = keep + __shfl_xor(send, o, 64);
-                        }
-                    }
-                    cnt = half;
-                }
-                float v = vals[0];
-#pragma unroll
-                for (int o = NQ / (2 * R); o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+                scatter_step<LNQ - 1, R / 2>(vals, q);
+                if constexpr (LR == 2) scatter_step<LNQ - 2, 1>(vals, q);
+                const float v = tree_sum_low<LNQ - LR>(vals[0]);
                 if (q % (NQ / R) == 0) st_io<BF16>(a.y, ybase + (q / (NQ / R)) * P + p, v);
             } else {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    float v = yacc[r];
-#pragma unroll
-                    for (int o = NQ / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-                    yacc[r] = v;
-                }
+                for (int r = 0; r < R; ++r) yacc[r] = group_sum<NQ>(yacc[r]);
                 if (q == 0) {
 #pragma unroll
                     for (int r = 0; r < R; ++r) st_io<BF16>(a.y, ybase + r * P + p, yacc[r]);

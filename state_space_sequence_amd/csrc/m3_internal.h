@@ -91,10 +91,64 @@ __device__ __forceinline__ void st_io(void *p, int64_t i, float v) {
         static_cast<float *>(p)[i] = v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+// ---- cross-lane exchanges without LDS round trips: DPP lane moves inside a
+// 16-lane row and the gfx950 row swaps across rows
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
+
+// The two halves a row swap brings together: for B = 4 lanes l and l ^ 16, for
+// B = 5 lanes l and l ^ 32. Returns (first, second) with first + second equal, in
+// the lower lane, to a + partner's a and, in the upper lane, to b + partner's b.
+template <int B>
+__device__ __forceinline__ void row_swap(float a, float b, float &first, float &second) {
+    static_assert(B == 4 || B == 5, "row swaps pair bit 4 or bit 5");
+    if constexpr (B == 4) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        first = __uint_as_float(p[0]);
+        second = __uint_as_float(p[1]);
+    } else {
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        first = __uint_as_float(p[0]);
+        second = __uint_as_float(p[1]);
+    }
+}
+
+// x of a partner lane whose index differs from this lane's in bit B (B <= 3). For
+// B = 2 and B = 3 the pairing (mirror of 8 / 16 lanes) also flips the lower bits;
+// callers rely only on it being an involution that flips bit B.
+template <int B>
+__device__ __forceinline__ float lane_partner(float x) {
+    static_assert(B >= 0 && B <= 3, "DPP pairings cover bits 0..3");
+    if constexpr (B == 0) return dpp_mov<0xB1>(x);        // quad_perm [1,0,3,2]
+    else if constexpr (B == 1) return dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    else if constexpr (B == 2) return dpp_mov<0x141>(x);  // row_half_mirror
+    else return dpp_mov<0x140>(x);                        // row_mirror
+}
+
+// x summed over the aligned group of G lanes (G a power of two, at most 64); the
+// low bits go first, so every mirror pairing meets lanes that already hold equal sums
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (G >= 2) x += lane_partner<0>(x);
+    if constexpr (G >= 4) x += lane_partner<1>(x);
+    if constexpr (G >= 8) x += lane_partner<2>(x);
+    if constexpr (G >= 16) x += lane_partner<3>(x);
+    if constexpr (G >= 32) {
+        float f, s;
+        row_swap<4>(x, x, f, s);
+        x = f + s;
+    }
+    if constexpr (G >= 64) {
+        float f, s;
+        row_swap<5>(x, x, f, s);
+        x = f + s;
+    }
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
 }  // namespace m3i

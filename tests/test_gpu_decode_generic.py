@@ -25,6 +25,12 @@ DECODE_CASES = [
     (4, 8, 1, 64, 128, 1, "bf16", False, False),
     (4, 8, 1, 64, 64, 4, "bf16", False, True),
     (1, 2, 1, 200, 32, 2, "bf16", True, False),
+    # every lane-group width of the output reductions: 64-lane rows (both row
+    # swaps), 4-lane rows with R = 4 (no tree), 32-lane SISO rows
+    (1, 3, 1, 48, 256, 4, "bf16", False, False),
+    (2, 2, 1, 16, 256, 2, "f32", False, True),
+    (2, 3, 1, 16, 16, 4, "f32", True, False),
+    (1, 2, 1, 32, 256, 1, "f32", False, False),
 ]
 
 
