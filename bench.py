@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_DENSE_TFLOPS = 2516.6     # MI355X dense bf16 MFMA, TFLOP/s
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_siso_prefill_1p5b.json")
+MFMA_BUSY_FILE = os.path.join(ROOT, "profiles", "pmc_mfma_busy_siso_prefill_1p5b.json")
 KERNEL_SRC = os.path.join(ROOT, "state_space_sequence_amd", "csrc", "m3_scan_mfma.hip")
 
 
@@ -111,6 +112,31 @@ def traffic_from_counters(bytes_alg):
     return pm.get("hbm_bytes_per_launch")
 
 
+def mfma_busy_from_counters():
+    """MFMA-busy fraction of the headline kernel from the committed counter summary
+    (SQ_VALU_MFMA_BUSY_CYCLES over all SIMDs and the kernel's cycles), if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(MFMA_BUSY_FILE) as f:
+            pm = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if pm.get("kernel_src_sha256") != src_digest():
+        return None
+    return pm.get("mfma_busy_frac")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(shape, chains_target):
     """The oracle as it stands, on a bounded sample: whole sequences of a few
     (batch, head) chains of the same workload, scaled to the workload's tokens/s."""
@@ -128,6 +154,13 @@ def cpu_baseline(shape, chains_target):
     chains = nb * H
     frac = chains / (shape.batch * shape.nheads)
     full_time = dt / frac
+    # one host thread on a smaller sample (one batch entry's heads / 8)
+    s1 = shape.replace(batch=1, nheads=max(1, H // 8))
+    inp1 = make_scan_inputs(s1, seed=98)
+    t1 = time.perf_counter()
+    oracle.scan(inp1, s1, nthreads=1)
+    dt1 = time.perf_counter() - t1
+    full_time1 = dt1 * (shape.batch * shape.nheads) / (s1.batch * s1.nheads)
     return {
         "value": shape.batch * shape.seqlen / full_time,
         "unit": "tokens/s",
@@ -136,6 +169,10 @@ def cpu_baseline(shape, chains_target):
         "sample": "%d of %d (batch, head) chains, full L=%d, fp64 C oracle with OpenMP over chains; "
                   "%.2f s measured, scaled by %d/%d" % (chains, shape.batch * shape.nheads, shape.seqlen, dt,
                                                          shape.batch * shape.nheads, chains),
+        "cpu_model": cpu_model(),
+        "value_1thread": shape.batch * shape.seqlen / full_time1,
+        "sample_1thread": "%d chains on one thread, %.2f s measured, scaled by %d/%d"
+                          % (s1.batch * s1.nheads, dt1, shape.batch * shape.nheads, s1.batch * s1.nheads),
     }
 
 
@@ -207,7 +244,8 @@ def main():
             "kernel": "scan_mfma_kernel<full, R=1>", "avg_launch_ms": round(kern_ms, 5),
             "alg_bytes_per_launch": balg,
             "mfma_frac_dense": round(fl_dense / (kern_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4),
-            "mfma_frac_causal": round(fl_causal / (kern_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4)}
+            "mfma_frac_causal": round(fl_causal / (kern_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4),
+            "mfma_busy_frac_counter": mfma_busy_from_counters()}
     log("prefill: %.4f ms/step, %.3e tokens/s, %.0f GB/s (%.1f%% of HBM peak)"
         % (kern_ms, value, achieved, 100 * achieved / HBM_PEAK_GBS))
     del d, y, hf
