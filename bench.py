@@ -62,10 +62,10 @@ def prefill_flops(s):
     return nch * dense, nch * causal
 
 
-def decode_bytes(s) -> int:
+def decode_bytes(s, state_bytes=4) -> int:
     io = 2 if s.io == "bf16" else 4
     b, H, G, P, N, R = s.batch, s.nheads, s.ngroups, s.headdim, s.dstate, s.rank
-    return (2 * b * H * P * N * 4               # state read + write
+    return (2 * b * H * P * N * state_bytes     # state read + write
             + 3 * b * H * R * P * io            # x, x_prev, y
             + 3 * b * G * R * N * io            # Braw, Craw, Braw_prev
             + 3 * b * H * 4 + b * G * (N // 2) * 4 + 2 * H * R * N * 4)
@@ -320,11 +320,16 @@ def main():
             torch.cuda.empty_cache()
         # ---- decode steps, cycling 4 state buffers so the 256 MB last-level cache
         # cannot hold the state between steps
-        for nm in ("decode_siso_n128", "decode_mimo4_n128", "decode_siso_n64", "decode_mimo4_n64"):
+        # (then the same four with the state stored in bf16)
+        decode_runs = [(nm, False) for nm in ("decode_siso_n128", "decode_mimo4_n128", "decode_siso_n64",
+                                              "decode_mimo4_n64")]
+        decode_runs += [(nm, True) for nm, _ in decode_runs]
+        for nm, bf16_state in decode_runs:
             sd = WORKLOADS[nm]
             dinp = make_decode_inputs(sd, seed=3)
             de = m3.to_device(dinp, sd.io)
-            states = [de["h"].clone() for _ in range(4)]
+            h0 = de["h"].to(torch.bfloat16) if bf16_state else de["h"]
+            states = [h0.clone() for _ in range(4)]
             ydec = torch.empty_like(de["x"])
             base = (de["x"], de["Braw"], de["Craw"], de["dt"], de["A"], de["lam"], de["theta"],
                     de["B_bias"], de["C_bias"])
@@ -340,12 +345,13 @@ def main():
             torch.cuda.synchronize()
             tms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(reps))
             med = tms[reps // 2]
-            bb = decode_bytes(sd)
+            bb = decode_bytes(sd, 2 if bf16_state else 4)
             ent = {"us_per_step": round(1e3 * med, 2), "p10_us": round(1e3 * tms[reps // 10], 2),
                    "p90_us": round(1e3 * tms[(9 * reps) // 10], 2),
                    "hbm_frac": round(bb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bb}
-            log(nm, ent)
-            extra[nm] = ent
+            key = nm + ("_bf16state" if bf16_state else "")
+            log(key, ent)
+            extra[key] = ent
             del de, states
             torch.cuda.empty_cache()
 

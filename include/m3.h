@@ -68,6 +68,11 @@ typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
 /* flags */
 #define M3_FLAG_FORCE_GENERIC 1u /* use the fp32 vector-ALU chunked kernel even where
                                     the bf16 matrix-core kernel applies */
+#define M3_FLAG_BF16_STATE 2u    /* decode only: the state h is stored as bf16 [b,H,P,N],
+                                    read, updated in fp32 and written back rounded to
+                                    nearest even (the Mamba-3 paper times decode with
+                                    fp32 and with bf16 state, §4.4 Table 6). m3_scan_fwd
+                                    rejects it with M3_ERR_INVALID_ARG. */
 
 typedef struct {
     int64_t batch;     /* b >= 0 */
@@ -125,7 +130,8 @@ typedef struct {
     const float *C_normw;  /* [N] or NULL */
     const void *x_prev;    /* [b,H,R,P] io, previous token, or NULL (first token) */
     const void *Braw_prev; /* [b,G,R,N] io, or NULL; both or neither */
-    float *h;              /* in/out [b,H,P,N] state, updated in place */
+    void *h;               /* in/out [b,H,P,N] state, updated in place: fp32, or bf16
+                              with M3_FLAG_BF16_STATE */
     void *y;               /* out [b,H,R,P] io */
 } m3_decode_io;
 

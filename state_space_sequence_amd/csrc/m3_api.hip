@@ -43,6 +43,7 @@ m3_status check_shape(const m3_shape *s) {
     if (s->io_dtype != M3_F32 && s->io_dtype != M3_BF16) return M3_ERR_INVALID_ARG;
     if (!(s->eps >= 0.f) || !isfinite(s->eps)) return M3_ERR_INVALID_ARG;
     if (s->nsegments < 0) return M3_ERR_INVALID_ARG;
+    if (s->flags & ~M3_FLAG_FORCE_GENERIC) return M3_ERR_INVALID_ARG;  // (the bf16-state flag is decode only)
     if (s->batch > (1LL << 31) || s->nheads > (1LL << 20) || s->seqlen > (1LL << 40)) return M3_ERR_UNSUPPORTED;
     return M3_OK;
 }
@@ -95,7 +96,7 @@ const char *m3_status_str(m3_status st) {
     return "unknown status";
 }
 
-int m3_version(void) { return 100; }
+int m3_version(void) { return 101; }
 
 m3_status m3_scan_plan(const m3_shape *shape, m3_plan *plan) {
     m3_status st = check_shape(shape);
@@ -178,6 +179,7 @@ m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *st
     if (s.batch < 0 || s.nheads < 1 || s.ngroups < 1 || s.headdim < 1 || s.dstate < 2 || s.rank < 1)
         return M3_ERR_INVALID_ARG;
     if (s.nheads % s.ngroups != 0 || s.dstate % 2 != 0) return M3_ERR_INVALID_ARG;
+    if (s.flags & ~M3_FLAG_BF16_STATE) return M3_ERR_INVALID_ARG;
     if (s.io_dtype != M3_F32 && s.io_dtype != M3_BF16) return M3_ERR_INVALID_ARG;
     if (!(s.eps >= 0.f) || !isfinite(s.eps)) return M3_ERR_INVALID_ARG;
     if ((io->x_prev == nullptr) != (io->Braw_prev == nullptr)) return M3_ERR_INVALID_ARG;
@@ -199,6 +201,7 @@ m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *st
     a.x = io->x; a.Braw = io->Braw; a.Craw = io->Craw; a.dt = io->dt; a.A = io->A; a.lam = io->lam;
     a.theta = io->theta; a.B_bias = io->B_bias; a.C_bias = io->C_bias; a.B_normw = io->B_normw;
     a.C_normw = io->C_normw; a.x_prev = io->x_prev; a.Braw_prev = io->Braw_prev; a.h = io->h; a.y = io->y;
+    a.bf16_state = (s.flags & M3_FLAG_BF16_STATE) != 0;
     hipError_t e = launch_decode(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }

@@ -20,6 +20,8 @@
 // are formed once per workgroup in LDS. State rows are streamed with
 // non-temporal accesses (read once, written once). y for a row is reduced over
 // the N/(2V) lanes that share the row.
+#include <type_traits>
+
 #include "m3_internal.h"
 
 namespace m3i {
@@ -101,14 +103,68 @@ __device__ __forceinline__ float tree_sum_low(float x) {
     return x;
 }
 
-template <bool BF16, int N, int R, int V, int KBATCH>
+// Registers of V state columns: V floats for an fp32 state, V bf16 values packed
+// in V/2 dwords for a bf16 state (arithmetic is fp32 either way).
+template <bool BS, int V>
+struct StateT {
+    typedef typename VecT<V>::type type;
+};
+template <>
+struct StateT<true, 4> {
+    typedef unsigned int type __attribute__((ext_vector_type(2)));
+};
+template <>
+struct StateT<true, 2> {
+    typedef unsigned int type;
+};
+
+__device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 v = {(__bf16)a, (__bf16)b};  // round to nearest even
+    return __builtin_bit_cast(unsigned int, v);
+}
+
+template <bool BS, int V>
+__device__ __forceinline__ void unpack_state(const typename StateT<BS, V>::type &v, float *o) {
+    if constexpr (!BS) {
+        unpack<V>(v, o);
+    } else if constexpr (V == 2) {
+        o[0] = __uint_as_float(v << 16);
+        o[1] = __uint_as_float(v & 0xffff0000u);
+    } else {
+        static_assert(V == 4, "bf16 state: 2 or 4 columns per thread");
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            o[2 * k] = __uint_as_float(v[k] << 16);
+            o[2 * k + 1] = __uint_as_float(v[k] & 0xffff0000u);
+        }
+    }
+}
+
+template <bool BS, int V>
+__device__ __forceinline__ typename StateT<BS, V>::type pack_state(const float *o) {
+    if constexpr (!BS) {
+        return pack<V>(o);
+    } else if constexpr (V == 2) {
+        return pack_bf16x2(o[0], o[1]);
+    } else {
+        typename StateT<true, 4>::type v;
+        v[0] = pack_bf16x2(o[0], o[1]);
+        v[1] = pack_bf16x2(o[2], o[3]);
+        return v;
+    }
+}
+
+template <bool BF16, bool BS, int N, int R, int V, int KBATCH>
 __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(DecodeArgs a) {
     constexpr int HALF = N / 2;
     constexpr int NQ = HALF / V;            // lanes that share one row p
     constexpr int ROWS = kThreads / NQ;     // rows covered per pass of the workgroup
     constexpr int KB = KBATCH;              // passes whose state is held in registers at once
     static_assert(NQ >= 2 && NQ <= 64 && (64 % NQ) == 0, "unsupported N/V");
-    typedef typename VecT<V>::type vec;
+    typedef typename VecT<V>::type vec;       // V floats (LDS coefficient reads)
+    typedef typename StateT<BS, V>::type svec;  // V state values as stored
+    typedef typename std::conditional<BS, __bf16, float>::type selem;
 
     extern __shared__ float sm[];
     // every array below starts on a 16-byte boundary (sizes are multiples of 4
@@ -135,16 +191,16 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     const int n0 = V * q;
     const int prow = tid / NQ;
     const int passes = (P + ROWS - 1) / ROWS;
-    float *hbase = a.h + bh * (int64_t)P * N;
+    selem *hbase = static_cast<selem *>(a.h) + bh * (int64_t)P * N;
 
     // ---- first batch of state rows: in flight during the set-up below
-    vec lo[KB], hiv[KB];
+    svec lo[KB], hiv[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
         const int p = prow + k * ROWS;
         if (k < passes && p < P) {
-            lo[k] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(hbase + (int64_t)p * N + n0));
-            hiv[k] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(hbase + (int64_t)p * N + HALF + n0));
+            lo[k] = __builtin_nontemporal_load(reinterpret_cast<const svec *>(hbase + (int64_t)p * N + n0));
+            hiv[k] = __builtin_nontemporal_load(reinterpret_cast<const svec *>(hbase + (int64_t)p * N + HALF + n0));
         }
     }
 
@@ -227,8 +283,8 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
             for (int k = 0; k < KB; ++k) {
                 const int p = prow + (kb + k) * ROWS;
                 if (kb + k < passes && p < P) {
-                    lo[k] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(hbase + (int64_t)p * N + n0));
-                    hiv[k] = __builtin_nontemporal_load(reinterpret_cast<const vec *>(hbase + (int64_t)p * N + HALF + n0));
+                    lo[k] = __builtin_nontemporal_load(reinterpret_cast<const svec *>(hbase + (int64_t)p * N + n0));
+                    hiv[k] = __builtin_nontemporal_load(reinterpret_cast<const svec *>(hbase + (int64_t)p * N + HALF + n0));
                 }
             }
         }
@@ -245,8 +301,8 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
                 xpv[r] = sxp[p * R + r];
             }
             float l[V], h[V];
-            unpack<V>(lo[k], l);
-            unpack<V>(hiv[k], h);
+            unpack_state<BS, V>(lo[k], l);
+            unpack_state<BS, V>(hiv[k], h);
             float yacc[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) yacc[r] = 0.f;
@@ -268,8 +324,8 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
 #pragma unroll
                 for (int r = 0; r < R; ++r) yacc[r] += cl[r][c] * nu + ch[r][c] * nv;
             }
-            __builtin_nontemporal_store(pack<V>(l), reinterpret_cast<vec *>(hbase + (int64_t)p * N + n0));
-            __builtin_nontemporal_store(pack<V>(h), reinterpret_cast<vec *>(hbase + (int64_t)p * N + HALF + n0));
+            __builtin_nontemporal_store(pack_state<BS, V>(l), reinterpret_cast<svec *>(hbase + (int64_t)p * N + n0));
+            __builtin_nontemporal_store(pack_state<BS, V>(h), reinterpret_cast<svec *>(hbase + (int64_t)p * N + HALF + n0));
             if constexpr (R == 2 || R == 4) {
                 // reduce-scatter over the NQ lanes of the row: at the top log2(R)
                 // bits of the lane group a lane keeps half of its partial sums and
@@ -298,28 +354,28 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     }
 }
 
-template <bool BF16, int N>
+template <bool BF16, bool BS, int N>
 hipError_t launch_n(const DecodeArgs &a, hipStream_t s) {
     const size_t smem = sizeof(float) * (5 * a.R * N + 3 * N + 4 * a.R + 2 * a.R * a.P);
     dim3 grid((unsigned)(a.b * a.H)), block(kThreads);
     switch (a.R) {
-        case 1: hipLaunchKernelGGL((decode_kernel<BF16, N, 1, 4, 2>), grid, block, smem, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<BF16, N, 2, 2, 4>), grid, block, smem, s, a); break;
-        case 3: hipLaunchKernelGGL((decode_kernel<BF16, N, 3, 2, 4>), grid, block, smem, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<BF16, N, 4, 2, 4>), grid, block, smem, s, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 1, 4, 2>), grid, block, smem, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 2, 2, 4>), grid, block, smem, s, a); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 3, 2, 4>), grid, block, smem, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 4, 2, 4>), grid, block, smem, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <bool BF16>
+template <bool BF16, bool BS>
 hipError_t launch_io(const DecodeArgs &a, hipStream_t s) {
     switch (a.N) {
-        case 16: return launch_n<BF16, 16>(a, s);
-        case 32: return launch_n<BF16, 32>(a, s);
-        case 64: return launch_n<BF16, 64>(a, s);
-        case 128: return launch_n<BF16, 128>(a, s);
-        case 256: return launch_n<BF16, 256>(a, s);
+        case 16: return launch_n<BF16, BS, 16>(a, s);
+        case 32: return launch_n<BF16, BS, 32>(a, s);
+        case 64: return launch_n<BF16, BS, 64>(a, s);
+        case 128: return launch_n<BF16, BS, 128>(a, s);
+        case 256: return launch_n<BF16, BS, 256>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -328,7 +384,8 @@ hipError_t launch_io(const DecodeArgs &a, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     if (a.b * a.H == 0) return hipSuccess;
-    return a.bf16 ? launch_io<true>(a, s) : launch_io<false>(a, s);
+    if (a.bf16_state) return a.bf16 ? launch_io<true, true>(a, s) : launch_io<false, true>(a, s);
+    return a.bf16 ? launch_io<true, false>(a, s) : launch_io<false, false>(a, s);
 }
 
 }  // namespace m3i

@@ -32,7 +32,8 @@ struct DecodeArgs {
     const float *dt, *A, *lam, *theta;
     const float *B_bias, *C_bias, *B_normw, *C_normw;
     const void *x_prev, *Braw_prev;
-    float *h;
+    void *h;          // [b,H,P,N] fp32, or bf16 when bf16_state
+    bool bf16_state;  // state stored as bf16 (rounded to nearest even), arithmetic in fp32
     void *y;
 };
 

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libm3.so")
 M3_OK = 0
 M3_F32, M3_BF16 = 0, 1
 M3_FLAG_FORCE_GENERIC = 1
+M3_FLAG_BF16_STATE = 2
 
 
 class Shape(ctypes.Structure):
@@ -153,10 +154,12 @@ def scan_fwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *, chunk=64, eps=
 def decode_step(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, h, *, eps=1e-5,
                 B_normw=None, C_normw=None, x_prev=None, Braw_prev=None, y=None, stream=None):
     """One decode step (m3_decode_step). x [b,H,R,P], Braw/Craw [b,G,R,N], dt/A/lam [b,H],
-    theta [b,G,N/2], h [b,H,P,N] fp32 updated in place. Returns y [b,H,R,P]."""
+    theta [b,G,N/2], h [b,H,P,N] updated in place: fp32, or bf16 (then the step runs with
+    M3_FLAG_BF16_STATE). Returns y [b,H,R,P]."""
     b, H, R, P = x.shape
     G, N = Braw.shape[1], Braw.shape[3]
-    shape = make_shape(b, 1, H, G, P, N, R, 1, _io_dtype(x), eps)
+    flags = M3_FLAG_BF16_STATE if h.dtype == torch.bfloat16 else 0
+    shape = make_shape(b, 1, H, G, P, N, R, 1, _io_dtype(x), eps, flags)
     if y is None:
         y = torch.empty_like(x)
     io = DecodeIO(_ptr(x), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),

@@ -30,12 +30,16 @@ def gpu_scan(inp, shape, **kw):
     return y.float().cpu().numpy().astype(np.float64), h.cpu().numpy().astype(np.float64)
 
 
-def gpu_decode(inp, shape):
+def gpu_decode(inp, shape, bf16_state=False):
+    """One decode step on the GPU. With bf16_state the state is handed over as bf16
+    (the caller passes a state whose values are bf16-exact) and comes back as bf16."""
     from state_space_sequence_amd import m3
     d = m3.to_device(inp, shape.io)
     h = d["h"].clone()
+    if bf16_state:
+        h = h.to(torch.bfloat16)
     y = m3.decode_step(d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"],
                        d["B_bias"], d["C_bias"], h, eps=shape.eps, B_normw=d.get("B_normw"),
                        C_normw=d.get("C_normw"), x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"))
     torch.cuda.synchronize()
-    return y.float().cpu().numpy().astype(np.float64), h.cpu().numpy().astype(np.float64)
+    return y.float().cpu().numpy().astype(np.float64), h.float().cpu().numpy().astype(np.float64)

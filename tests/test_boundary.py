@@ -116,6 +116,21 @@ def test_decode_validation(m3):
     assert m3.lib.m3_decode_step(None, ctypes.byref(io), None) == -1
 
 
+def test_flags_validated(m3):
+    """The bf16-state flag is decode only; unknown flag bits are rejected by both calls."""
+    assert m3.M3_FLAG_BF16_STATE == 2
+    assert _scan(m3, _shape(m3, flags=m3.M3_FLAG_BF16_STATE), _fake_io(m3)) == -1
+    assert _scan(m3, _shape(m3, flags=8), _fake_io(m3)) == -1
+    io = m3.DecodeIO()
+    s = _shape(m3, flags=m3.M3_FLAG_FORCE_GENERIC)
+    assert m3.lib.m3_decode_step(ctypes.byref(s), ctypes.byref(io), None) == -1
+    # with the bf16-state flag the decode call gets past the flag check (and stops at the NULL tensors)
+    s = _shape(m3, flags=m3.M3_FLAG_BF16_STATE)
+    assert m3.lib.m3_decode_step(ctypes.byref(s), ctypes.byref(io), None) == -1
+    s = _shape(m3, batch=0, flags=m3.M3_FLAG_BF16_STATE)
+    assert m3.lib.m3_decode_step(ctypes.byref(s), ctypes.byref(io), None) == 0
+
+
 def test_plans_for_workloads(m3):
     from state_space_sequence_amd.inputs import WORKLOADS
     for name, w in WORKLOADS.items():

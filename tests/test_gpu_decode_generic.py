@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
-from state_space_sequence_amd.inputs import WORKLOADS, Shape, make_decode_inputs, make_scan_inputs
+from state_space_sequence_amd.inputs import WORKLOADS, Shape, make_decode_inputs, make_scan_inputs, round_bf16
 from tests.gpu_helpers import TOL_BF16, TOL_F32, gpu_decode, gpu_scan, relerr
 
 pytestmark = pytest.mark.gpu
@@ -137,3 +137,66 @@ def test_generic_is_deterministic():
     y1, h1 = gpu_scan(inp, shape, force_generic=True)
     y2, h2 = gpu_scan(inp, shape, force_generic=True)
     assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+# ---- decode with the state stored in bf16 (read and written as bf16, updated in fp32)
+BF16_STATE_CASES = [
+    # (b, H, G, P, N, R, io, first_token)
+    (3, 4, 1, 64, 128, 1, "bf16", False),
+    (2, 4, 1, 64, 128, 4, "bf16", False),
+    (2, 6, 2, 32, 64, 2, "f32", True),
+    (1, 3, 1, 48, 256, 4, "bf16", False),
+    (2, 2, 1, 16, 16, 3, "f32", False),
+]
+# A state rounded to nearest even in bf16 (8 significant bits) is within half an
+# ulp of the fp32 result: at most 2^-8 of the largest power of two not above the
+# element, so at most 2^-8 = 3.9e-3 against the largest element; the fp32
+# arithmetic adds ~1e-6.
+TOL_BF16_STATE = 4e-3
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", BF16_STATE_CASES)
+def test_decode_bf16_state_matches_oracle(case):
+    b, H, G, P, N, R, io, first = case
+    shape = Shape(b, 1, H, G, P, N, R, 1, io)
+    say("decode bf16 state", case)
+    inp = make_decode_inputs(shape, seed=12, first_token=first)
+    inp["h"] = round_bf16(inp["h"])  # the stored state is bf16: both sides start from its values
+    y, h = gpu_decode(inp, shape, bf16_state=True)
+    yr, hr = oracle.decode(inp, shape)
+    say("err y %.2e h %.2e" % (relerr(y, yr), relerr(h, hr)))
+    assert relerr(h, hr) < TOL_BF16_STATE
+    # y comes from the fp32 update before the state is rounded
+    assert relerr(y, yr) < (TOL_F32 if io == "f32" else TOL_BF16)
+    # the stored state is exactly representable in bf16
+    assert np.array_equal(round_bf16(h.astype(np.float32)), h.astype(np.float32))
+
+
+@pytest.mark.gpu
+def test_decode_bf16_state_several_steps():
+    """Eight chained steps with a bf16 state against the oracle stepped the same
+    way (its state rounded to bf16 between steps, by the test)."""
+    shape = Shape(2, 1, 4, 1, 64, 128, 4, 1, "bf16")
+    steps = [make_decode_inputs(shape, seed=40 + k, first_token=(k == 0)) for k in range(8)]
+    h_ref = round_bf16(steps[0]["h"]).astype(np.float64)
+    import torch
+    from state_space_sequence_amd import m3
+    h_gpu = torch.from_numpy(h_ref.astype(np.float32)).cuda().to(torch.bfloat16)
+    for k, inp in enumerate(steps):
+        if k > 0:  # the previous token's x and raw B carry the trapezoid's second term
+            inp["x_prev"], inp["Braw_prev"] = steps[k - 1]["x"], steps[k - 1]["Braw"]
+        inp["h"] = h_ref.astype(np.float32)
+        yr, hr = oracle.decode(inp, shape)
+        d = m3.to_device(inp, shape.io)
+        y = m3.decode_step(d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"],
+                           d["B_bias"], d["C_bias"], h_gpu, eps=shape.eps,
+                           x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"))
+        torch.cuda.synchronize()
+        yg = y.float().cpu().numpy()
+        hg = h_gpu.float().cpu().numpy()
+        say("step %d err y %.2e h %.2e" % (k, relerr(yg, yr), relerr(hg, hr)))
+        # one rounding per step on each side, not always to the same neighbour
+        assert relerr(yg, yr) < TOL_BF16 and relerr(hg, hr) < 4 * TOL_BF16_STATE
+        # the GPU keeps its own chained state; the oracle's is rounded the same way
+        h_ref = round_bf16(hr.astype(np.float32)).astype(np.float64)
