@@ -88,3 +88,54 @@ def decode(inp: dict, shape, *, nthreads: int = 0):
     d["h0"] = inp["h"]
     y, h = scan(d, s, nthreads=nthreads)
     return y[:, 0], h
+
+
+# ---------------------------------------------------------------------------
+# Fused MIMO projections and output gate (Mamba-3 paper, App. C "MIMO for
+# Mamba-3"): inside a head, the rank-R input is the per-rank scaling of one
+# P-vector, the gate Z is formed the same way, the SSM output Y (P x R) is
+# gated by SiLU(Z) and contracted back to P with per-(p, r) weights.
+# Weights are per head: W_X, W_Z, W_O of shape [H, P, R].
+
+def expand_ranks(v, W):
+    """App. C, X_t = contract(PR, P -> PR)(W_X, X'_t): out[..., h, r, p] = W[h, p, r] * v[..., h, p].
+    v has shape [..., H, P]; returns float64 [..., H, R, P]."""
+    v = np.asarray(v, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    return v[..., None, :] * np.swapaxes(W, -1, -2)
+
+
+def silu(z):
+    """App. C's residual function uses SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def gate_contract(y, z_in, W_Z, W_O):
+    """App. C: Z = W_Z (.) Z' (as for X), Y' = Y (.) SiLU(Z), O' = contract(PR, PR -> P)(W_O', Y'):
+    O'[..., h, p] = sum_r W_O[h, p, r] * Y[..., h, r, p] * SiLU(Z[..., h, r, p])."""
+    z = expand_ranks(z_in, W_Z)
+    gated = np.asarray(y, dtype=np.float64) * silu(z)
+    return np.einsum("...hrp,hpr->...hp", gated, np.asarray(W_O, dtype=np.float64))
+
+
+def scan_fused(inp: dict, shape, *, nthreads: int = 0, want_state: bool = True):
+    """Prefill with the fused projections: inputs carry x_in [b,L,H,P] (X'), z_in [b,L,H,P] (Z'),
+    W_X / W_Z / W_O [H,P,R] and, optionally, x_prev_in [b,H,P]. Returns (O' [b,L,H,P], h_final)."""
+    d = dict(inp)
+    d["x"] = expand_ranks(inp["x_in"], inp["W_X"]).astype(np.float32)
+    xp = inp.get("x_prev_in")
+    d["x_prev"] = None if xp is None else expand_ranks(xp, inp["W_X"]).astype(np.float32)
+    y, h = scan(d, shape, nthreads=nthreads, want_state=want_state)
+    return gate_contract(y, inp["z_in"], inp["W_Z"], inp["W_O"]), h
+
+
+def decode_fused(inp: dict, shape, *, nthreads: int = 0):
+    """One decode step with the fused projections (per-token tensors without the L axis:
+    x_in, z_in [b,H,P], x_prev_in [b,H,P] or absent). Returns (O' [b,H,P], h_new)."""
+    d = dict(inp)
+    d["x"] = expand_ranks(inp["x_in"], inp["W_X"]).astype(np.float32)
+    xp = inp.get("x_prev_in")
+    d["x_prev"] = None if xp is None else expand_ranks(xp, inp["W_X"]).astype(np.float32)
+    y, h = decode(d, shape, nthreads=nthreads)
+    return gate_contract(y, inp["z_in"], inp["W_Z"], inp["W_O"]), h

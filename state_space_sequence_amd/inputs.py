@@ -38,6 +38,8 @@ __all__ = [
     "round_bf16",
     "make_scan_inputs",
     "make_decode_inputs",
+    "make_fused_scan_inputs",
+    "make_fused_decode_inputs",
     "slice_chain",
 ]
 
@@ -172,6 +174,51 @@ def make_decode_inputs(shape: Shape, seed: int, *, first_token: bool = False,
     return out
 
 
+def _fused_extras(shape: Shape, seed: int, lead: tuple, with_prev: bool) -> dict:
+    """Draws for the fused MIMO projections and gate: X', Z' ~ N(0,1) of shape
+    lead + (H, P) in the io dtype; per-head weights W_X, W_Z ~ 1 + 0.5 N(0,1) and
+    W_O ~ N(0,1)/sqrt(R), shape [H, P, R], fp32; X' of the previous token when asked."""
+    H, P, R = shape.nheads, shape.headdim, shape.rank
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    bf = shape.io == "bf16"
+
+    def io_cast(a):
+        return round_bf16(a) if bf else np.ascontiguousarray(a, dtype=np.float32)
+
+    out = dict(
+        x_in=io_cast(_normal(rng, lead + (H, P))),
+        z_in=io_cast(_normal(rng, lead + (H, P))),
+        W_X=(1.0 + 0.5 * rng.standard_normal(size=(H, P, R))).astype(np.float32),
+        W_Z=(1.0 + 0.5 * rng.standard_normal(size=(H, P, R))).astype(np.float32),
+        W_O=(rng.standard_normal(size=(H, P, R)) / math.sqrt(R)).astype(np.float32),
+    )
+    out["x_prev_in"] = io_cast(_normal(rng, (lead[0], H, P))) if with_prev else None
+    return out
+
+
+def make_fused_scan_inputs(shape: Shape, seed: int, **kw) -> dict:
+    """Prefill inputs for the fused projections: the make_scan_inputs draws (B, C, dt,
+    A, lambda, theta, biases, optional h0 / gains / previous raw B) with x replaced by
+    X' [b,L,H,P] and the gate and weights added (x and x_prev are None)."""
+    d = make_scan_inputs(shape, seed, **kw)
+    d.update(_fused_extras(shape, seed, (shape.batch, shape.seqlen), d["x_prev"] is not None))
+    d["x"] = None
+    d["x_prev"] = None
+    return d
+
+
+def make_fused_decode_inputs(shape: Shape, seed: int, *, first_token: bool = False,
+                             with_normw: bool = False) -> dict:
+    """Decode inputs for the fused projections: make_decode_inputs with x replaced
+    by X' [b,H,P], plus Z' [b,H,P], the weights and (unless first_token) X' of the
+    previous token."""
+    d = make_decode_inputs(shape, seed, first_token=first_token, with_normw=with_normw)
+    d.update(_fused_extras(shape, seed, (shape.batch,), not first_token))
+    d["x"] = None
+    d["x_prev"] = None
+    return d
+
+
 def slice_chain(inp: dict, shape: Shape, b: int, h: int) -> tuple[dict, Shape]:
     """Cut the prefill inputs of one (batch, head) chain out of a full input set,
     as a batch-1, one-head, one-group problem. Chains are independent, so this is
@@ -182,13 +229,13 @@ def slice_chain(inp: dict, shape: Shape, b: int, h: int) -> tuple[dict, Shape]:
     for k, v in inp.items():
         if v is None:
             out[k] = None
-        elif k in ("x", "dt", "A", "lam"):
+        elif k in ("x", "dt", "A", "lam", "x_in", "z_in"):
             out[k] = np.ascontiguousarray(v[b:b + 1, :, h:h + 1])
         elif k in ("Braw", "Craw", "theta"):
             out[k] = np.ascontiguousarray(v[b:b + 1, :, g:g + 1])
-        elif k in ("B_bias", "C_bias"):
+        elif k in ("B_bias", "C_bias", "W_X", "W_Z", "W_O"):
             out[k] = np.ascontiguousarray(v[h:h + 1])
-        elif k in ("h0", "x_prev"):
+        elif k in ("h0", "x_prev", "x_prev_in"):
             out[k] = np.ascontiguousarray(v[b:b + 1, h:h + 1])
         elif k == "Braw_prev":
             out[k] = np.ascontiguousarray(v[b:b + 1, g:g + 1])
