@@ -111,8 +111,18 @@ typedef struct {
                               with them, position 0 gets the beta term of the
                               trapezoid; without, it has none (§3.1.3 unrolling
                               starts from h_0 = gamma_0 B_0 x_0) */
-    void *y;               /* out [b,L,H,R,P] io */
+    void *y;               /* out [b,L,H,R,P] io (not written, may be NULL, with W_X set) */
     float *h_final;        /* out [b,H,P,N] state after position L-1, or NULL */
+    /* Fused MIMO projections and output gate (Mamba-3 paper App. C), all NULL to
+     * leave them out. With W_X set, x and x_prev hold X' [b,L,H,P] and [b,H,P]
+     * (no rank axis); the kernel forms X[r][p] = W_X[h][p][r] X'[p], runs the
+     * recurrence, and writes o[p] = sum_r W_O[h][p][r] Y[r][p] SiLU(W_Z[h][p][r] Z'[p])
+     * instead of y. Needs the bf16 matrix-core shape (M3_ERR_UNSUPPORTED otherwise). */
+    const void *z;         /* [b,L,H,P] io: Z' */
+    const float *W_X;      /* [H,P,R] rank expansion of X' */
+    const float *W_Z;      /* [H,P,R] rank expansion of Z' */
+    const float *W_O;      /* [H,P,R] contraction of the gated output over the ranks */
+    void *o;               /* out [b,L,H,P] io */
 } m3_scan_io;
 
 /* Decode (single token) arguments: the per-token tensors have no L axis. */
@@ -132,7 +142,13 @@ typedef struct {
     const void *Braw_prev; /* [b,G,R,N] io, or NULL; both or neither */
     void *h;               /* in/out [b,H,P,N] state, updated in place: fp32, or bf16
                               with M3_FLAG_BF16_STATE */
-    void *y;               /* out [b,H,R,P] io */
+    void *y;               /* out [b,H,R,P] io (not written, may be NULL, with W_X set) */
+    /* Fused MIMO projections and gate, as in m3_scan_io: x and x_prev are X' [b,H,P] */
+    const void *z;         /* [b,H,P] io: Z' */
+    const float *W_X;      /* [H,P,R] */
+    const float *W_Z;      /* [H,P,R] */
+    const float *W_O;      /* [H,P,R] */
+    void *o;               /* out [b,H,P] io */
 } m3_decode_io;
 
 /* What m3_scan_fwd will launch for a shape (for logs and tests). */

@@ -96,7 +96,7 @@ const char *m3_status_str(m3_status st) {
     return "unknown status";
 }
 
-int m3_version(void) { return 101; }
+int m3_version(void) { return 102; }
 
 m3_status m3_scan_plan(const m3_shape *shape, m3_plan *plan) {
     m3_status st = check_shape(shape);
@@ -127,17 +127,21 @@ m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspa
     const m3_shape &s = *shape;
     if ((io->x_prev == nullptr) != (io->Braw_prev == nullptr)) return M3_ERR_INVALID_ARG;
     const bool work = s.batch * s.seqlen > 0;
+    const bool fused = io->W_X != nullptr;
+    if (fused && (!io->W_Z || !io->W_O)) return M3_ERR_INVALID_ARG;
+    if (!fused && (io->W_Z || io->W_O || io->z || io->o)) return M3_ERR_INVALID_ARG;
     if (work && (!io->x || !io->Braw || !io->Craw || !io->dt || !io->A || !io->lam || !io->theta ||
-                 !io->B_bias || !io->C_bias || !io->y))
+                 !io->B_bias || !io->C_bias || (fused ? (!io->z || !io->o) : !io->y)))
         return M3_ERR_INVALID_ARG;
     const void *ptrs[] = {io->x, io->Braw, io->Craw, io->dt, io->A, io->lam, io->theta, io->B_bias,
                           io->C_bias, io->B_normw, io->C_normw, io->h0, io->x_prev, io->Braw_prev,
-                          io->y, io->h_final, workspace};
+                          io->y, io->h_final, workspace, io->z, io->W_X, io->W_Z, io->W_O, io->o};
     for (const void *p : ptrs)
         if (!aligned16(p)) return M3_ERR_MISALIGNED;
     Plan p;
     st = make_plan(s, &p);
     if (st != M3_OK) return st;
+    if (fused && p.kernel != 1) return M3_ERR_UNSUPPORTED;  // the fp32 kernel does not take the fused form
     if (p.ws_bytes > 0 && (workspace == nullptr || ws_bytes < p.ws_bytes)) return M3_ERR_WORKSPACE_TOO_SMALL;
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -149,6 +153,7 @@ m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspa
     a.theta = io->theta; a.B_bias = io->B_bias; a.C_bias = io->C_bias; a.B_normw = io->B_normw;
     a.C_normw = io->C_normw; a.h0 = io->h0; a.x_prev = io->x_prev; a.Braw_prev = io->Braw_prev;
     a.y = io->y; a.h_final = io->h_final;
+    a.fused = fused; a.z = io->z; a.W_X = io->W_X; a.W_Z = io->W_Z; a.W_O = io->W_O; a.o = io->o;
 
     hipError_t e = hipSuccess;
     if (s.batch * s.nheads == 0) return M3_OK;
@@ -187,11 +192,15 @@ m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *st
     if (!(N == 16 || N == 32 || N == 64 || N == 128 || N == 256) || s.headdim > kDecodeMaxP ||
         s.rank > kDecodeMaxR || s.batch > (1LL << 31))
         return M3_ERR_UNSUPPORTED;
+    const bool fused = io->W_X != nullptr;
+    if (fused && (!io->W_Z || !io->W_O)) return M3_ERR_INVALID_ARG;
+    if (!fused && (io->W_Z || io->W_O || io->z || io->o)) return M3_ERR_INVALID_ARG;
     if (s.batch > 0 && (!io->x || !io->Braw || !io->Craw || !io->dt || !io->A || !io->lam || !io->theta ||
-                        !io->B_bias || !io->C_bias || !io->h || !io->y))
+                        !io->B_bias || !io->C_bias || !io->h || (fused ? (!io->z || !io->o) : !io->y)))
         return M3_ERR_INVALID_ARG;
     const void *ptrs[] = {io->x, io->Braw, io->Craw, io->dt, io->A, io->lam, io->theta, io->B_bias,
-                          io->C_bias, io->B_normw, io->C_normw, io->x_prev, io->Braw_prev, io->h, io->y};
+                          io->C_bias, io->B_normw, io->C_normw, io->x_prev, io->Braw_prev, io->h, io->y,
+                          io->z, io->W_X, io->W_Z, io->W_O, io->o};
     for (const void *p : ptrs)
         if (!aligned16(p)) return M3_ERR_MISALIGNED;
     if (s.batch == 0) return M3_OK;
@@ -202,6 +211,7 @@ m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *st
     a.theta = io->theta; a.B_bias = io->B_bias; a.C_bias = io->C_bias; a.B_normw = io->B_normw;
     a.C_normw = io->C_normw; a.x_prev = io->x_prev; a.Braw_prev = io->Braw_prev; a.h = io->h; a.y = io->y;
     a.bf16_state = (s.flags & M3_FLAG_BF16_STATE) != 0;
+    a.fused = fused; a.z = io->z; a.W_X = io->W_X; a.W_Z = io->W_Z; a.W_O = io->W_O; a.o = io->o;
     hipError_t e = launch_decode(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }

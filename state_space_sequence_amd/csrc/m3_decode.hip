@@ -20,6 +20,12 @@
 // are formed once per workgroup in LDS. State rows are streamed with
 // non-temporal accesses (read once, written once). y for a row is reduced over
 // the N/(2V) lanes that share the row.
+//
+// With the fused rank projections (App. C) x and x_prev are X' [P] and the
+// step writes O'[p] = sum_r W_O[p][r] y[r][p] SiLU(W_Z[p][r] Z'[p]) instead of y:
+// X = W_X (.) X' is formed in LDS with x, and the gate factors
+// W_O SiLU(W_Z Z') in a table, so each lane contracts its R partial sums with
+// the gate before the one reduction over the row's lanes.
 #include <type_traits>
 
 #include "m3_internal.h"
@@ -181,6 +187,7 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     float *srs = ssn + HALF;     // [4R]     1/rms per row
     float *sx = srs + 4 * R;     // [P][R]
     float *sxp = sx + R * a.P;   // [P][R]
+    float *sgt = sxp + R * a.P;  // [P][R]   fused: W_O SiLU(W_Z Z')
 
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x;
@@ -212,11 +219,24 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
         sBp[e] = a.has_prev ? ld_io<BF16>(a.Braw_prev, rowBC + e) : 0.f;
     }
     const int64_t rowX = (bi * a.H + hi) * R * P;
-    for (int e = tid; e < R * P; e += kThreads) {
-        // stored rank-minor, [p][r], so one row's ranks are adjacent
-        const int r = e / P, p = e % P;
-        sx[p * R + r] = ld_io<BF16>(a.x, rowX + e);
-        sxp[p * R + r] = a.has_prev ? ld_io<BF16>(a.x_prev, rowX + e) : 0.f;
+    if (!a.fused) {
+        for (int e = tid; e < R * P; e += kThreads) {
+            // stored rank-minor, [p][r], so one row's ranks are adjacent
+            const int r = e / P, p = e % P;
+            sx[p * R + r] = ld_io<BF16>(a.x, rowX + e);
+            sxp[p * R + r] = a.has_prev ? ld_io<BF16>(a.x_prev, rowX + e) : 0.f;
+        }
+    } else {
+        // W is [H][P][R]: e = p R + r is already the table order
+        const int64_t rowP = (bi * a.H + hi) * P;
+        const float *wx = a.W_X + hi * R * P, *wz = a.W_Z + hi * R * P, *wo = a.W_O + hi * R * P;
+        for (int e = tid; e < R * P; e += kThreads) {
+            const int p = e / R;
+            sx[e] = wx[e] * ld_io<BF16>(a.x, rowP + p);
+            sxp[e] = a.has_prev ? wx[e] * ld_io<BF16>(a.x_prev, rowP + p) : 0.f;
+            const float zz = wz[e] * ld_io<BF16>(a.z, rowP + p);
+            sgt[e] = wo[e] * (zz / (1.f + expf(-zz)));
+        }
     }
     for (int e = tid; e < R * N; e += kThreads) {
         sbb[e] = a.B_bias[hi * R * N + e];
@@ -326,7 +346,14 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
             }
             __builtin_nontemporal_store(pack_state<BS, V>(l), reinterpret_cast<svec *>(hbase + (int64_t)p * N + n0));
             __builtin_nontemporal_store(pack_state<BS, V>(h), reinterpret_cast<svec *>(hbase + (int64_t)p * N + HALF + n0));
-            if constexpr (R == 2 || R == 4) {
+            if (a.fused) {
+                // the gate is linear in y: contract the ranks first, then reduce once
+                float v = 0.f;
+#pragma unroll
+                for (int r = 0; r < R; ++r) v += sgt[p * R + r] * yacc[r];
+                v = group_sum<NQ>(v);
+                if (q == 0) st_io<BF16>(a.o, (bi * a.H + hi) * P + p, v);
+            } else if constexpr (R == 2 || R == 4) {
                 // reduce-scatter over the NQ lanes of the row: at the top log2(R)
                 // bits of the lane group a lane keeps half of its partial sums and
                 // adds the partner's matching half; the low bits then sum one value.
@@ -356,7 +383,7 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
 
 template <bool BF16, bool BS, int N>
 hipError_t launch_n(const DecodeArgs &a, hipStream_t s) {
-    const size_t smem = sizeof(float) * (5 * a.R * N + 3 * N + 4 * a.R + 2 * a.R * a.P);
+    const size_t smem = sizeof(float) * (5 * a.R * N + 3 * N + 4 * a.R + (a.fused ? 3 : 2) * a.R * a.P);
     dim3 grid((unsigned)(a.b * a.H)), block(kThreads);
     switch (a.R) {
         case 1: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 1, 4, 2>), grid, block, smem, s, a); break;

@@ -21,6 +21,11 @@ struct ScanArgs {
     const void *x_prev, *Braw_prev;
     void *y;
     float *h_final;
+    // fused projections (fused == W_X given): x / x_prev are X' without the rank axis
+    bool fused;
+    const void *z;
+    const float *W_X, *W_Z, *W_O;
+    void *o;
 };
 
 struct DecodeArgs {
@@ -35,6 +40,11 @@ struct DecodeArgs {
     void *h;          // [b,H,P,N] fp32, or bf16 when bf16_state
     bool bf16_state;  // state stored as bf16 (rounded to nearest even), arithmetic in fp32
     void *y;
+    // fused projections (fused == W_X given): x / x_prev are X' [b,H,P]
+    bool fused;
+    const void *z;
+    const float *W_X, *W_Z, *W_O;
+    void *o;
 };
 
 // Segment-split bookkeeping for the matrix-core prefill (state passing).

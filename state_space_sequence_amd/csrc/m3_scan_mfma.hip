@@ -35,6 +35,8 @@
 // per CU): B_bar [row][n], B_bar*scale transposed [n][row], X transposed
 // [p][row], the bf16 copy of the state transposed [p][n] for the Y_off product,
 // and small per-row scalar tables.
+#include <type_traits>
+
 #include "m3_internal.h"
 
 namespace m3i {
@@ -122,6 +124,11 @@ struct alignas(16) Smem {
     alignas(16) float normw[2][kN];       // BCNorm gains (ones when absent)
 };
 
+// with the fused rank projections: W_X, W_Z, W_O of this head, [rank][p]
+struct SmemFused : Smem {
+    alignas(16) float fw[3][4][kP];
+};
+
 struct ChainPos {
     int64_t chain, seg, c_begin, c_end;
 };
@@ -180,23 +187,27 @@ __device__ __forceinline__ Lane make_lane(int l, int w, int64_t H) {
     return ln;
 }
 
-// Uniform (per workgroup and chunk) bases of a chunk's blocks.
+// Uniform (per workgroup and chunk) bases of a chunk's blocks. With the fused
+// projections x is X' and z is Z' (one row of P per token, no rank axis) and the
+// output goes to o, also one row per token.
 struct ChunkBase {
-    const __bf16 *B, *Cr, *x;
+    const __bf16 *B, *Cr, *x, *z;
     const float *th;
     const float *dt, *A, *lam;
     __bf16 *y;
 };
 
-template <int R>
+template <int R, bool FUSED>
 __device__ __forceinline__ ChunkBase chunk_base(const ScanArgs &a, int64_t bi, int64_t hi, int64_t g, int64_t c0) {
     ChunkBase cb;
     const int64_t t0 = bi * a.L + c0;  // first token of the chunk
     cb.B = static_cast<const __bf16 *>(a.Braw) + (t0 * a.G + g) * R * kN;
     cb.Cr = static_cast<const __bf16 *>(a.Craw) + (t0 * a.G + g) * R * kN;
     cb.th = a.theta + (t0 * a.G + g) * kHalf;
-    cb.x = static_cast<const __bf16 *>(a.x) + (t0 * a.H + hi) * R * kP;
-    cb.y = static_cast<__bf16 *>(a.y) + (t0 * a.H + hi) * R * kP;
+    constexpr int XR = FUSED ? 1 : R;  // x rows per token
+    cb.x = static_cast<const __bf16 *>(a.x) + (t0 * a.H + hi) * XR * kP;
+    cb.y = static_cast<__bf16 *>(FUSED ? a.o : a.y) + (t0 * a.H + hi) * XR * kP;
+    cb.z = FUSED ? static_cast<const __bf16 *>(a.z) + (t0 * a.H + hi) * kP : nullptr;
     cb.dt = a.dt + t0 * a.H + hi;
     cb.A = a.A + t0 * a.H + hi;
     cb.lam = a.lam + t0 * a.H + hi;
@@ -208,6 +219,7 @@ __device__ __forceinline__ ChunkBase chunk_base(const ScanArgs &a, int64_t bi, i
 // so the loads are in flight while the previous chunk is computed.
 struct ChunkRegs {
     bf16x8 rb[4], rc[4], xf[2];
+    bf16x4 zf[4];  // fused projections: Z' of the row's token at the lane's output columns
     f32x4 th[4];
     float d, av, lm;  // dt, A, lambda of the token of row l (lane l holds row l)
     float dn, lmn;    // dt and lambda of the token after it (0 past the end)
@@ -216,7 +228,7 @@ struct ChunkRegs {
 
 // nv: tokens of the chunk; avail: tokens from the chunk's first one to the end
 // of the sequence (capped at C + 1).
-template <int MODE, int R>
+template <int MODE, int R, bool FUSED>
 __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, int nv, int avail, int64_t G,
                                            int64_t H, ChunkRegs &cr) {
     // token scalars in row layout: lane l holds row l, i.e. token l / R
@@ -256,9 +268,16 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
     cr.th[1] = pt[2 * ln.lg + 1];
     cr.th[2] = pt[8 + 2 * ln.lg];
     cr.th[3] = pt[8 + 2 * ln.lg + 1];
-    const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + (tr * (int)H * R + ln.r_row) * kP);
+    const int offx = FUSED ? tr * (int)H * kP : (tr * (int)H * R + ln.r_row) * kP;
+    const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + offx);
     cr.xf[0] = px[ln.lg];
     cr.xf[1] = px[4 + ln.lg];
+    if constexpr (FUSED && MODE != kPass1) {
+        // columns p = 16pb + 4lg..+3 of the output rows this lane holds
+        const bf16x4 *pz = reinterpret_cast<const bf16x4 *>(cb.z + offx + 4 * ln.lg);
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) cr.zf[pb] = pz[4 * pb];
+    }
 }
 
 // bf16x8 fragment with a single 1.0 at slot j (none when j is outside 0..7)
@@ -270,10 +289,22 @@ __device__ __forceinline__ bf16x8 unit_fragment(int j) {
     return __builtin_bit_cast(bf16x8, u);
 }
 
-template <int MODE, int R, bool HAS_W>
+// X' (fused projections) or x of the previous token, element (r, p)
+template <int R, bool FUSED>
+__device__ __forceinline__ float prev_x(const ScanArgs &a, int64_t bi, int64_t hi, int r, int p) {
+    if constexpr (FUSED) {
+        const __bf16 *xp = static_cast<const __bf16 *>(a.x_prev) + (bi * a.H + hi) * kP;
+        return a.W_X[(hi * kP + p) * R + r] * (float)xp[p];
+    } else {
+        const __bf16 *xp = static_cast<const __bf16 *>(a.x_prev) + ((bi * a.H + hi) * R) * kP;
+        return (float)xp[r * kP + p];
+    }
+}
+
+template <int MODE, int R, bool HAS_W, bool FUSED>
 __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, SplitPlan sp) {
     constexpr int C = kRows / R;  // tokens per chunk
-    __shared__ Smem sm;
+    __shared__ typename std::conditional<FUSED, SmemFused, Smem>::type sm;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -294,6 +325,14 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         sm.normw[e / kN][e % kN] = src ? src[e % kN] : 1.f;
     }
     if (tid < kHalf) sm.carry[tid] = 0.f;
+    if constexpr (FUSED) {
+        // global W is [H][P][R]: e runs over (p, r) of this head, rank fastest
+        for (int e = tid; e < 3 * R * kP; e += kThreads) {
+            const int which = e / (R * kP), rem = e % (R * kP);
+            const float *W = (which == 0) ? a.W_X : ((which == 1) ? a.W_Z : a.W_O);
+            sm.fw[which][rem % R][rem / R] = W[hi * (R * kP) + rem];
+        }
+    }
 
     // state fragments: acc[q][pb] holds state[n = 16(w+4q) + 4lg + j][p = 16pb + lr]
     f32x4 acc[2][4];
@@ -322,7 +361,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         if (a.has_prev && L > 0) {
             // fold (1 - lam_0) dt_0 B_{-1} x_{-1}^T into the starting state
             const __bf16 *bp = static_cast<const __bf16 *>(a.Braw_prev) + ((bi * G + g) * R) * kN;
-            const __bf16 *xp = static_cast<const __bf16 *>(a.x_prev) + ((bi * H + hi) * R) * kP;
             float rsr[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -343,7 +381,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                         float s = 0.f;
 #pragma unroll
                         for (int r = 0; r < R; ++r)
-                            s += ((float)bp[r * kN + n] * rsr[r] * wn + bb[r * kN + n]) * (float)xp[r * kP + p];
+                            s += ((float)bp[r * kN + n] * rsr[r] * wn + bb[r * kN + n]) *
+                                 prev_x<R, FUSED>(a, bi, hi, r, p);
                         acc[q][pb][j] += f * s;
                     }
         }
@@ -373,13 +412,14 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         const int64_t c0 = pos.c_begin * C;
         const int nv = (int)((L - c0) < C ? (L - c0) : C);
         const int avail = (int)((L - c0) < C + 1 ? (L - c0) : C + 1);
-        load_chunk<MODE, R>(chunk_base<R>(a, bi, hi, g, c0), make_lane<R>(tid & 63, w, H), nv, avail, G, H, cr);
+        load_chunk<MODE, R, FUSED>(chunk_base<R, FUSED>(a, bi, hi, g, c0), make_lane<R>(tid & 63, w, H), nv, avail,
+                                   G, H, cr);
     }
 
     for (int64_t c = pos.c_begin; c < pos.c_end; ++c) {
         const int64_t c0 = c * C;
         const int nv = (int)((L - c0) < C ? (L - c0) : C);
-        const ChunkBase cb = chunk_base<R>(a, bi, hi, g, c0);
+        const ChunkBase cb = chunk_base<R, FUSED>(a, bi, hi, g, c0);
         // lane-derived indices, recomputed per chunk (see opaque())
         const Lane ln = make_lane<R>(opaque(tid & 63), w, H);
         const int l = ln.l, lr = ln.lr, lg = ln.lg, row = ln.row, r_row = ln.r_row, t_row = ln.t_row;
@@ -397,6 +437,23 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         }
         xf[0] = cr.xf[0];
         xf[1] = cr.xf[1];
+        bf16x4 zf[4];
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) zf[pb] = cr.zf[pb];
+            // rank expansion X = W_X (.) X' for this lane's rank (App. C), rounded
+            // to bf16 like any other matrix-core operand
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&sm.fw[0][r_row][32 * hh + 8 * lg]);
+                const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&sm.fw[0][r_row][32 * hh + 8 * lg + 4]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xf[hh][j] = (__bf16)((float)xf[hh][j] * w0[j]);
+                    xf[hh][j + 4] = (__bf16)((float)xf[hh][j + 4] * w1[j]);
+                }
+            }
+        }
         // ---- X^T through the matrix core: T = X-fragment x selection, exact for
         // bf16 operands; the output lane holds rows 16w + 4lg..+3 of column lr
 #pragma unroll
@@ -577,7 +634,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             const int64_t c1 = c0 + C;
             const int nv1 = (int)((L - c1) < C ? (L - c1) : C);
             const int avail1 = (int)((L - c1) < C + 1 ? (L - c1) : C + 1);
-            load_chunk<MODE, R>(chunk_base<R>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
+            load_chunk<MODE, R, FUSED>(chunk_base<R, FUSED>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
         }
 
         if constexpr (MODE != kPass1) {
@@ -655,7 +712,23 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                         yv = mfma(xv, pfr[m2], yv);
                     }
                 }
-                if (valid) {
+                if constexpr (FUSED) {
+                    // gate and rank contraction (App. C): sum over the R lanes of the
+                    // token of W_O Y SiLU(W_Z Z'); the token's rank-0 lane stores it
+                    const f32x4 wz = *reinterpret_cast<const f32x4 *>(&sm.fw[1][r_row][16 * pb + 4 * lg]);
+                    const f32x4 wo = *reinterpret_cast<const f32x4 *>(&sm.fw[2][r_row][16 * pb + 4 * lg]);
+                    f32x4 ov;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float zz = wz[j] * (float)zf[pb][j];
+                        const float silu = zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz));
+                        ov[j] = group_sum<R>(wo[j] * yv[j] * silu);
+                    }
+                    if (valid && r_row == 0) {
+                        const bf16x4 o = {(__bf16)ov[0], (__bf16)ov[1], (__bf16)ov[2], (__bf16)ov[3]};
+                        *reinterpret_cast<bf16x4 *>(cb.y + t_row * (int)H * kP + 16 * pb + 4 * lg) = o;
+                    }
+                } else if (valid) {
                     const bf16x4 o = {(__bf16)yv[0], (__bf16)yv[1], (__bf16)yv[2], (__bf16)yv[3]};
                     *reinterpret_cast<bf16x4 *>(cb.y + ln.offX + 16 * pb + 4 * lg) = o;
                 }
@@ -737,7 +810,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 
 // Chain the segment end states: H_in[0] = h0 (+ fold of the previous token);
 // H_in[k+1] = exp(D_k) R(Phi_k) H_in[k] + E_k. Overwrites E_k with H_in[k].
-template <int R>
+template <int R, bool FUSED>
 __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan sp) {
     __shared__ float rsp[4];
     const int tid = threadIdx.x;
@@ -753,7 +826,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
     }
     if (a.has_prev && a.L > 0) {
         const __bf16 *bp = static_cast<const __bf16 *>(a.Braw_prev) + ((bi * a.G + g) * R) * kN;
-        const __bf16 *xp = static_cast<const __bf16 *>(a.x_prev) + ((bi * a.H + hi) * R) * kP;
         const int wv = tid >> 6, l = tid & 63;
         if (wv < R) {
             const float v0 = (float)bp[wv * kN + 2 * l], v1 = (float)bp[wv * kN + 2 * l + 1];
@@ -770,7 +842,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
             const int p = (tid + kThreads * k) / kHalf;
             float sl = 0.f, sh = 0.f;
             for (int r = 0; r < R; ++r) {
-                const float xv = (float)xp[r * kP + p];
+                const float xv = prev_x<R, FUSED>(a, bi, hi, r, p);
                 sl += ((float)bp[r * kN + i] * rsp[r] * wl + bb[r * kN + i]) * xv;
                 sh += ((float)bp[r * kN + i + kHalf] * rsp[r] * wh + bb[r * kN + i + kHalf]) * xv;
             }
@@ -796,28 +868,34 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
     }
 }
 
-template <int R, bool HAS_W>
+template <int R, bool HAS_W, bool FUSED>
 hipError_t launch_rw(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
     const int64_t chains = a.b * a.H;
     if (sp.nseg <= 1) {
-        hipLaunchKernelGGL((scan_mfma_kernel<kFull, R, HAS_W>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp);
+        hipLaunchKernelGGL((scan_mfma_kernel<kFull, R, HAS_W, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a,
+                           sp);
         return hipGetLastError();
     }
     const unsigned nblk = (unsigned)(chains * sp.nseg);
-    hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R, HAS_W>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
+    hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R, HAS_W, FUSED>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((combine_kernel<R>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp);
+    hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R, HAS_W>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
+    hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R, HAS_W, FUSED>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
     return hipGetLastError();
+}
+
+template <int R, bool FUSED>
+hipError_t launch_rf(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
+    if (a.B_normw || a.C_normw) return launch_rw<R, true, FUSED>(a, sp, s);
+    return launch_rw<R, false, FUSED>(a, sp, s);
 }
 
 template <int R>
 hipError_t launch_r(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
-    if (a.B_normw || a.C_normw) return launch_rw<R, true>(a, sp, s);
-    return launch_rw<R, false>(a, sp, s);
+    return a.fused ? launch_rf<R, true>(a, sp, s) : launch_rf<R, false>(a, sp, s);
 }
 
 }  // namespace

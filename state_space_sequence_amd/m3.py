@@ -33,13 +33,13 @@ class Shape(ctypes.Structure):
 class ScanIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "Braw", "Craw", "dt", "A", "lam", "theta", "B_bias", "C_bias", "B_normw", "C_normw",
-        "h0", "x_prev", "Braw_prev", "y", "h_final")]
+        "h0", "x_prev", "Braw_prev", "y", "h_final", "z", "W_X", "W_Z", "W_O", "o")]
 
 
 class DecodeIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "Braw", "Craw", "dt", "A", "lam", "theta", "B_bias", "C_bias", "B_normw", "C_normw",
-        "x_prev", "Braw_prev", "h", "y")]
+        "x_prev", "Braw_prev", "h", "y", "z", "W_X", "W_Z", "W_O", "o")]
 
 
 class Plan(ctypes.Structure):
@@ -151,6 +151,33 @@ def scan_fwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *, chunk=64, eps=
     return y, h_final
 
 
+def scan_fused_fwd(x_in, z_in, W_X, W_Z, W_O, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *,
+                   chunk=64, eps=1e-5, B_normw=None, C_normw=None, h0=None, x_prev_in=None,
+                   Braw_prev=None, o=None, h_final=None, want_state=True, workspace=None,
+                   nsegments=0, stream=None):
+    """Prefill with the fused MIMO projections and gate (m3_scan_fwd with W_X set).
+    x_in, z_in [b,L,H,P] (X', Z'), W_X/W_Z/W_O [H,P,R], x_prev_in [b,H,P] or None.
+    Returns (o [b,L,H,P], h_final)."""
+    b, L, H, P = x_in.shape
+    R = W_X.shape[2]
+    G, N = Braw.shape[2], Braw.shape[4]
+    shape = make_shape(b, L, H, G, P, N, R, chunk, _io_dtype(x_in), eps, 0, nsegments)
+    if o is None:
+        o = torch.empty_like(x_in)
+    if h_final is None and want_state:
+        h_final = torch.empty((b, H, P, N), dtype=torch.float32, device=x_in.device)
+    ws = workspace_bytes(shape)
+    if ws and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=x_in.device)
+    io = ScanIO(_ptr(x_in), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
+                _ptr(B_bias), _ptr(C_bias), _ptr(B_normw), _ptr(C_normw), _ptr(h0),
+                _ptr(x_prev_in), _ptr(Braw_prev), None, _ptr(h_final),
+                _ptr(z_in), _ptr(W_X), _ptr(W_Z), _ptr(W_O), _ptr(o))
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.m3_scan_fwd(ctypes.byref(shape), ctypes.byref(io), _ptr(workspace), wsb, _stream(stream)))
+    return o, h_final
+
+
 def decode_step(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, h, *, eps=1e-5,
                 B_normw=None, C_normw=None, x_prev=None, Braw_prev=None, y=None, stream=None):
     """One decode step (m3_decode_step). x [b,H,R,P], Braw/Craw [b,G,R,N], dt/A/lam [b,H],
@@ -169,11 +196,30 @@ def decode_step(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, h, *, eps=1e-5
     return y
 
 
+def decode_fused_step(x_in, z_in, W_X, W_Z, W_O, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, h, *,
+                      eps=1e-5, B_normw=None, C_normw=None, x_prev_in=None, Braw_prev=None, o=None,
+                      stream=None):
+    """One decode step with the fused projections. x_in, z_in [b,H,P], W_* [H,P,R],
+    h [b,H,P,N] (fp32 or bf16) updated in place. Returns o [b,H,P]."""
+    b, H, P = x_in.shape
+    R = W_X.shape[2]
+    G, N = Braw.shape[1], Braw.shape[3]
+    flags = M3_FLAG_BF16_STATE if h.dtype == torch.bfloat16 else 0
+    shape = make_shape(b, 1, H, G, P, N, R, 1, _io_dtype(x_in), eps, flags)
+    if o is None:
+        o = torch.empty_like(x_in)
+    io = DecodeIO(_ptr(x_in), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
+                  _ptr(B_bias), _ptr(C_bias), _ptr(B_normw), _ptr(C_normw), _ptr(x_prev_in),
+                  _ptr(Braw_prev), _ptr(h), None, _ptr(z_in), _ptr(W_X), _ptr(W_Z), _ptr(W_O), _ptr(o))
+    _check(lib.m3_decode_step(ctypes.byref(shape), ctypes.byref(io), _stream(stream)))
+    return o
+
+
 # ---------------------------------------------------------------- helpers ---
 def to_device(inp: dict, io: str, device="cuda"):
     """Move a numpy input dict (from state_space_sequence_amd.inputs) to the GPU:
     io tensors in bf16 or fp32 (bf16 values are exact), the rest fp32."""
-    io_keys = ("x", "Braw", "Craw", "x_prev", "Braw_prev")
+    io_keys = ("x", "Braw", "Craw", "x_prev", "Braw_prev", "x_in", "z_in", "x_prev_in")
     out = {}
     for k, v in inp.items():
         if v is None:

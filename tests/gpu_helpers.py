@@ -43,3 +43,31 @@ def gpu_decode(inp, shape, bf16_state=False):
                        C_normw=d.get("C_normw"), x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"))
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64), h.float().cpu().numpy().astype(np.float64)
+
+
+def gpu_scan_fused(inp, shape, **kw):
+    """Prefill with the fused projections (inputs from make_fused_scan_inputs)."""
+    from state_space_sequence_amd import m3
+    d = m3.to_device(inp, shape.io)
+    o, h = m3.scan_fused_fwd(d["x_in"], d["z_in"], d["W_X"], d["W_Z"], d["W_O"], d["Braw"], d["Craw"],
+                             d["dt"], d["A"], d["lam"], d["theta"], d["B_bias"], d["C_bias"],
+                             chunk=shape.chunk, eps=shape.eps, B_normw=d.get("B_normw"),
+                             C_normw=d.get("C_normw"), h0=d.get("h0"), x_prev_in=d.get("x_prev_in"),
+                             Braw_prev=d.get("Braw_prev"), **kw)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), h.cpu().numpy().astype(np.float64)
+
+
+def gpu_decode_fused(inp, shape, bf16_state=False):
+    """One fused decode step (inputs from make_fused_decode_inputs)."""
+    from state_space_sequence_amd import m3
+    d = m3.to_device(inp, shape.io)
+    h = d["h"].clone()
+    if bf16_state:
+        h = h.to(torch.bfloat16)
+    o = m3.decode_fused_step(d["x_in"], d["z_in"], d["W_X"], d["W_Z"], d["W_O"], d["Braw"], d["Craw"],
+                             d["dt"], d["A"], d["lam"], d["theta"], d["B_bias"], d["C_bias"], h,
+                             eps=shape.eps, B_normw=d.get("B_normw"), C_normw=d.get("C_normw"),
+                             x_prev_in=d.get("x_prev_in"), Braw_prev=d.get("Braw_prev"))
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), h.float().cpu().numpy().astype(np.float64)

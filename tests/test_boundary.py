@@ -58,10 +58,15 @@ def _scan(m3, shape, io=None, ws=None, wsb=0):
     return m3.lib.m3_scan_fwd(ctypes.byref(shape), ctypes.byref(io), ws, wsb, None)
 
 
-def _fake_io(m3, base=0x100000, misalign=None, drop=None):
+FUSED_FIELDS = ("z", "W_X", "W_Z", "W_O", "o")
+
+
+def _fake_io(m3, base=0x100000, misalign=None, drop=None, fused=False):
     io = m3.ScanIO()
     for i, (name, _) in enumerate(m3.ScanIO._fields_):
         if name in ("B_normw", "C_normw", "h0", "x_prev", "Braw_prev", "h_final"):
+            continue
+        if (name in FUSED_FIELDS) != fused and name in FUSED_FIELDS + ("y",):
             continue
         setattr(io, name, base + 0x1000 * (i + 1))
     if misalign:
@@ -85,6 +90,43 @@ def test_null_io_and_missing_tensor(m3):
     assert m3.lib.m3_scan_fwd(None, None, None, 0, None) == -1
     for name in ("x", "Braw", "Craw", "dt", "A", "lam", "theta", "B_bias", "C_bias", "y"):
         assert _scan(m3, s, _fake_io(m3, drop=name)) == -1, name
+
+
+def test_fused_fields_validated(m3):
+    s = _shape(m3, rank=4)
+    # each fused pointer but y is required once W_X is set
+    for name in FUSED_FIELDS:
+        assert _scan(m3, s, _fake_io(m3, fused=True, drop=name)) == -1, name
+    # a fused pointer without W_X is an error, not silently ignored
+    for name in ("z", "W_Z", "W_O", "o"):
+        io = _fake_io(m3)
+        setattr(io, name, 0x900000)
+        assert _scan(m3, s, io) == -1, name
+    for name in ("z", "W_X", "o"):
+        assert _scan(m3, s, _fake_io(m3, fused=True, misalign=name)) == -3, name
+    # the fp32 kernel does not take the fused form
+    assert _scan(m3, _shape(m3, rank=4, io_dtype=m3.M3_F32, dstate=64, headdim=32),
+                 _fake_io(m3, fused=True)) == -2
+
+
+def test_decode_fused_fields_validated(m3):
+    s = _shape(m3, rank=4, seqlen=1, chunk=1)
+    def dio(fused, drop=None):
+        io = m3.DecodeIO()
+        for i, (name, _) in enumerate(m3.DecodeIO._fields_):
+            if name in ("B_normw", "C_normw", "x_prev", "Braw_prev"):
+                continue
+            if (name in FUSED_FIELDS) != fused and name in FUSED_FIELDS + ("y",):
+                continue
+            setattr(io, name, 0x100000 + 0x1000 * (i + 1))
+        if drop:
+            setattr(io, drop, None)
+        return io
+    for name in FUSED_FIELDS + ("h",):
+        assert m3.lib.m3_decode_step(ctypes.byref(s), ctypes.byref(dio(True, name)), None) == -1, name
+    io = dio(False)
+    io.z = 0x900000
+    assert m3.lib.m3_decode_step(ctypes.byref(s), ctypes.byref(io), None) == -1
 
 
 def test_prev_token_both_or_neither(m3):
