@@ -71,6 +71,20 @@ def decode_bytes(s, state_bytes=4) -> int:
             + 3 * b * H * 4 + b * G * (N // 2) * 4 + 2 * H * R * N * 4)
 
 
+def fused_prefill_bytes(s) -> int:
+    """The fused-projection prefill moves X', Z' and O' (one P-row per token)
+    instead of x and y (R rows each), plus the three [H,P,R] weights."""
+    io = 2 if s.io == "bf16" else 4
+    b, L, H, P, R = s.batch, s.seqlen, s.nheads, s.headdim, s.rank
+    return prefill_bytes(s) - 2 * b * L * H * R * P * io + 3 * b * L * H * P * io + 3 * H * P * R * 4
+
+
+def fused_decode_bytes(s, state_bytes=4) -> int:
+    io = 2 if s.io == "bf16" else 4
+    b, H, P, R = s.batch, s.nheads, s.headdim, s.rank
+    return decode_bytes(s, state_bytes) - 3 * b * H * R * P * io + 4 * b * H * P * io + 3 * H * P * R * 4
+
+
 # ----------------------------------------------------------------- helpers --
 def scan_args(d, s):
     return (d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"], d["B_bias"], d["C_bias"])
@@ -196,7 +210,8 @@ def main():
 
     import torch
     from state_space_sequence_amd import m3
-    from state_space_sequence_amd.inputs import WORKLOADS, make_decode_inputs, make_scan_inputs
+    from state_space_sequence_amd.inputs import (WORKLOADS, make_decode_inputs, make_fused_decode_inputs,
+                                                 make_fused_scan_inputs, make_scan_inputs)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -350,6 +365,63 @@ def main():
                    "p90_us": round(1e3 * tms[(9 * reps) // 10], 2),
                    "hbm_frac": round(bb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bb}
             key = nm + ("_bf16state" if bf16_state else "")
+            log(key, ent)
+            extra[key] = ent
+            del de, states
+            torch.cuda.empty_cache()
+
+        # ---- the fused rank projections and gate (MIMO rank 4): prefill and decode
+        nm = "mimo4_prefill_1p5b"
+        sf = WORKLOADS[nm]
+        inp = make_fused_scan_inputs(sf, seed=8)
+        df = m3.to_device(inp, sf.io)
+        del inp
+        of = torch.empty_like(df["x_in"])
+        hf2 = torch.empty((sf.batch, sf.nheads, sf.headdim, sf.dstate), dtype=torch.float32, device=dev)
+        fargs = (df["x_in"], df["z_in"], df["W_X"], df["W_Z"], df["W_O"], df["Braw"], df["Craw"], df["dt"],
+                 df["A"], df["lam"], df["theta"], df["B_bias"], df["C_bias"])
+        for _ in range(3):
+            m3.scan_fused_fwd(*fargs, chunk=sf.chunk, eps=sf.eps, o=of, h_final=hf2)
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+        evs[0].record()
+        for k in range(10):
+            m3.scan_fused_fwd(*fargs, chunk=sf.chunk, eps=sf.eps, o=of, h_final=hf2)
+            evs[k + 1].record()
+        torch.cuda.synchronize()
+        ms = sum(evs[k].elapsed_time(evs[k + 1]) for k in range(10)) / 10
+        bb = fused_prefill_bytes(sf)
+        ent = {"tokens_per_s": round(sf.batch * sf.seqlen / (ms * 1e-3), 1), "ms": round(ms, 4),
+               "hbm_frac": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bb}
+        log(nm + "_fused", ent)
+        extra[nm + "_fused"] = ent
+        del df, of, hf2
+        torch.cuda.empty_cache()
+        for nm, bf16_state in (("decode_mimo4_n128", False), ("decode_mimo4_n128", True)):
+            sd = WORKLOADS[nm]
+            de = m3.to_device(make_fused_decode_inputs(sd, seed=9), sd.io)
+            h0 = de["h"].to(torch.bfloat16) if bf16_state else de["h"]
+            states = [h0.clone() for _ in range(4)]
+            od = torch.empty_like(de["x_in"])
+            base = (de["x_in"], de["z_in"], de["W_X"], de["W_Z"], de["W_O"], de["Braw"], de["Craw"], de["dt"],
+                    de["A"], de["lam"], de["theta"], de["B_bias"], de["C_bias"])
+            for k in range(8):
+                m3.decode_fused_step(*base, states[k % 4], x_prev_in=de["x_prev_in"], Braw_prev=de["Braw_prev"], o=od)
+            torch.cuda.synchronize()
+            reps = 40
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            evs[0].record()
+            for k in range(reps):
+                m3.decode_fused_step(*base, states[k % 4], x_prev_in=de["x_prev_in"], Braw_prev=de["Braw_prev"], o=od)
+                evs[k + 1].record()
+            torch.cuda.synchronize()
+            tms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(reps))
+            med = tms[reps // 2]
+            bb = fused_decode_bytes(sd, 2 if bf16_state else 4)
+            ent = {"us_per_step": round(1e3 * med, 2), "p10_us": round(1e3 * tms[reps // 10], 2),
+                   "p90_us": round(1e3 * tms[(9 * reps) // 10], 2),
+                   "hbm_frac": round(bb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bb}
+            key = nm + "_fused" + ("_bf16state" if bf16_state else "")
             log(key, ent)
             extra[key] = ent
             del de, states
