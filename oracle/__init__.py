@@ -139,3 +139,86 @@ def decode_fused(inp: dict, shape, *, nthreads: int = 0):
     d["x_prev"] = None if xp is None else expand_ranks(xp, inp["W_X"]).astype(np.float32)
     y, h = decode(d, shape, nthreads=nthreads)
     return gate_contract(y, inp["z_in"], inp["W_Z"], inp["W_O"]), h
+
+
+# ---------------------------------------------------------------------------
+# Skip term and output norm. The skip is the D term of the SSM output equation
+# (szyisi.cn article on Mamba-3, section introducing state space models:
+# y = C h + D x), one weight per head, added to every rank row of y. The
+# optional output RMSNorm is the Mamba-2 norm that BCNorm makes optional
+# (Mamba-3 paper §3.4 "BC / QK normalization"), studied in §4.1.2 / Table 4 and
+# App. E Table 9 as grouped or default, before or after the gate. Built here:
+# the grouped form with one group per head (RMS over that head's P channels of
+# one token and rank row), with a per-channel gain [H, P], ε the BCNorm ε.
+
+def d_skip(y, x, D):
+    """y + D[h] x for y, x of shape [..., H, R, P] and D of shape [H]."""
+    y = np.asarray(y, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    return y + np.asarray(D, dtype=np.float64)[:, None, None] * x
+
+
+def out_rmsnorm(v, w, eps, *, rank_axis: bool):
+    """Grouped output RMSNorm: v / sqrt(mean over the last axis (P) of v^2 + eps), times
+    the gain w [H, P] (ones when None). v is [..., H, R, P] (rank_axis) or [..., H, P]."""
+    v = np.asarray(v, dtype=np.float64)
+    out = v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + float(eps))
+    if w is not None:
+        w = np.asarray(w, dtype=np.float64)
+        out = out * (w[:, None, :] if rank_axis else w)
+    return out
+
+
+def scan_out(inp: dict, shape, *, out_norm: bool = False, nthreads: int = 0):
+    """Prefill with the skip term (inp["D"], [H], optional) and, if out_norm, the grouped
+    output RMSNorm (gain inp["out_normw"], optional) on y. Returns (y, h_final)."""
+    y, h = scan(inp, shape, nthreads=nthreads)
+    if inp.get("D") is not None:
+        y = d_skip(y, inp["x"], inp["D"])
+    if out_norm:
+        y = out_rmsnorm(y, inp.get("out_normw"), shape.eps, rank_axis=True)
+    return y, h
+
+
+def decode_out(inp: dict, shape, *, out_norm: bool = False, nthreads: int = 0):
+    """decode with the skip term and the optional output norm (see scan_out)."""
+    y, h = decode(inp, shape, nthreads=nthreads)
+    if inp.get("D") is not None:
+        y = d_skip(y, inp["x"], inp["D"])
+    if out_norm:
+        y = out_rmsnorm(y, inp.get("out_normw"), shape.eps, rank_axis=True)
+    return y, h
+
+
+def _gated_out(y, x, inp, eps, out_norm):
+    """Y (+ D X), normed before the gate ("pre") or O' normed after the gate and the
+    rank contraction ("post"), or neither (None)."""
+    if inp.get("D") is not None:
+        y = d_skip(y, x, inp["D"])
+    if out_norm == "pre":
+        y = out_rmsnorm(y, inp.get("out_normw"), eps, rank_axis=True)
+    o = gate_contract(y, inp["z_in"], inp["W_Z"], inp["W_O"])
+    if out_norm == "post":
+        o = out_rmsnorm(o, inp.get("out_normw"), eps, rank_axis=False)
+    return o
+
+
+def scan_fused_out(inp: dict, shape, *, out_norm=None, nthreads: int = 0):
+    """scan_fused with the skip term on Y (D times the expanded X) and the output norm
+    before ("pre") or after ("post") the gate. Returns (O', h_final)."""
+    d = dict(inp)
+    d["x"] = expand_ranks(inp["x_in"], inp["W_X"]).astype(np.float32)
+    xp = inp.get("x_prev_in")
+    d["x_prev"] = None if xp is None else expand_ranks(xp, inp["W_X"]).astype(np.float32)
+    y, h = scan(d, shape, nthreads=nthreads)
+    return _gated_out(y, d["x"], inp, shape.eps, out_norm), h
+
+
+def decode_fused_out(inp: dict, shape, *, out_norm=None, nthreads: int = 0):
+    """decode_fused with the skip term and the output norm (see scan_fused_out)."""
+    d = dict(inp)
+    d["x"] = expand_ranks(inp["x_in"], inp["W_X"]).astype(np.float32)
+    xp = inp.get("x_prev_in")
+    d["x_prev"] = None if xp is None else expand_ranks(xp, inp["W_X"]).astype(np.float32)
+    y, h = decode(d, shape, nthreads=nthreads)
+    return _gated_out(y, d["x"], inp, shape.eps, out_norm), h

@@ -40,6 +40,7 @@ __all__ = [
     "make_decode_inputs",
     "make_fused_scan_inputs",
     "make_fused_decode_inputs",
+    "epilogue_extras",
     "slice_chain",
 ]
 
@@ -219,6 +220,17 @@ def make_fused_decode_inputs(shape: Shape, seed: int, *, first_token: bool = Fal
     return d
 
 
+def epilogue_extras(shape: Shape, seed: int, *, with_D: bool = True, with_normw: bool = True) -> dict:
+    """Draws for the skip term and the output norm: D ~ 1 + 0.5 N(0,1) per head [H] and
+    the output-norm gain out_normw ~ 1 + 0.1 N(0,1) per (head, channel) [H, P], fp32, from
+    a generator of their own (seed + 104729) so every other draw is unchanged."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    H, P = shape.nheads, shape.headdim
+    D = (1.0 + 0.5 * rng.standard_normal(size=(H,))).astype(np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(size=(H, P))).astype(np.float32)
+    return {"D": D if with_D else None, "out_normw": w if with_normw else None}
+
+
 def slice_chain(inp: dict, shape: Shape, b: int, h: int) -> tuple[dict, Shape]:
     """Cut the prefill inputs of one (batch, head) chain out of a full input set,
     as a batch-1, one-head, one-group problem. Chains are independent, so this is
@@ -233,7 +245,7 @@ def slice_chain(inp: dict, shape: Shape, b: int, h: int) -> tuple[dict, Shape]:
             out[k] = np.ascontiguousarray(v[b:b + 1, :, h:h + 1])
         elif k in ("Braw", "Craw", "theta"):
             out[k] = np.ascontiguousarray(v[b:b + 1, :, g:g + 1])
-        elif k in ("B_bias", "C_bias", "W_X", "W_Z", "W_O"):
+        elif k in ("B_bias", "C_bias", "W_X", "W_Z", "W_O", "D", "out_normw"):
             out[k] = np.ascontiguousarray(v[h:h + 1])
         elif k in ("h0", "x_prev", "x_prev_in"):
             out[k] = np.ascontiguousarray(v[b:b + 1, h:h + 1])
