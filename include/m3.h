@@ -73,6 +73,17 @@ typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
                                     nearest even (the Mamba-3 paper times decode with
                                     fp32 and with bf16 state, §4.4 Table 6). m3_scan_fwd
                                     rejects it with M3_ERR_INVALID_ARG. */
+#define M3_FLAG_OUT_NORM 4u      /* grouped output RMSNorm: every output row of P
+                                    channels (one head, one token, one rank row of y)
+                                    becomes v / sqrt(mean(v^2) + eps) * out_normw[h][:],
+                                    eps the BCNorm eps. The optional Mamba-2 norm that
+                                    BCNorm makes optional (Mamba-3 paper §3.4), studied
+                                    grouped and before/after the gate in §4.1.2 Table 4
+                                    and App. E Table 9. With the fused gate the norm is
+                                    applied to each rank row of Y before the gate. */
+#define M3_FLAG_NORM_AFTER_GATE 8u /* with M3_FLAG_OUT_NORM and the fused gate (W_X set):
+                                    norm O' (after the gate and the rank contraction)
+                                    instead of Y. M3_ERR_INVALID_ARG without both. */
 
 typedef struct {
     int64_t batch;     /* b >= 0 */
@@ -123,6 +134,11 @@ typedef struct {
     const float *W_Z;      /* [H,P,R] rank expansion of Z' */
     const float *W_O;      /* [H,P,R] contraction of the gated output over the ranks */
     void *o;               /* out [b,L,H,P] io */
+    /* Output epilogue. D: skip term y += D[h] x on every rank row (with W_X set,
+     * x is the expanded X), the D term of the SSM output equation y = C h + D x
+     * (szyisi.cn article on Mamba-3, state space model section). NULL = none. */
+    const float *D;        /* [H] */
+    const float *out_normw; /* [H,P] gain of the output norm (M3_FLAG_OUT_NORM); NULL = ones */
 } m3_scan_io;
 
 /* Decode (single token) arguments: the per-token tensors have no L axis. */
@@ -149,6 +165,8 @@ typedef struct {
     const float *W_Z;      /* [H,P,R] */
     const float *W_O;      /* [H,P,R] */
     void *o;               /* out [b,H,P] io */
+    const float *D;        /* [H] skip term, as in m3_scan_io, or NULL */
+    const float *out_normw; /* [H,P] output-norm gain, as in m3_scan_io, or NULL */
 } m3_decode_io;
 
 /* What m3_scan_fwd will launch for a shape (for logs and tests). */

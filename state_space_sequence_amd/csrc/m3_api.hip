@@ -43,7 +43,8 @@ m3_status check_shape(const m3_shape *s) {
     if (s->io_dtype != M3_F32 && s->io_dtype != M3_BF16) return M3_ERR_INVALID_ARG;
     if (!(s->eps >= 0.f) || !isfinite(s->eps)) return M3_ERR_INVALID_ARG;
     if (s->nsegments < 0) return M3_ERR_INVALID_ARG;
-    if (s->flags & ~M3_FLAG_FORCE_GENERIC) return M3_ERR_INVALID_ARG;  // (the bf16-state flag is decode only)
+    // (the bf16-state flag is decode only)
+    if (s->flags & ~(M3_FLAG_FORCE_GENERIC | M3_FLAG_OUT_NORM | M3_FLAG_NORM_AFTER_GATE)) return M3_ERR_INVALID_ARG;
     if (s->batch > (1LL << 31) || s->nheads > (1LL << 20) || s->seqlen > (1LL << 40)) return M3_ERR_UNSUPPORTED;
     return M3_OK;
 }
@@ -96,7 +97,16 @@ const char *m3_status_str(m3_status st) {
     return "unknown status";
 }
 
-int m3_version(void) { return 102; }
+int m3_version(void) { return 103; }
+
+// Output epilogue flags against the pointers: the gain needs the norm flag, and
+// the after-gate position needs the norm and the fused gate.
+static bool epilogue_ok(uint32_t flags, bool fused, const float *out_normw) {
+    const bool onorm = (flags & M3_FLAG_OUT_NORM) != 0;
+    if (out_normw && !onorm) return false;
+    if ((flags & M3_FLAG_NORM_AFTER_GATE) && !(onorm && fused)) return false;
+    return true;
+}
 
 m3_status m3_scan_plan(const m3_shape *shape, m3_plan *plan) {
     m3_status st = check_shape(shape);
@@ -130,12 +140,14 @@ m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspa
     const bool fused = io->W_X != nullptr;
     if (fused && (!io->W_Z || !io->W_O)) return M3_ERR_INVALID_ARG;
     if (!fused && (io->W_Z || io->W_O || io->z || io->o)) return M3_ERR_INVALID_ARG;
+    if (!epilogue_ok(s.flags, fused, io->out_normw)) return M3_ERR_INVALID_ARG;
     if (work && (!io->x || !io->Braw || !io->Craw || !io->dt || !io->A || !io->lam || !io->theta ||
                  !io->B_bias || !io->C_bias || (fused ? (!io->z || !io->o) : !io->y)))
         return M3_ERR_INVALID_ARG;
     const void *ptrs[] = {io->x, io->Braw, io->Craw, io->dt, io->A, io->lam, io->theta, io->B_bias,
                           io->C_bias, io->B_normw, io->C_normw, io->h0, io->x_prev, io->Braw_prev,
-                          io->y, io->h_final, workspace, io->z, io->W_X, io->W_Z, io->W_O, io->o};
+                          io->y, io->h_final, workspace, io->z, io->W_X, io->W_Z, io->W_O, io->o,
+                          io->D, io->out_normw};
     for (const void *p : ptrs)
         if (!aligned16(p)) return M3_ERR_MISALIGNED;
     Plan p;
@@ -154,6 +166,9 @@ m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspa
     a.C_normw = io->C_normw; a.h0 = io->h0; a.x_prev = io->x_prev; a.Braw_prev = io->Braw_prev;
     a.y = io->y; a.h_final = io->h_final;
     a.fused = fused; a.z = io->z; a.W_X = io->W_X; a.W_Z = io->W_Z; a.W_O = io->W_O; a.o = io->o;
+    a.D = io->D; a.out_normw = io->out_normw;
+    a.onorm = (s.flags & M3_FLAG_OUT_NORM) != 0;
+    a.norm_after_gate = (s.flags & M3_FLAG_NORM_AFTER_GATE) != 0;
 
     hipError_t e = hipSuccess;
     if (s.batch * s.nheads == 0) return M3_OK;
@@ -184,7 +199,7 @@ m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *st
     if (s.batch < 0 || s.nheads < 1 || s.ngroups < 1 || s.headdim < 1 || s.dstate < 2 || s.rank < 1)
         return M3_ERR_INVALID_ARG;
     if (s.nheads % s.ngroups != 0 || s.dstate % 2 != 0) return M3_ERR_INVALID_ARG;
-    if (s.flags & ~M3_FLAG_BF16_STATE) return M3_ERR_INVALID_ARG;
+    if (s.flags & ~(M3_FLAG_BF16_STATE | M3_FLAG_OUT_NORM | M3_FLAG_NORM_AFTER_GATE)) return M3_ERR_INVALID_ARG;
     if (s.io_dtype != M3_F32 && s.io_dtype != M3_BF16) return M3_ERR_INVALID_ARG;
     if (!(s.eps >= 0.f) || !isfinite(s.eps)) return M3_ERR_INVALID_ARG;
     if ((io->x_prev == nullptr) != (io->Braw_prev == nullptr)) return M3_ERR_INVALID_ARG;
@@ -195,12 +210,13 @@ m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *st
     const bool fused = io->W_X != nullptr;
     if (fused && (!io->W_Z || !io->W_O)) return M3_ERR_INVALID_ARG;
     if (!fused && (io->W_Z || io->W_O || io->z || io->o)) return M3_ERR_INVALID_ARG;
+    if (!epilogue_ok(s.flags, fused, io->out_normw)) return M3_ERR_INVALID_ARG;
     if (s.batch > 0 && (!io->x || !io->Braw || !io->Craw || !io->dt || !io->A || !io->lam || !io->theta ||
                         !io->B_bias || !io->C_bias || !io->h || (fused ? (!io->z || !io->o) : !io->y)))
         return M3_ERR_INVALID_ARG;
     const void *ptrs[] = {io->x, io->Braw, io->Craw, io->dt, io->A, io->lam, io->theta, io->B_bias,
                           io->C_bias, io->B_normw, io->C_normw, io->x_prev, io->Braw_prev, io->h, io->y,
-                          io->z, io->W_X, io->W_Z, io->W_O, io->o};
+                          io->z, io->W_X, io->W_Z, io->W_O, io->o, io->D, io->out_normw};
     for (const void *p : ptrs)
         if (!aligned16(p)) return M3_ERR_MISALIGNED;
     if (s.batch == 0) return M3_OK;
@@ -212,6 +228,9 @@ m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *st
     a.C_normw = io->C_normw; a.x_prev = io->x_prev; a.Braw_prev = io->Braw_prev; a.h = io->h; a.y = io->y;
     a.bf16_state = (s.flags & M3_FLAG_BF16_STATE) != 0;
     a.fused = fused; a.z = io->z; a.W_X = io->W_X; a.W_Z = io->W_Z; a.W_O = io->W_O; a.o = io->o;
+    a.D = io->D; a.out_normw = io->out_normw;
+    a.onorm = (s.flags & M3_FLAG_OUT_NORM) != 0;
+    a.norm_after_gate = (s.flags & M3_FLAG_NORM_AFTER_GATE) != 0;
     hipError_t e = launch_decode(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }

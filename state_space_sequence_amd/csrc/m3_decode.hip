@@ -26,6 +26,11 @@
 // X = W_X (.) X' is formed in LDS with x, and the gate factors
 // W_O SiLU(W_Z Z') in a table, so each lane contracts its R partial sums with
 // the gate before the one reduction over the row's lanes.
+//
+// Output epilogue: the skip D[h] x (the D term of y = C h + D x) is added by the
+// lane that stores a value. With the grouped output RMSNorm the output vectors
+// (each rank row of y, or Y before the gate, or O' after it) are staged in LDS
+// until their mean square over P is known, and written after one more barrier.
 #include <type_traits>
 
 #include "m3_internal.h"
@@ -188,6 +193,8 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     float *sx = srs + 4 * R;     // [P][R]
     float *sxp = sx + R * a.P;   // [P][R]
     float *sgt = sxp + R * a.P;  // [P][R]   fused: W_O SiLU(W_Z Z')
+    float *sy = sgt + (a.fused ? R * a.P : 0);  // [R][P] output norm: rows before the norm
+    float *srn = sy + R * a.P;   // [R]      output norm: 1/rms per row
 
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x;
@@ -266,6 +273,11 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     }
     __syncthreads();
 
+    const float dsk = a.D ? a.D[hi] : 0.f;
+    // with the output norm, what is staged: each rank row of y (or of Y, before the
+    // gate), or the gated and contracted O' (after the gate)
+    const bool stage_ranks = a.onorm && !(a.fused && a.norm_after_gate);
+    const bool stage_o = a.onorm && a.fused && a.norm_after_gate;
     const float alpha = expf(d * Av);
     const float beta = a.has_prev ? (1.0f - lm) * d * alpha : 0.f;
     const float gamma = lm * d;
@@ -346,13 +358,28 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
             }
             __builtin_nontemporal_store(pack_state<BS, V>(l), reinterpret_cast<svec *>(hbase + (int64_t)p * N + n0));
             __builtin_nontemporal_store(pack_state<BS, V>(h), reinterpret_cast<svec *>(hbase + (int64_t)p * N + HALF + n0));
-            if (a.fused) {
-                // the gate is linear in y: contract the ranks first, then reduce once
-                float v = 0.f;
+            if (stage_ranks) {
+                // every rank row of the output, skip included, into LDS for the norm
 #pragma unroll
-                for (int r = 0; r < R; ++r) v += sgt[p * R + r] * yacc[r];
-                v = group_sum<NQ>(v);
-                if (q == 0) st_io<BF16>(a.o, (bi * a.H + hi) * P + p, v);
+                for (int r = 0; r < R; ++r) {
+                    const float v = group_sum<NQ>(yacc[r]);
+                    if (q == 0) sy[r * P + p] = v + dsk * xv[r];
+                }
+            } else if (a.fused) {
+                // the gate is linear in y: contract the ranks first, then reduce once
+                float v = 0.f, vs = 0.f;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    v += sgt[p * R + r] * yacc[r];
+                    vs += sgt[p * R + r] * xv[r];
+                }
+                v = group_sum<NQ>(v) + dsk * vs;
+                if (q == 0) {
+                    if (stage_o)
+                        sy[p] = v;
+                    else
+                        st_io<BF16>(a.o, (bi * a.H + hi) * P + p, v);
+                }
             } else if constexpr (R == 2 || R == 4) {
                 // reduce-scatter over the NQ lanes of the row: at the top log2(R)
                 // bits of the lane group a lane keeps half of its partial sums and
@@ -368,14 +395,45 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
                 scatter_step<LNQ - 1, R / 2>(vals, q);
                 if constexpr (LR == 2) scatter_step<LNQ - 2, 1>(vals, q);
                 const float v = tree_sum_low<LNQ - LR>(vals[0]);
-                if (q % (NQ / R) == 0) st_io<BF16>(a.y, ybase + (q / (NQ / R)) * P + p, v);
+                const int rk = q / (NQ / R);
+                if (q % (NQ / R) == 0) st_io<BF16>(a.y, ybase + rk * P + p, v + dsk * sx[p * R + rk]);
             } else {
 #pragma unroll
                 for (int r = 0; r < R; ++r) yacc[r] = group_sum<NQ>(yacc[r]);
                 if (q == 0) {
 #pragma unroll
-                    for (int r = 0; r < R; ++r) st_io<BF16>(a.y, ybase + r * P + p, yacc[r]);
+                    for (int r = 0; r < R; ++r) st_io<BF16>(a.y, ybase + r * P + p, yacc[r] + dsk * xv[r]);
                 }
+            }
+        }
+    }
+
+    if (a.onorm) {
+        // grouped output RMSNorm over the P channels of each staged vector
+        __syncthreads();
+        const int nvec = stage_o ? 1 : R;
+        for (int k = wave; k < nvec; k += kThreads / 64) {
+            float ss = 0.f;
+            for (int p = lane; p < P; p += 64) ss += sy[k * P + p] * sy[k * P + p];
+            ss = wave_sum(ss);
+            if (lane == 0) srn[k] = 1.0f / sqrtf(ss / (float)P + a.eps);
+        }
+        __syncthreads();
+        const float *wn = a.out_normw ? a.out_normw + hi * P : nullptr;
+        const int64_t rowP = (bi * a.H + hi) * P;
+        if (!a.fused) {
+            for (int e = tid; e < R * P; e += kThreads) {
+                const int p = e % P;
+                st_io<BF16>(a.y, ybase + e, sy[e] * srn[e / P] * (wn ? wn[p] : 1.f));
+            }
+        } else if (stage_o) {
+            for (int p = tid; p < P; p += kThreads) st_io<BF16>(a.o, rowP + p, sy[p] * srn[0] * (wn ? wn[p] : 1.f));
+        } else {
+            // normalised Y, then the gate and the rank contraction
+            for (int p = tid; p < P; p += kThreads) {
+                float v = 0.f;
+                for (int r = 0; r < R; ++r) v += sgt[p * R + r] * sy[r * P + p] * srn[r];
+                st_io<BF16>(a.o, rowP + p, v * (wn ? wn[p] : 1.f));
             }
         }
     }
@@ -383,7 +441,8 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
 
 template <bool BF16, bool BS, int N>
 hipError_t launch_n(const DecodeArgs &a, hipStream_t s) {
-    const size_t smem = sizeof(float) * (5 * a.R * N + 3 * N + 4 * a.R + (a.fused ? 3 : 2) * a.R * a.P);
+    const size_t smem = sizeof(float) * (5 * a.R * N + 3 * N + 4 * a.R + (a.fused ? 3 : 2) * a.R * a.P +
+                                         (a.onorm ? a.R * a.P + a.R : 0));
     dim3 grid((unsigned)(a.b * a.H)), block(kThreads);
     switch (a.R) {
         case 1: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 1, 4, 2>), grid, block, smem, s, a); break;

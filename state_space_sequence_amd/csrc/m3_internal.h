@@ -26,6 +26,9 @@ struct ScanArgs {
     const void *z;
     const float *W_X, *W_Z, *W_O;
     void *o;
+    // output epilogue: skip D[h] x, grouped output RMSNorm (gain [H,P] or NULL)
+    const float *D, *out_normw;
+    bool onorm, norm_after_gate;
 };
 
 struct DecodeArgs {
@@ -45,6 +48,8 @@ struct DecodeArgs {
     const void *z;
     const float *W_X, *W_Z, *W_O;
     void *o;
+    const float *D, *out_normw;
+    bool onorm, norm_after_gate;
 };
 
 // Segment-split bookkeeping for the matrix-core prefill (state passing).

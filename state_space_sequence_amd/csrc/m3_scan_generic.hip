@@ -20,6 +20,9 @@
 //    exp(cs_t) C_bar_t^T S, S <- exp(cs_end) S + sum_s exp(cs_end - cs_s) w_s B_bar_s X_s^T,
 //    with cs the chunk-local cumulative log decay.
 //  * MIMO rows are the flattened (token, rank) pairs; the mask depends on tokens.
+//  * output epilogue: the skip D[h] x_t (the D term of y = C h + D x) and the
+//    grouped output RMSNorm of every (token, rank) row over its P channels; with
+//    the norm the chunk's rows are staged in LDS until their mean square is known.
 #include "m3_internal.h"
 
 namespace m3i {
@@ -54,7 +57,9 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a) {
     float *rsB = carry + HALF;       // [T] 1/rms of B rows
     float *rsC = rsB + T;            // [T]
     float *misc = rsC + T;           // [4]: exp(cs_end)
+    float *Yb = misc + 4;            // [T][P] output rows before the norm (only with the norm)
     float *Phi = Pm;
+    const float dsk = a.D ? a.D[hi] : 0.f;
 
     // ---- initial state (physical frame = rotated frame at position -1)
     for (int e = tid; e < N * P; e += kThreads) {
@@ -204,10 +209,30 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a) {
             for (int n = 0; n < N; ++n) off += Cb[rho * N + n] * S[n * P + p];
             float intra = 0.f;
             for (int sg = 0; sg < T; ++sg) intra += Pm[rho * T + sg] * Xs[sg * P + p];
-            const float yv = expf(lcs[t]) * off + intra;
-            st_io<BF16>(a.y, (((bi * L + c0 + t) * a.H + hi) * R + r) * P + p, yv);
+            const float yv = expf(lcs[t]) * off + intra + dsk * Xs[e];
+            if (a.onorm)
+                Yb[e] = yv;
+            else
+                st_io<BF16>(a.y, (((bi * L + c0 + t) * a.H + hi) * R + r) * P + p, yv);
         }
         __syncthreads();
+        if (a.onorm) {
+            // one thread per row: mean square over P, in a fixed order
+            for (int rho = tid; rho < T; rho += kThreads) {
+                float ss = 0.f;
+                for (int p = 0; p < P; ++p) ss += Yb[rho * P + p] * Yb[rho * P + p];
+                rsB[rho] = 1.0f / sqrtf(ss / (float)P + a.eps);
+            }
+            __syncthreads();
+            for (int e = tid; e < T * P; e += kThreads) {
+                const int rho = e / P, p = e % P;
+                const int t = rho / R, r = rho % R;
+                if (t >= nv) continue;
+                const float wn = a.out_normw ? a.out_normw[hi * P + p] : 1.f;
+                st_io<BF16>(a.y, (((bi * L + c0 + t) * a.H + hi) * R + r) * P + p, Yb[e] * rsB[rho] * wn);
+            }
+            __syncthreads();
+        }
         // ---- state update
         const float dec = misc[0];
         const float lend = lcs[C - 1];
@@ -241,7 +266,8 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a) {
 size_t generic_smem_bytes(const ScanArgs &a) {
     const int64_t T = a.C * a.R;
     const int64_t pmsz = (T * T > a.C * (a.N / 2)) ? T * T : a.C * (a.N / 2);
-    return sizeof(float) * (size_t)(a.N * a.P + 2 * T * a.N + T * a.P + pmsz + 4 * a.C + a.N / 2 + 2 * T + 4);
+    return sizeof(float) * (size_t)(a.N * a.P + 2 * T * a.N + T * a.P + pmsz + 4 * a.C + a.N / 2 + 2 * T + 4 +
+                                    (a.onorm ? T * a.P : 0));
 }
 
 hipError_t launch_scan_generic(const ScanArgs &a, hipStream_t s) {

@@ -122,6 +122,7 @@ struct alignas(16) Smem {
     alignas(16) float carry[kHalf];       // cumulative angle before the current chunk, mod 1 revolution
     alignas(16) float bias[2][4][kN];     // B / C bias of this head, per rank
     alignas(16) float normw[2][kN];       // BCNorm gains (ones when absent)
+    alignas(16) float onw[kP];            // output-norm gain of this head (ones when absent)
 };
 
 // with the fused rank projections: W_X, W_Z, W_O of this head, [rank][p]
@@ -301,7 +302,7 @@ __device__ __forceinline__ float prev_x(const ScanArgs &a, int64_t bi, int64_t h
     }
 }
 
-template <int MODE, int R, bool HAS_W, bool FUSED>
+template <int MODE, int R, bool HAS_W, bool FUSED, bool ONORM>
 __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, SplitPlan sp) {
     constexpr int C = kRows / R;  // tokens per chunk
     __shared__ typename std::conditional<FUSED, SmemFused, Smem>::type sm;
@@ -325,6 +326,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         sm.normw[e / kN][e % kN] = src ? src[e % kN] : 1.f;
     }
     if (tid < kHalf) sm.carry[tid] = 0.f;
+    if constexpr (ONORM) {
+        if (tid < kP) sm.onw[tid] = a.out_normw ? a.out_normw[hi * kP + tid] : 1.f;
+    }
+    // skip term D x: added to the diagonal of the masked scores (P[t][t] += D), so
+    // the X^T P^T product carries it
+    const float dsk = (MODE != kPass1 && a.D) ? a.D[hi] : 0.f;
     if constexpr (FUSED) {
         // global W is [H][P][R]: e runs over (p, r) of this head, rank fastest
         for (int e = tid; e < 3 * R * kP; e += kThreads) {
@@ -663,13 +670,14 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             for (int sb = 0; sb < 3; ++sb)
                 tws[sb] = *reinterpret_cast<const f32x4 *>(&sm.tw[w > 0 ? w - 1 : 0][16 * sb + 4 * lg]);
             // diagonal block w: exp(cs_t - cs_s) w_s below the diagonal, gamma on it
-            f32x4 mdiag;
+            f32x4 mdiag, dadd;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int stok = (16 * w + 4 * lg + j) / R;
                 const float e = __builtin_amdgcn_exp2f(fminf(l2t - l2s[j], 0.f)) * ws[j];
                 const float before = (stok < ttok) ? 1.f : 0.f, same = (stok == ttok) ? 1.f : 0.f;
                 mdiag[j] = before * e + same * gmt;
+                dadd[j] = (4 * lg + j == lr) ? dsk : 0.f;  // the row's own entry
             }
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
@@ -680,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 #pragma unroll
                     for (int j = 0; j < 4; ++j) sT[sb][j] *= tws[sb < 3 ? sb : 2][j] * ft;
                 } else if (sb == w) {
-                    sT[sb] *= mdiag;
+                    sT[sb] = sT[sb] * mdiag + dadd;
                 }
             }
             bf16x8 pfr[2];
@@ -693,8 +701,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 }
             // ---- Y^T = (St C_bar^T) diag(exp(cs)) + X^T P^T ; lane: column t = row, rows p
             const float eo = sm.eoff[row];
-#pragma unroll
-            for (int pb = 0; pb < 4; ++pb) {
+            auto y_block = [&](int pb) -> f32x4 {
                 const int p = 16 * pb + lr;
                 f32x4 yv = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -712,9 +719,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                         yv = mfma(xv, pfr[m2], yv);
                     }
                 }
+                return yv;
+            };
+            // gate and rank contraction (App. C): sum over the R lanes of the token of
+            // W_O Y SiLU(W_Z Z'); every lane of the token ends with the sum
+            auto gate_block = [&](int pb, const f32x4 &yv) -> f32x4 {
                 if constexpr (FUSED) {
-                    // gate and rank contraction (App. C): sum over the R lanes of the
-                    // token of W_O Y SiLU(W_Z Z'); the token's rank-0 lane stores it
                     const f32x4 wz = *reinterpret_cast<const f32x4 *>(&sm.fw[1][r_row][16 * pb + 4 * lg]);
                     const f32x4 wo = *reinterpret_cast<const f32x4 *>(&sm.fw[2][r_row][16 * pb + 4 * lg]);
                     f32x4 ov;
@@ -724,13 +734,58 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                         const float silu = zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz));
                         ov[j] = group_sum<R>(wo[j] * yv[j] * silu);
                     }
-                    if (valid && r_row == 0) {
-                        const bf16x4 o = {(__bf16)ov[0], (__bf16)ov[1], (__bf16)ov[2], (__bf16)ov[3]};
-                        *reinterpret_cast<bf16x4 *>(cb.y + t_row * (int)H * kP + 16 * pb + 4 * lg) = o;
+                    return ov;
+                } else {
+                    return yv;
+                }
+            };
+            __bf16 *const orow = FUSED ? cb.y + t_row * (int)H * kP : cb.y + ln.offX;
+            auto store_block = [&](int pb, const f32x4 &v) {
+                const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+                *reinterpret_cast<bf16x4 *>(orow + 16 * pb + 4 * lg) = o;
+            };
+            // the token's rank-0 lane stores the gated output
+            const bool writer = valid && (!FUSED || r_row == 0);
+            if constexpr (!ONORM) {
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    const f32x4 yv = y_block(pb);
+                    if constexpr (FUSED) {
+                        const f32x4 ov = gate_block(pb, yv);
+                        if (writer) store_block(pb, ov);
+                    } else if (writer) {
+                        store_block(pb, yv);
                     }
-                } else if (valid) {
-                    const bf16x4 o = {(__bf16)yv[0], (__bf16)yv[1], (__bf16)yv[2], (__bf16)yv[3]};
-                    *reinterpret_cast<bf16x4 *>(cb.y + ln.offX + 16 * pb + 4 * lg) = o;
+                }
+            } else {
+                // grouped output RMSNorm: a row's 64 channels sit in lanes lr + 16 lg
+                // (16 each), so the mean square is a 16-term sum and a sum over rows
+                f32x4 v4[4], wn[4];
+#pragma unroll
+                for (int pb = 0; pb < 4; ++pb) {
+                    v4[pb] = y_block(pb);
+                    wn[pb] = *reinterpret_cast<const f32x4 *>(&sm.onw[16 * pb + 4 * lg]);
+                }
+                auto norm4 = [&]() {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ss = __builtin_fmaf(v4[pb][j], v4[pb][j], ss);
+                    const float rs = __builtin_amdgcn_rsqf(sum_over_rows(ss) * (1.f / kP) + a.eps);
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) v4[pb] = v4[pb] * wn[pb] * rs;
+                };
+                const bool after = FUSED && a.norm_after_gate;
+                if (!after) norm4();  // each rank row of y (of Y, before the gate)
+                if constexpr (FUSED) {
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) v4[pb] = gate_block(pb, v4[pb]);
+                    if (after) norm4();  // O', after the gate and the rank contraction
+                }
+                if (writer) {
+#pragma unroll
+                    for (int pb = 0; pb < 4; ++pb) store_block(pb, v4[pb]);
                 }
             }
             __syncthreads();  // B3: St and Bb reads done
@@ -868,29 +923,31 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
     }
 }
 
-template <int R, bool HAS_W, bool FUSED>
+template <int R, bool HAS_W, bool FUSED, bool ONORM>
 hipError_t launch_rw(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
     const int64_t chains = a.b * a.H;
     if (sp.nseg <= 1) {
-        hipLaunchKernelGGL((scan_mfma_kernel<kFull, R, HAS_W, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a,
-                           sp);
+        hipLaunchKernelGGL((scan_mfma_kernel<kFull, R, HAS_W, FUSED, ONORM>), dim3((unsigned)chains), dim3(kThreads), 0,
+                           s, a, sp);
         return hipGetLastError();
     }
     const unsigned nblk = (unsigned)(chains * sp.nseg);
-    hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R, HAS_W, FUSED>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
+    // pass 1 produces no output, so it takes no output norm
+    hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R, HAS_W, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R, HAS_W, FUSED>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
+    hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R, HAS_W, FUSED, ONORM>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
     return hipGetLastError();
 }
 
 template <int R, bool FUSED>
 hipError_t launch_rf(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
-    if (a.B_normw || a.C_normw) return launch_rw<R, true, FUSED>(a, sp, s);
-    return launch_rw<R, false, FUSED>(a, sp, s);
+    const bool hw = a.B_normw || a.C_normw;
+    if (a.onorm) return hw ? launch_rw<R, true, FUSED, true>(a, sp, s) : launch_rw<R, false, FUSED, true>(a, sp, s);
+    return hw ? launch_rw<R, true, FUSED, false>(a, sp, s) : launch_rw<R, false, FUSED, false>(a, sp, s);
 }
 
 template <int R>

@@ -19,6 +19,8 @@ M3_OK = 0
 M3_F32, M3_BF16 = 0, 1
 M3_FLAG_FORCE_GENERIC = 1
 M3_FLAG_BF16_STATE = 2
+M3_FLAG_OUT_NORM = 4
+M3_FLAG_NORM_AFTER_GATE = 8
 
 
 class Shape(ctypes.Structure):
@@ -33,13 +35,13 @@ class Shape(ctypes.Structure):
 class ScanIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "Braw", "Craw", "dt", "A", "lam", "theta", "B_bias", "C_bias", "B_normw", "C_normw",
-        "h0", "x_prev", "Braw_prev", "y", "h_final", "z", "W_X", "W_Z", "W_O", "o")]
+        "h0", "x_prev", "Braw_prev", "y", "h_final", "z", "W_X", "W_Z", "W_O", "o", "D", "out_normw")]
 
 
 class DecodeIO(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "Braw", "Craw", "dt", "A", "lam", "theta", "B_bias", "C_bias", "B_normw", "C_normw",
-        "x_prev", "Braw_prev", "h", "y", "z", "W_X", "W_Z", "W_O", "o")]
+        "x_prev", "Braw_prev", "h", "y", "z", "W_X", "W_Z", "W_O", "o", "D", "out_normw")]
 
 
 class Plan(ctypes.Structure):
@@ -111,11 +113,23 @@ def make_shape(batch, seqlen, nheads, ngroups, headdim, dstate, rank, chunk, io_
     return Shape(batch, seqlen, nheads, ngroups, headdim, dstate, rank, chunk, io_dtype, flags, eps, nsegments)
 
 
-def scan_shape(x, Braw, chunk, eps=1e-5, *, force_generic=False, nsegments=0) -> Shape:
+def _norm_flags(out_norm) -> int:
+    """out_norm: False/None (no output norm), True or "pre" (norm y, or Y before the
+    gate), "post" (norm O' after the gate; fused form only)."""
+    if not out_norm:
+        return 0
+    if out_norm is True or out_norm == "pre":
+        return M3_FLAG_OUT_NORM
+    if out_norm == "post":
+        return M3_FLAG_OUT_NORM | M3_FLAG_NORM_AFTER_GATE
+    raise ValueError("out_norm must be False, True, 'pre' or 'post'")
+
+
+def scan_shape(x, Braw, chunk, eps=1e-5, *, force_generic=False, nsegments=0, out_norm=False) -> Shape:
     b, L, H, R, P = x.shape
     G, N = Braw.shape[2], Braw.shape[4]
     return make_shape(b, L, H, G, P, N, R, chunk, _io_dtype(x), eps,
-                      M3_FLAG_FORCE_GENERIC if force_generic else 0, nsegments)
+                      (M3_FLAG_FORCE_GENERIC if force_generic else 0) | _norm_flags(out_norm), nsegments)
 
 
 def plan(shape: Shape) -> Plan:
@@ -131,10 +145,12 @@ def workspace_bytes(shape: Shape) -> int:
 def scan_fwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *, chunk=64, eps=1e-5,
              B_normw=None, C_normw=None, h0=None, x_prev=None, Braw_prev=None,
              y=None, h_final=None, want_state=True, workspace=None, nsegments=0,
-             force_generic=False, stream=None):
+             force_generic=False, D=None, out_norm=False, out_normw=None, stream=None):
     """Chunked-scan prefill (m3_scan_fwd). Shapes: x [b,L,H,R,P], Braw/Craw [b,L,G,R,N],
-    dt/A/lam [b,L,H], theta [b,L,G,N/2], biases [H,R,N]. Returns (y, h_final)."""
-    shape = scan_shape(x, Braw, chunk, eps, force_generic=force_generic, nsegments=nsegments)
+    dt/A/lam [b,L,H], theta [b,L,G,N/2], biases [H,R,N]; optional skip D [H] and output
+    norm (out_norm=True, gain out_normw [H,P]). Returns (y, h_final)."""
+    shape = scan_shape(x, Braw, chunk, eps, force_generic=force_generic, nsegments=nsegments,
+                       out_norm=out_norm)
     if y is None:
         y = torch.empty_like(x)
     if h_final is None and want_state:
@@ -146,6 +162,7 @@ def scan_fwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *, chunk=64, eps=
     io = ScanIO(_ptr(x), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
                 _ptr(B_bias), _ptr(C_bias), _ptr(B_normw), _ptr(C_normw), _ptr(h0),
                 _ptr(x_prev), _ptr(Braw_prev), _ptr(y), _ptr(h_final))
+    io.D, io.out_normw = _ptr(D), _ptr(out_normw)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.m3_scan_fwd(ctypes.byref(shape), ctypes.byref(io), _ptr(workspace), wsb, _stream(stream)))
     return y, h_final
@@ -154,14 +171,15 @@ def scan_fwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *, chunk=64, eps=
 def scan_fused_fwd(x_in, z_in, W_X, W_Z, W_O, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *,
                    chunk=64, eps=1e-5, B_normw=None, C_normw=None, h0=None, x_prev_in=None,
                    Braw_prev=None, o=None, h_final=None, want_state=True, workspace=None,
-                   nsegments=0, stream=None):
+                   nsegments=0, D=None, out_norm=None, out_normw=None, stream=None):
     """Prefill with the fused MIMO projections and gate (m3_scan_fwd with W_X set).
-    x_in, z_in [b,L,H,P] (X', Z'), W_X/W_Z/W_O [H,P,R], x_prev_in [b,H,P] or None.
+    x_in, z_in [b,L,H,P] (X', Z'), W_X/W_Z/W_O [H,P,R], x_prev_in [b,H,P] or None;
+    skip D [H], output norm out_norm None / "pre" / "post" with gain out_normw [H,P].
     Returns (o [b,L,H,P], h_final)."""
     b, L, H, P = x_in.shape
     R = W_X.shape[2]
     G, N = Braw.shape[2], Braw.shape[4]
-    shape = make_shape(b, L, H, G, P, N, R, chunk, _io_dtype(x_in), eps, 0, nsegments)
+    shape = make_shape(b, L, H, G, P, N, R, chunk, _io_dtype(x_in), eps, _norm_flags(out_norm), nsegments)
     if o is None:
         o = torch.empty_like(x_in)
     if h_final is None and want_state:
@@ -172,45 +190,48 @@ def scan_fused_fwd(x_in, z_in, W_X, W_Z, W_O, Braw, Craw, dt, A, lam, theta, B_b
     io = ScanIO(_ptr(x_in), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
                 _ptr(B_bias), _ptr(C_bias), _ptr(B_normw), _ptr(C_normw), _ptr(h0),
                 _ptr(x_prev_in), _ptr(Braw_prev), None, _ptr(h_final),
-                _ptr(z_in), _ptr(W_X), _ptr(W_Z), _ptr(W_O), _ptr(o))
+                _ptr(z_in), _ptr(W_X), _ptr(W_Z), _ptr(W_O), _ptr(o), _ptr(D), _ptr(out_normw))
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.m3_scan_fwd(ctypes.byref(shape), ctypes.byref(io), _ptr(workspace), wsb, _stream(stream)))
     return o, h_final
 
 
 def decode_step(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, h, *, eps=1e-5,
-                B_normw=None, C_normw=None, x_prev=None, Braw_prev=None, y=None, stream=None):
+                B_normw=None, C_normw=None, x_prev=None, Braw_prev=None, y=None, D=None,
+                out_norm=False, out_normw=None, stream=None):
     """One decode step (m3_decode_step). x [b,H,R,P], Braw/Craw [b,G,R,N], dt/A/lam [b,H],
     theta [b,G,N/2], h [b,H,P,N] updated in place: fp32, or bf16 (then the step runs with
-    M3_FLAG_BF16_STATE). Returns y [b,H,R,P]."""
+    M3_FLAG_BF16_STATE); skip D and output norm as in scan_fwd. Returns y [b,H,R,P]."""
     b, H, R, P = x.shape
     G, N = Braw.shape[1], Braw.shape[3]
-    flags = M3_FLAG_BF16_STATE if h.dtype == torch.bfloat16 else 0
+    flags = (M3_FLAG_BF16_STATE if h.dtype == torch.bfloat16 else 0) | _norm_flags(out_norm)
     shape = make_shape(b, 1, H, G, P, N, R, 1, _io_dtype(x), eps, flags)
     if y is None:
         y = torch.empty_like(x)
     io = DecodeIO(_ptr(x), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
                   _ptr(B_bias), _ptr(C_bias), _ptr(B_normw), _ptr(C_normw), _ptr(x_prev),
                   _ptr(Braw_prev), _ptr(h), _ptr(y))
+    io.D, io.out_normw = _ptr(D), _ptr(out_normw)
     _check(lib.m3_decode_step(ctypes.byref(shape), ctypes.byref(io), _stream(stream)))
     return y
 
 
 def decode_fused_step(x_in, z_in, W_X, W_Z, W_O, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, h, *,
                       eps=1e-5, B_normw=None, C_normw=None, x_prev_in=None, Braw_prev=None, o=None,
-                      stream=None):
+                      D=None, out_norm=None, out_normw=None, stream=None):
     """One decode step with the fused projections. x_in, z_in [b,H,P], W_* [H,P,R],
     h [b,H,P,N] (fp32 or bf16) updated in place. Returns o [b,H,P]."""
     b, H, P = x_in.shape
     R = W_X.shape[2]
     G, N = Braw.shape[1], Braw.shape[3]
-    flags = M3_FLAG_BF16_STATE if h.dtype == torch.bfloat16 else 0
+    flags = (M3_FLAG_BF16_STATE if h.dtype == torch.bfloat16 else 0) | _norm_flags(out_norm)
     shape = make_shape(b, 1, H, G, P, N, R, 1, _io_dtype(x_in), eps, flags)
     if o is None:
         o = torch.empty_like(x_in)
     io = DecodeIO(_ptr(x_in), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
                   _ptr(B_bias), _ptr(C_bias), _ptr(B_normw), _ptr(C_normw), _ptr(x_prev_in),
-                  _ptr(Braw_prev), _ptr(h), None, _ptr(z_in), _ptr(W_X), _ptr(W_Z), _ptr(W_O), _ptr(o))
+                  _ptr(Braw_prev), _ptr(h), None, _ptr(z_in), _ptr(W_X), _ptr(W_Z), _ptr(W_O), _ptr(o),
+                  _ptr(D), _ptr(out_normw))
     _check(lib.m3_decode_step(ctypes.byref(shape), ctypes.byref(io), _stream(stream)))
     return o
 

@@ -25,12 +25,13 @@ def gpu_scan(inp, shape, **kw):
     y, h = m3.scan_fwd(d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"],
                        d["B_bias"], d["C_bias"], chunk=shape.chunk, eps=shape.eps,
                        B_normw=d.get("B_normw"), C_normw=d.get("C_normw"), h0=d.get("h0"),
-                       x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"), **kw)
+                       x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"), D=d.get("D"),
+                       out_normw=d.get("out_normw"), **kw)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64), h.cpu().numpy().astype(np.float64)
 
 
-def gpu_decode(inp, shape, bf16_state=False):
+def gpu_decode(inp, shape, bf16_state=False, **kw):
     """One decode step on the GPU. With bf16_state the state is handed over as bf16
     (the caller passes a state whose values are bf16-exact) and comes back as bf16."""
     from state_space_sequence_amd import m3
@@ -40,7 +41,8 @@ def gpu_decode(inp, shape, bf16_state=False):
         h = h.to(torch.bfloat16)
     y = m3.decode_step(d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"],
                        d["B_bias"], d["C_bias"], h, eps=shape.eps, B_normw=d.get("B_normw"),
-                       C_normw=d.get("C_normw"), x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"))
+                       C_normw=d.get("C_normw"), x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"),
+                       D=d.get("D"), out_normw=d.get("out_normw"), **kw)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64), h.float().cpu().numpy().astype(np.float64)
 
@@ -53,12 +55,12 @@ def gpu_scan_fused(inp, shape, **kw):
                              d["dt"], d["A"], d["lam"], d["theta"], d["B_bias"], d["C_bias"],
                              chunk=shape.chunk, eps=shape.eps, B_normw=d.get("B_normw"),
                              C_normw=d.get("C_normw"), h0=d.get("h0"), x_prev_in=d.get("x_prev_in"),
-                             Braw_prev=d.get("Braw_prev"), **kw)
+                             Braw_prev=d.get("Braw_prev"), D=d.get("D"), out_normw=d.get("out_normw"), **kw)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), h.cpu().numpy().astype(np.float64)
 
 
-def gpu_decode_fused(inp, shape, bf16_state=False):
+def gpu_decode_fused(inp, shape, bf16_state=False, **kw):
     """One fused decode step (inputs from make_fused_decode_inputs)."""
     from state_space_sequence_amd import m3
     d = m3.to_device(inp, shape.io)
@@ -68,6 +70,7 @@ def gpu_decode_fused(inp, shape, bf16_state=False):
     o = m3.decode_fused_step(d["x_in"], d["z_in"], d["W_X"], d["W_Z"], d["W_O"], d["Braw"], d["Craw"],
                              d["dt"], d["A"], d["lam"], d["theta"], d["B_bias"], d["C_bias"], h,
                              eps=shape.eps, B_normw=d.get("B_normw"), C_normw=d.get("C_normw"),
-                             x_prev_in=d.get("x_prev_in"), Braw_prev=d.get("Braw_prev"))
+                             x_prev_in=d.get("x_prev_in"), Braw_prev=d.get("Braw_prev"), D=d.get("D"),
+                             out_normw=d.get("out_normw"), **kw)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), h.float().cpu().numpy().astype(np.float64)

@@ -64,7 +64,7 @@ FUSED_FIELDS = ("z", "W_X", "W_Z", "W_O", "o")
 def _fake_io(m3, base=0x100000, misalign=None, drop=None, fused=False):
     io = m3.ScanIO()
     for i, (name, _) in enumerate(m3.ScanIO._fields_):
-        if name in ("B_normw", "C_normw", "h0", "x_prev", "Braw_prev", "h_final"):
+        if name in ("B_normw", "C_normw", "h0", "x_prev", "Braw_prev", "h_final", "D", "out_normw"):
             continue
         if (name in FUSED_FIELDS) != fused and name in FUSED_FIELDS + ("y",):
             continue
@@ -114,7 +114,7 @@ def test_decode_fused_fields_validated(m3):
     def dio(fused, drop=None):
         io = m3.DecodeIO()
         for i, (name, _) in enumerate(m3.DecodeIO._fields_):
-            if name in ("B_normw", "C_normw", "x_prev", "Braw_prev"):
+            if name in ("B_normw", "C_normw", "x_prev", "Braw_prev", "D", "out_normw"):
                 continue
             if (name in FUSED_FIELDS) != fused and name in FUSED_FIELDS + ("y",):
                 continue
@@ -162,7 +162,7 @@ def test_flags_validated(m3):
     """The bf16-state flag is decode only; unknown flag bits are rejected by both calls."""
     assert m3.M3_FLAG_BF16_STATE == 2
     assert _scan(m3, _shape(m3, flags=m3.M3_FLAG_BF16_STATE), _fake_io(m3)) == -1
-    assert _scan(m3, _shape(m3, flags=8), _fake_io(m3)) == -1
+    assert _scan(m3, _shape(m3, flags=16), _fake_io(m3)) == -1
     io = m3.DecodeIO()
     s = _shape(m3, flags=m3.M3_FLAG_FORCE_GENERIC)
     assert m3.lib.m3_decode_step(ctypes.byref(s), ctypes.byref(io), None) == -1
@@ -171,6 +171,32 @@ def test_flags_validated(m3):
     assert m3.lib.m3_decode_step(ctypes.byref(s), ctypes.byref(io), None) == -1
     s = _shape(m3, batch=0, flags=m3.M3_FLAG_BF16_STATE)
     assert m3.lib.m3_decode_step(ctypes.byref(s), ctypes.byref(io), None) == 0
+
+
+def test_epilogue_validated(m3):
+    """The output-norm gain needs M3_FLAG_OUT_NORM; the after-gate position needs the norm
+    and the fused gate; D and the gain are alignment-checked like every other pointer."""
+    NORM, AFTER = m3.M3_FLAG_OUT_NORM, m3.M3_FLAG_NORM_AFTER_GATE
+    s = _shape(m3, rank=4)
+    io = _fake_io(m3)
+    io.out_normw = 0x900000
+    assert _scan(m3, s, io) == -1
+    assert _scan(m3, _shape(m3, rank=4, flags=NORM | AFTER), _fake_io(m3)) == -1
+    assert _scan(m3, _shape(m3, rank=4, flags=AFTER), _fake_io(m3, fused=True)) == -1
+    io = _fake_io(m3)
+    io.D = 0x900004
+    assert _scan(m3, s, io) == -3
+    io = _fake_io(m3, fused=True)
+    io.out_normw = 0x900008
+    assert _scan(m3, _shape(m3, rank=4, flags=NORM | AFTER), io) == -3
+    d = m3.DecodeIO()
+    d.out_normw = 0x900000
+    assert m3.lib.m3_decode_step(ctypes.byref(_shape(m3, rank=4, seqlen=1, chunk=1)), ctypes.byref(d), None) == -1
+    d = m3.DecodeIO()
+    sd = _shape(m3, rank=4, seqlen=1, chunk=1, batch=0, flags=NORM | AFTER)
+    assert m3.lib.m3_decode_step(ctypes.byref(sd), ctypes.byref(d), None) == -1
+    sd = _shape(m3, rank=4, seqlen=1, chunk=1, batch=0, flags=NORM)
+    assert m3.lib.m3_decode_step(ctypes.byref(sd), ctypes.byref(d), None) == 0
 
 
 def test_plans_for_workloads(m3):
