@@ -222,3 +222,82 @@ def decode_fused_out(inp: dict, shape, *, out_norm=None, nthreads: int = 0):
     d["x_prev"] = None if xp is None else expand_ranks(xp, inp["W_X"]).astype(np.float32)
     y, h = decode(d, shape, nthreads=nthreads)
     return _gated_out(y, d["x"], inp, shape.eps, out_norm), h
+
+
+# ---------------------------------------------------------------------------
+# Gradients of the prefill (training backward). The pages give no backward
+# derivation, so the oracle takes the plainest one: the derivative of the
+# forward's definition. ``scan_torch`` restates the sequential physical-frame
+# recurrence of m3_oracle.c (same definition, written independently with torch
+# float64 tensors on the CPU, one token at a time), and ``scan_grads`` applies
+# reverse-mode differentiation (torch.autograd, a library primitive) to it.
+# Pinned by: its forward agreeing with the C oracle, and its gradients agreeing
+# with central finite differences of the C oracle.
+
+GRAD_INPUTS = ("x", "Braw", "Craw", "dt", "A", "lam", "theta", "B_bias", "C_bias",
+               "B_normw", "C_normw", "h0", "x_prev", "Braw_prev")
+
+
+def scan_torch(t: dict, shape):
+    """The recurrence on torch float64 tensors t[...] (same layouts as scan). Returns
+    (y [b,L,H,R,P], h_final [b,H,P,N])."""
+    import torch
+    b, L, H, G = shape.batch, shape.seqlen, shape.nheads, shape.ngroups
+    P, N, R = shape.headdim, shape.dstate, shape.rank
+    half = N // 2
+    gi = torch.arange(H) // (H // G)  # group of each head
+
+    def bc(raw, w, bias):  # raw [b,H,R,N] -> BCNorm (RMS over N) * gain + bias
+        inv = 1.0 / torch.sqrt((raw * raw).mean(dim=-1, keepdim=True) + shape.eps)
+        out = raw * inv
+        if w is not None:
+            out = out * w
+        return out + bias
+
+    def rot(Hs, ang):  # rotate pairs (i, i + N/2) of Hs [b,H,N,P] by ang [b,H,N/2]
+        c, s = torch.cos(ang)[..., None], torch.sin(ang)[..., None]
+        lo, hi = Hs[:, :, :half], Hs[:, :, half:]
+        return torch.cat([c * lo - s * hi, s * lo + c * hi], dim=2)
+
+    Hs = t["h0"].transpose(-1, -2) if t.get("h0") is not None else torch.zeros(b, H, N, P, dtype=torch.float64)
+    prev = None
+    if t.get("x_prev") is not None:
+        prev = (bc(t["Braw_prev"][:, gi], t.get("B_normw"), t["B_bias"]), t["x_prev"])
+    ys = []
+    for k in range(L):
+        d, a, lm = t["dt"][:, k], t["A"][:, k], t["lam"][:, k]  # [b,H]
+        Bk = bc(t["Braw"][:, k][:, gi], t.get("B_normw"), t["B_bias"])  # [b,H,R,N]
+        Ck = bc(t["Craw"][:, k][:, gi], t.get("C_normw"), t["C_bias"])
+        xk = t["x"][:, k]  # [b,H,R,P]
+        alpha = torch.exp(d * a)
+        u = alpha[..., None, None] * Hs
+        if prev is not None:
+            beta = (1.0 - lm) * d * alpha
+            u = u + beta[..., None, None] * torch.einsum("bhrn,bhrp->bhnp", prev[0], prev[1])
+        ang = d[..., None] * t["theta"][:, k][:, gi]  # [b,H,N/2]
+        Hs = rot(u, ang) + (lm * d)[..., None, None] * torch.einsum("bhrn,bhrp->bhnp", Bk, xk)
+        ys.append(torch.einsum("bhrn,bhnp->bhrp", Ck, Hs))
+        prev = (Bk, xk)
+    y = torch.stack(ys, dim=1) if L > 0 else torch.zeros(b, 0, H, R, P, dtype=torch.float64)
+    return y, Hs.transpose(-1, -2)
+
+
+def scan_grads(inp: dict, shape, dy, dh_final=None):
+    """Gradients of <dy, y> + <dh_final, h_final> with respect to every input that is
+    present (GRAD_INPUTS order; absent inputs are skipped). Returns a dict of float64
+    arrays with the inputs' shapes."""
+    import torch
+    t, names = {}, []
+    for k in GRAD_INPUTS:
+        v = inp.get(k)
+        if v is None:
+            continue
+        t[k] = torch.tensor(np.asarray(v, dtype=np.float64), requires_grad=True)
+        names.append(k)
+    y, hf = scan_torch(t, shape)
+    outs, gouts = [y], [torch.tensor(np.asarray(dy, dtype=np.float64))]
+    if dh_final is not None:
+        outs.append(hf)
+        gouts.append(torch.tensor(np.asarray(dh_final, dtype=np.float64)))
+    g = torch.autograd.grad(outs, [t[k] for k in names], gouts, allow_unused=True)
+    return {k: (np.zeros(inp[k].shape) if gk is None else gk.detach().numpy()) for k, gk in zip(names, g)}
