@@ -169,6 +169,28 @@ typedef struct {
     const float *out_normw; /* [H,P] output-norm gain, as in m3_scan_io, or NULL */
 } m3_decode_io;
 
+/* Gradients of the prefill (m3_scan_bwd): upstream gradients in, the gradient of
+ * <dy, y> + <dh_final, h_final> with respect to every forward input out. All
+ * outputs are fp32 and fully overwritten. */
+typedef struct {
+    const void *dy;          /* [b,L,H,R,P] io: gradient of y */
+    const float *dh_final;   /* [b,H,P,N] gradient of h_final, or NULL (zero) */
+    float *dx;               /* [b,L,H,R,P] */
+    float *dBraw;            /* [b,L,G,R,N] */
+    float *dCraw;            /* [b,L,G,R,N] */
+    float *ddt;              /* [b,L,H] */
+    float *dA;               /* [b,L,H] */
+    float *dlam;             /* [b,L,H] */
+    float *dtheta;           /* [b,L,G,N/2] */
+    float *dB_bias;          /* [H,R,N] */
+    float *dC_bias;          /* [H,R,N] */
+    float *dB_normw;         /* [N]: required when the forward had B_normw, else NULL */
+    float *dC_normw;         /* [N]: required when the forward had C_normw, else NULL */
+    float *dh0;              /* [b,H,P,N] gradient of the initial state, or NULL (not wanted) */
+    float *dx_prev;          /* [b,H,R,P]: required when the forward had x_prev, else NULL */
+    float *dBraw_prev;       /* [b,G,R,N]: likewise */
+} m3_scan_grads;
+
 /* What m3_scan_fwd will launch for a shape (for logs and tests). */
 typedef struct {
     int32_t kernel;         /* 0 = fp32 vector-ALU chunked kernel, 1 = bf16 matrix-core kernel */
@@ -196,6 +218,24 @@ m3_status m3_scan_plan(const m3_shape *shape, m3_plan *plan);
  * y = h^T C (App. B.3 eq. 25 with App. C's rank-R form). Decode requires
  * N in {16, 32, 64, 128, 256}, P <= 256, R <= 4. */
 m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *stream);
+
+/* Prefill backward: the gradients of the chunked scan for training (the forward
+ * being m3_scan_fwd with the same shape and io). The pages give no backward; this
+ * is the adjoint of the chunked algorithm of §3.3 in the rotated frame of §3.2.2
+ * (Proposition 4), taken term by term: masked scores, carried state, decay,
+ * trapezoid weights (§3.1.3 eq. 7), rotation angles and BCNorm + bias (§3.4).
+ * Computed in fp32 for io fp32 or bf16, any L; shapes as for the fp32 prefill
+ * kernel (N, P <= 128, N * P <= 8192, R <= 4). shape->chunk is not used: the
+ * backward picks its own chunk (32 / R tokens), the result does not depend on it.
+ * The fused projections and the output epilogue are not differentiated here
+ * (M3_ERR_UNSUPPORTED when io->W_X or io->D is set or M3_FLAG_OUT_NORM is on);
+ * io->y and io->h_final are not read. The workspace (m3_scan_bwd_workspace_bytes)
+ * holds chunk-start states and per-head partial gradients. */
+m3_status m3_scan_bwd(const m3_shape *shape, const m3_scan_io *io, const m3_scan_grads *grads,
+                      void *workspace, size_t ws_bytes, void *stream);
+
+/* Bytes of device workspace m3_scan_bwd needs for this shape. */
+size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape);
 
 /* Human-readable name of a status code (static string). */
 const char *m3_status_str(m3_status status);

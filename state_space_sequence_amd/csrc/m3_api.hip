@@ -15,6 +15,17 @@ __global__ void state_copy_kernel(const float *h0, float *hf, int64_t n) {
 
 bool aligned16(const void *p) { return p == nullptr || (((uintptr_t)p) & 15u) == 0; }
 
+__global__ void fill_zero_kernel(float *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+hipError_t zero(float *p, int64_t n, hipStream_t s) {
+    if (!p || n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
 struct Plan {
     int kernel;       // 0 generic, 1 matrix-core
     int nseg;         // segments per sequence
@@ -97,7 +108,7 @@ const char *m3_status_str(m3_status st) {
     return "unknown status";
 }
 
-int m3_version(void) { return 103; }
+int m3_version(void) { return 104; }
 
 // Output epilogue flags against the pointers: the gain needs the norm flag, and
 // the after-gate position needs the norm and the fused gate.
@@ -190,6 +201,89 @@ m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspa
         if (p.nseg > 1) mfma_workspace_carve(workspace, s.batch * s.nheads, p.nseg, s.headdim, s.dstate, &sp);
         e = launch_scan_mfma(a, sp, hs);
     }
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+// Backward limits: those of the fp32 prefill kernel (the backward keeps every
+// tile of a 32-row chunk in LDS), N even.
+static bool bwd_shape_ok(const m3_shape &s) {
+    return s.dstate <= kGenericMaxN && s.headdim <= kGenericMaxP && s.dstate * s.headdim <= kGenericMaxNP &&
+           s.rank <= 4;
+}
+
+static ScanArgs bwd_args(const m3_shape &s, const m3_scan_io *io) {
+    ScanArgs a{};
+    a.b = s.batch; a.L = s.seqlen; a.H = s.nheads; a.G = s.ngroups; a.P = s.headdim; a.N = s.dstate;
+    a.R = s.rank; a.C = s.chunk; a.eps = s.eps; a.bf16 = (s.io_dtype == M3_BF16);
+    if (io) {
+        a.has_prev = io->x_prev != nullptr;
+        a.x = io->x; a.Braw = io->Braw; a.Craw = io->Craw; a.dt = io->dt; a.A = io->A; a.lam = io->lam;
+        a.theta = io->theta; a.B_bias = io->B_bias; a.C_bias = io->C_bias; a.B_normw = io->B_normw;
+        a.C_normw = io->C_normw; a.h0 = io->h0; a.x_prev = io->x_prev; a.Braw_prev = io->Braw_prev;
+    }
+    return a;
+}
+
+size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape) {
+    if (check_shape(shape) != M3_OK || !bwd_shape_ok(*shape)) return 0;
+    return scan_bwd_workspace_bytes(bwd_args(*shape, nullptr), nullptr);
+}
+
+m3_status m3_scan_bwd(const m3_shape *shape, const m3_scan_io *io, const m3_scan_grads *gr, void *workspace,
+                      size_t ws_bytes, void *stream) {
+    m3_status st = check_shape(shape);
+    if (st != M3_OK) return st;
+    if (!io || !gr) return M3_ERR_INVALID_ARG;
+    const m3_shape &s = *shape;
+    if (s.flags & ~M3_FLAG_FORCE_GENERIC) return (s.flags & M3_FLAG_OUT_NORM) ? M3_ERR_UNSUPPORTED : M3_ERR_INVALID_ARG;
+    if (io->W_X || io->W_Z || io->W_O || io->z || io->o || io->D || io->out_normw) return M3_ERR_UNSUPPORTED;
+    if ((io->x_prev == nullptr) != (io->Braw_prev == nullptr)) return M3_ERR_INVALID_ARG;
+    if (!bwd_shape_ok(s)) return M3_ERR_UNSUPPORTED;
+    const bool work = s.batch * s.seqlen > 0;
+    const bool prev = io->x_prev != nullptr;
+    // every gradient of an input that is present is required, and none of an absent one
+    if ((gr->dB_normw == nullptr) != (io->B_normw == nullptr) || (gr->dC_normw == nullptr) != (io->C_normw == nullptr) ||
+        (gr->dx_prev == nullptr) != !prev || (gr->dBraw_prev == nullptr) != !prev)
+        return M3_ERR_INVALID_ARG;
+    if (!gr->dB_bias || !gr->dC_bias) return M3_ERR_INVALID_ARG;
+    if (work && (!io->x || !io->Braw || !io->Craw || !io->dt || !io->A || !io->lam || !io->theta || !io->B_bias ||
+                 !io->C_bias || !gr->dy || !gr->dx || !gr->dBraw || !gr->dCraw || !gr->ddt || !gr->dA ||
+                 !gr->dlam || !gr->dtheta))
+        return M3_ERR_INVALID_ARG;
+    const void *ptrs[] = {io->x, io->Braw, io->Craw, io->dt, io->A, io->lam, io->theta, io->B_bias, io->C_bias,
+                          io->B_normw, io->C_normw, io->h0, io->x_prev, io->Braw_prev, gr->dy, gr->dh_final,
+                          gr->dx, gr->dBraw, gr->dCraw, gr->ddt, gr->dA, gr->dlam, gr->dtheta, gr->dB_bias,
+                          gr->dC_bias, gr->dB_normw, gr->dC_normw, gr->dh0, gr->dx_prev, gr->dBraw_prev, workspace};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return M3_ERR_MISALIGNED;
+    const ScanArgs a = bwd_args(s, io);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    const int64_t HRN = s.nheads * s.rank * s.dstate;
+    if (!work) {
+        // no token: the bias and gain gradients are zero, dh0 = dh_final (h_final = h0),
+        // and the previous token is never used
+        const int64_t nst = s.batch * s.nheads * s.headdim * s.dstate;
+        if ((e = zero(gr->dB_bias, HRN, hs)) != hipSuccess || (e = zero(gr->dC_bias, HRN, hs)) != hipSuccess ||
+            (e = zero(gr->dB_normw, s.dstate, hs)) != hipSuccess || (e = zero(gr->dC_normw, s.dstate, hs)) != hipSuccess ||
+            (e = zero(gr->dx_prev, s.batch * s.nheads * s.rank * s.headdim, hs)) != hipSuccess ||
+            (e = zero(gr->dBraw_prev, s.batch * s.ngroups * s.rank * s.dstate, hs)) != hipSuccess)
+            return M3_ERR_HIP;
+        if (gr->dh0 && nst > 0) {
+            hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, hs, gr->dh_final,
+                               gr->dh0, nst);
+            if (hipGetLastError() != hipSuccess) return M3_ERR_HIP;
+        }
+        return M3_OK;
+    }
+    const size_t need = scan_bwd_workspace_bytes(a, nullptr);
+    if (workspace == nullptr || ws_bytes < need) return M3_ERR_WORKSPACE_TOO_SMALL;
+    BwdIO bio{};
+    bio.dy = gr->dy; bio.dh_final = gr->dh_final; bio.dx = gr->dx; bio.dBraw = gr->dBraw; bio.dCraw = gr->dCraw;
+    bio.ddt = gr->ddt; bio.dA = gr->dA; bio.dlam = gr->dlam; bio.dtheta = gr->dtheta; bio.dB_bias = gr->dB_bias;
+    bio.dC_bias = gr->dC_bias; bio.dB_normw = gr->dB_normw; bio.dC_normw = gr->dC_normw; bio.dh0 = gr->dh0;
+    bio.dx_prev = gr->dx_prev; bio.dBraw_prev = gr->dBraw_prev;
+    e = launch_scan_bwd(a, bio, workspace, hs);
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 

@@ -61,7 +61,18 @@ struct SplitPlan {
     float *seg_angle;  // [b,H,nseg,N/2] total rotation angle of each segment, in revolutions mod 1
 };
 
+// gradient pointers of the prefill backward (m3_scan_grads)
+struct BwdIO {
+    const void *dy;
+    const float *dh_final;
+    float *dx, *dBraw, *dCraw, *ddt, *dA, *dlam, *dtheta, *dB_bias, *dC_bias, *dB_normw, *dC_normw, *dh0,
+        *dx_prev, *dBraw_prev;
+};
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, hipStream_t s);
+size_t scan_bwd_workspace_bytes(const ScanArgs &a, int64_t *nsplit_out);
+size_t scan_bwd_smem_bytes(const ScanArgs &a);
 hipError_t launch_scan_generic(const ScanArgs &a, hipStream_t s);
 hipError_t launch_scan_mfma(const ScanArgs &a, const SplitPlan &sp, hipStream_t s);
 

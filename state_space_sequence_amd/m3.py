@@ -44,6 +44,12 @@ class DecodeIO(ctypes.Structure):
         "x_prev", "Braw_prev", "h", "y", "z", "W_X", "W_Z", "W_O", "o", "D", "out_normw")]
 
 
+class ScanGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "dy", "dh_final", "dx", "dBraw", "dCraw", "ddt", "dA", "dlam", "dtheta", "dB_bias", "dC_bias",
+        "dB_normw", "dC_normw", "dh0", "dx_prev", "dBraw_prev")]
+
+
 class Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("nsegments", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
@@ -57,6 +63,11 @@ def _load():
     lib.m3_scan_fwd.restype = ctypes.c_int
     lib.m3_scan_fwd.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ScanIO), ctypes.c_void_p,
                                 ctypes.c_size_t, ctypes.c_void_p]
+    lib.m3_scan_bwd.restype = ctypes.c_int
+    lib.m3_scan_bwd.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ScanIO), ctypes.POINTER(ScanGrads),
+                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.m3_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.m3_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
     lib.m3_decode_step.restype = ctypes.c_int
     lib.m3_decode_step.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(DecodeIO), ctypes.c_void_p]
     lib.m3_scan_workspace_bytes.restype = ctypes.c_size_t
@@ -194,6 +205,53 @@ def scan_fused_fwd(x_in, z_in, W_X, W_Z, W_O, Braw, Craw, dt, A, lam, theta, B_b
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.m3_scan_fwd(ctypes.byref(shape), ctypes.byref(io), _ptr(workspace), wsb, _stream(stream)))
     return o, h_final
+
+
+def scan_bwd_workspace_bytes(shape: Shape) -> int:
+    return int(lib.m3_scan_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def scan_bwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, dy, *, eps=1e-5, B_normw=None,
+             C_normw=None, h0=None, x_prev=None, Braw_prev=None, dh_final=None, want_dh0=True,
+             workspace=None, grads=None, stream=None):
+    """Prefill backward (m3_scan_bwd): gradients of <dy, y> + <dh_final, h_final> with
+    respect to the forward inputs (same tensors as scan_fwd). Returns a dict of fp32
+    tensors named like the inputs (x, Braw, ..., h0, x_prev, Braw_prev when present)."""
+    b, L, H, R, P = x.shape
+    G, N = Braw.shape[2], Braw.shape[4]
+    shape = make_shape(b, L, H, G, P, N, R, max(1, 64 // R), _io_dtype(x), eps)
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    if grads is None:
+        grads = {"x": torch.empty(x.shape, **f32), "Braw": torch.empty(Braw.shape, **f32),
+                 "Craw": torch.empty(Craw.shape, **f32), "dt": torch.empty(dt.shape, **f32),
+                 "A": torch.empty(A.shape, **f32), "lam": torch.empty(lam.shape, **f32),
+                 "theta": torch.empty(theta.shape, **f32), "B_bias": torch.empty(B_bias.shape, **f32),
+                 "C_bias": torch.empty(C_bias.shape, **f32)}
+        if B_normw is not None:
+            grads["B_normw"] = torch.empty(B_normw.shape, **f32)
+        if C_normw is not None:
+            grads["C_normw"] = torch.empty(C_normw.shape, **f32)
+        if want_dh0:
+            grads["h0"] = torch.empty((b, H, P, N), **f32)
+        if x_prev is not None:
+            grads["x_prev"] = torch.empty(x_prev.shape, **f32)
+            grads["Braw_prev"] = torch.empty(Braw_prev.shape, **f32)
+    ws = scan_bwd_workspace_bytes(shape)
+    if workspace is None and ws:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    io = ScanIO(_ptr(x), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
+                _ptr(B_bias), _ptr(C_bias), _ptr(B_normw), _ptr(C_normw), _ptr(h0),
+                _ptr(x_prev), _ptr(Braw_prev), None, None)
+    gd = grads.get
+    gs = ScanGrads(_ptr(dy), _ptr(dh_final), _ptr(gd("x")), _ptr(gd("Braw")), _ptr(gd("Craw")), _ptr(gd("dt")),
+                   _ptr(gd("A")), _ptr(gd("lam")), _ptr(gd("theta")), _ptr(gd("B_bias")), _ptr(gd("C_bias")),
+                   _ptr(gd("B_normw")), _ptr(gd("C_normw")), _ptr(gd("h0")), _ptr(gd("x_prev")),
+                   _ptr(gd("Braw_prev")))
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.m3_scan_bwd(ctypes.byref(shape), ctypes.byref(io), ctypes.byref(gs), _ptr(workspace), wsb,
+                           _stream(stream)))
+    return grads
 
 
 def decode_step(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, h, *, eps=1e-5,
