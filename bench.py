@@ -85,6 +85,16 @@ def fused_decode_bytes(s, state_bytes=4) -> int:
     return decode_bytes(s, state_bytes) - 3 * b * H * R * P * io + 4 * b * H * P * io + 3 * H * P * R * 4
 
 
+def bwd_bytes(s) -> int:
+    """Bytes the prefill backward must move at least once: the forward's inputs and dy
+    (io dtype; dt/A/lam/theta fp32) in, every gradient (fp32) out."""
+    io = 2 if s.io == "bf16" else 4
+    b, L, H, G, P, N, R = s.batch, s.seqlen, s.nheads, s.ngroups, s.headdim, s.dstate, s.rank
+    return (2 * b * L * H * R * P * io + 2 * b * L * G * R * N * io + 3 * b * L * H * 4 + b * L * G * (N // 2) * 4
+            + b * L * H * R * P * 4 + 2 * b * L * G * R * N * 4 + 3 * b * L * H * 4 + b * L * G * (N // 2) * 4
+            + 4 * H * R * N * 4)
+
+
 # ----------------------------------------------------------------- helpers --
 def scan_args(d, s):
     return (d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"], d["B_bias"], d["C_bias"])
@@ -425,6 +435,40 @@ def main():
             log(key, ent)
             extra[key] = ent
             del de, states
+            torch.cuda.empty_cache()
+
+        # ---- prefill backward (training): SISO and MIMO rank-4, b8 L4096
+        for nm in ("siso_prefill_1p5b", "mimo4_prefill_1p5b"):
+            sb = WORKLOADS[nm]
+            inp = make_scan_inputs(sb, seed=10)
+            db = m3.to_device(inp, sb.io)
+            del inp
+            dyb = torch.randn(db["x"].shape, device=dev).to(db["x"].dtype)
+            bargs = (db["x"], db["Braw"], db["Craw"], db["dt"], db["A"], db["lam"], db["theta"], db["B_bias"],
+                     db["C_bias"], dyb)
+            grads = m3.scan_bwd(*bargs, eps=sb.eps)
+            shp = m3.make_shape(sb.batch, sb.seqlen, sb.nheads, sb.ngroups, sb.headdim, sb.dstate, sb.rank,
+                                sb.chunk, m3.M3_BF16, sb.eps)
+            wsb = m3.scan_bwd_workspace_bytes(shp)
+            wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            for _ in range(2):
+                m3.scan_bwd(*bargs, eps=sb.eps, grads=grads, workspace=wsp)
+            torch.cuda.synchronize()
+            reps = 5
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            evs[0].record()
+            for k in range(reps):
+                m3.scan_bwd(*bargs, eps=sb.eps, grads=grads, workspace=wsp)
+                evs[k + 1].record()
+            torch.cuda.synchronize()
+            ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(reps))[reps // 2]
+            bb = bwd_bytes(sb)
+            ent = {"tokens_per_s": round(sb.batch * sb.seqlen / (ms * 1e-3), 1), "ms": round(ms, 3),
+                   "hbm_frac": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bb,
+                   "workspace_bytes": wsb}
+            log(nm + "_backward", ent)
+            extra[nm + "_backward"] = ent
+            del db, dyb, grads, wsp
             torch.cuda.empty_cache()
 
     cpu = None

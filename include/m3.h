@@ -225,7 +225,7 @@ m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *st
  * (Proposition 4), taken term by term: masked scores, carried state, decay,
  * trapezoid weights (§3.1.3 eq. 7), rotation angles and BCNorm + bias (§3.4).
  * Computed in fp32 for io fp32 or bf16, any L; shapes as for the fp32 prefill
- * kernel (N, P <= 128, N * P <= 8192, R <= 4). shape->chunk is not used: the
+ * kernel (N, P <= 128, N * P <= 8192, R <= 4) with N and P multiples of 4. shape->chunk is not used: the
  * backward picks its own chunk (32 / R tokens), the result does not depend on it.
  * The fused projections and the output epilogue are not differentiated here
  * (M3_ERR_UNSUPPORTED when io->W_X or io->D is set or M3_FLAG_OUT_NORM is on);

@@ -205,10 +205,10 @@ m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspa
 }
 
 // Backward limits: those of the fp32 prefill kernel (the backward keeps every
-// tile of a 32-row chunk in LDS), N even.
+// tile of a 32-row chunk in LDS), and N, P multiples of 4 (16-byte row reads).
 static bool bwd_shape_ok(const m3_shape &s) {
     return s.dstate <= kGenericMaxN && s.headdim <= kGenericMaxP && s.dstate * s.headdim <= kGenericMaxNP &&
-           s.rank <= 4;
+           s.rank <= 4 && s.dstate % 4 == 0 && s.headdim % 4 == 0;
 }
 
 static ScanArgs bwd_args(const m3_shape &s, const m3_scan_io *io) {

@@ -27,8 +27,8 @@
 // W_O SiLU(W_Z Z') in a table, so each lane contracts its R partial sums with
 // the gate before the one reduction over the row's lanes.
 //
-// Output epilogue: the skip D[h] x (the D term of y = C h + D x) is added by the
-// lane that stores a value. With the grouped output RMSNorm the output vectors
+// Output epilogue: the skip D[h] x (the D term of y = C h + D x) starts the
+// partial sums of each row's first lane. With the grouped output RMSNorm the output vectors
 // (each rank row of y, or Y before the gate, or O' after it) are staged in LDS
 // until their mean square over P is known, and written after one more barrier.
 #include <type_traits>
@@ -166,7 +166,7 @@ __device__ __forceinline__ typename StateT<BS, V>::type pack_state(const float *
     }
 }
 
-template <bool BF16, bool BS, int N, int R, int V, int KBATCH>
+template <bool BF16, bool BS, int N, int R, int V, int KBATCH, bool ONORM>
 __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(DecodeArgs a) {
     constexpr int HALF = N / 2;
     constexpr int NQ = HALF / V;            // lanes that share one row p
@@ -276,8 +276,8 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     const float dsk = a.D ? a.D[hi] : 0.f;
     // with the output norm, what is staged: each rank row of y (or of Y, before the
     // gate), or the gated and contracted O' (after the gate)
-    const bool stage_ranks = a.onorm && !(a.fused && a.norm_after_gate);
-    const bool stage_o = a.onorm && a.fused && a.norm_after_gate;
+    const bool stage_ranks = ONORM && !(a.fused && a.norm_after_gate);
+    const bool stage_o = ONORM && a.fused && a.norm_after_gate;
     const float alpha = expf(d * Av);
     const float beta = a.has_prev ? (1.0f - lm) * d * alpha : 0.f;
     const float gamma = lm * d;
@@ -335,9 +335,11 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
             float l[V], h[V];
             unpack_state<BS, V>(lo[k], l);
             unpack_state<BS, V>(hiv[k], h);
+            // the skip term D x enters the sum of the row's first lane, so every
+            // reduction below carries it
             float yacc[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) yacc[r] = 0.f;
+            for (int r = 0; r < R; ++r) yacc[r] = (q == 0) ? dsk * xv[r] : 0.f;
 #pragma unroll
             for (int c = 0; c < V; ++c) {
                 float u = alpha * l[c], v = alpha * h[c];
@@ -363,17 +365,14 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const float v = group_sum<NQ>(yacc[r]);
-                    if (q == 0) sy[r * P + p] = v + dsk * xv[r];
+                    if (q == 0) sy[r * P + p] = v;
                 }
             } else if (a.fused) {
                 // the gate is linear in y: contract the ranks first, then reduce once
-                float v = 0.f, vs = 0.f;
+                float v = 0.f;
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    v += sgt[p * R + r] * yacc[r];
-                    vs += sgt[p * R + r] * xv[r];
-                }
-                v = group_sum<NQ>(v) + dsk * vs;
+                for (int r = 0; r < R; ++r) v += sgt[p * R + r] * yacc[r];
+                v = group_sum<NQ>(v);
                 if (q == 0) {
                     if (stage_o)
                         sy[p] = v;
@@ -396,19 +395,19 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
                 if constexpr (LR == 2) scatter_step<LNQ - 2, 1>(vals, q);
                 const float v = tree_sum_low<LNQ - LR>(vals[0]);
                 const int rk = q / (NQ / R);
-                if (q % (NQ / R) == 0) st_io<BF16>(a.y, ybase + rk * P + p, v + dsk * sx[p * R + rk]);
+                if (q % (NQ / R) == 0) st_io<BF16>(a.y, ybase + rk * P + p, v);
             } else {
 #pragma unroll
                 for (int r = 0; r < R; ++r) yacc[r] = group_sum<NQ>(yacc[r]);
                 if (q == 0) {
 #pragma unroll
-                    for (int r = 0; r < R; ++r) st_io<BF16>(a.y, ybase + r * P + p, yacc[r] + dsk * xv[r]);
+                    for (int r = 0; r < R; ++r) st_io<BF16>(a.y, ybase + r * P + p, yacc[r]);
                 }
             }
         }
     }
 
-    if (a.onorm) {
+    if constexpr (ONORM) {
         // grouped output RMSNorm over the P channels of each staged vector
         __syncthreads();
         const int nvec = stage_o ? 1 : R;
@@ -439,19 +438,24 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     }
 }
 
-template <bool BF16, bool BS, int N>
-hipError_t launch_n(const DecodeArgs &a, hipStream_t s) {
+template <bool BF16, bool BS, int N, bool ONORM>
+hipError_t launch_nn(const DecodeArgs &a, hipStream_t s) {
     const size_t smem = sizeof(float) * (5 * a.R * N + 3 * N + 4 * a.R + (a.fused ? 3 : 2) * a.R * a.P +
                                          (a.onorm ? a.R * a.P + a.R : 0));
     dim3 grid((unsigned)(a.b * a.H)), block(kThreads);
     switch (a.R) {
-        case 1: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 1, 4, 2>), grid, block, smem, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 2, 2, 4>), grid, block, smem, s, a); break;
-        case 3: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 3, 2, 4>), grid, block, smem, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 4, 2, 4>), grid, block, smem, s, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 1, 4, 2, ONORM>), grid, block, smem, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 2, 2, 4, ONORM>), grid, block, smem, s, a); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 3, 2, 4, ONORM>), grid, block, smem, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<BF16, BS, N, 4, 2, 4, ONORM>), grid, block, smem, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <bool BF16, bool BS, int N>
+hipError_t launch_n(const DecodeArgs &a, hipStream_t s) {
+    return a.onorm ? launch_nn<BF16, BS, N, true>(a, s) : launch_nn<BF16, BS, N, false>(a, s);
 }
 
 template <bool BF16, bool BS>

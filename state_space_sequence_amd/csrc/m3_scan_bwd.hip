@@ -36,12 +36,30 @@ namespace m3i {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kChainThreads = 512;  // chain kernel: 8 waves, one workgroup per CU (LDS-bound)
 constexpr int kRowsB = 32;  // rows (token, rank) per backward chunk
 constexpr float kInv2Pi = 0.15915494309189535f;
 
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// x / d for a runtime divisor by one multiply-high: with m = floor(2^32 / d) + 1,
+// floor(x m / 2^32) = floor(x / d) whenever x < 2^16 and d < 2^16 (the error term
+// x (m d - 2^32) / (d 2^32) stays below 1/d). Every item index here is below 2^16.
+struct FDiv {
+    uint32_t d;
+    uint64_t m;
+    __device__ explicit FDiv(uint32_t dd) : d(dd), m((1ull << 32) / dd + 1) {}
+    __device__ int q(int x) const { return (int)(((uint64_t)(uint32_t)x * m) >> 32); }
+};
+__device__ __forceinline__ f4 ld4(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+__device__ __forceinline__ float dot4(f4 a, f4 b, float c) {
+    return __builtin_fmaf(a[3], b[3], __builtin_fmaf(a[2], b[2], __builtin_fmaf(a[1], b[1], __builtin_fmaf(a[0], b[0], c))));
+}
+
 struct BwdDims {
     int N, P, R, half, Cb, T, nch, npb;
-    int64_t slot;  // floats per checkpoint slot: N*P state + N/2 angle carry
+    int NS, PS, HS;  // padded LDS row strides (one extra float: strided walks hit distinct banks)
+    int64_t slot;    // floats per checkpoint slot: N*P state + N/2 angle carry
 };
 
 __host__ __device__ inline BwdDims bwd_dims(int64_t L, int64_t N, int64_t P, int64_t R) {
@@ -53,30 +71,33 @@ __host__ __device__ inline BwdDims bwd_dims(int64_t L, int64_t N, int64_t P, int
     d.Cb = kRowsB / (int)R > 0 ? kRowsB / (int)R : 1;
     d.T = d.Cb * (int)R;
     d.nch = (int)((L + d.Cb - 1) / d.Cb);
-    d.npb = (int)((P + 7) / 8);
+    d.npb = (int)(P / 4);  // dx items: 4 columns each (P % 4 == 0)
+    d.NS = d.N + 4;  // rows stay 16-byte aligned for vector reads and shift by 4 banks
+    d.PS = d.P + 4;
+    d.HS = d.half + 1;
     d.slot = N * P + N / 2;
     return d;
 }
 
-// floats of the aliased region (state copy in the forward sweep; scores, mask
-// and per-token angle tables in the reverse sweep)
+// floats of the aliased region (the state in the forward sweep; scores, mask and
+// per-token angle tables in the reverse sweep)
 __host__ __device__ inline int alias_floats(const BwdDims &d) {
-    const int a = d.N * d.P;
-    const int b = 2 * d.T * d.T + 2 * d.Cb * d.Cb + 2 * d.Cb * d.half;
-    return a > b ? a : b;
+    const int a = d.N * d.PS;
+    const int b = 2 * d.T * d.T + 2 * d.Cb * d.Cb + 2 * d.Cb * d.HS;
+    return ((a > b ? a : b) + 3) / 4 * 4;  // keeps the tiles after it 16-byte aligned
 }
 
 __host__ __device__ inline size_t chain_smem_floats(const BwdDims &d) {
-    return (size_t)d.N * d.P           // dS
+    return (size_t)d.N * d.PS          // dS
            + alias_floats(d)           // U
-           + 3 * (size_t)d.T * d.N     // B_bar, C_bar, dCoff
-           + 2 * (size_t)d.T * d.P     // X, dY
-           + (size_t)d.Cb * d.half     // Phi
+           + 3 * (size_t)d.T * d.NS    // B_bar, C_bar, dCoff
+           + 2 * (size_t)d.T * d.PS    // X, dY
+           + 2 * (size_t)d.Cb * d.half // Phi, theta
            + (size_t)d.T * d.npb       // Q partials
-           + 8 * (size_t)d.Cb          // token scalars
+           + 14 * (size_t)(d.Cb + 1)   // token scalars
            + 2 * (size_t)d.T           // 1/rms of B, C rows
            + 2 * (size_t)d.half        // angle carry, reverse angle-gradient carry
-           + kThreads + 4;             // reduction scratch
+           + kChainThreads + 4;        // reduction scratch
 }
 
 struct BwdArgs {
@@ -94,11 +115,15 @@ struct BwdArgs {
     float *fold;  // [b,H]       gradient of the fold factor (1 - lam_0) dt_0
 };
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs ba) {
+template <bool BF16, int R>
+__global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs ba) {
     const ScanArgs &a = ba.f;
-    const BwdDims dm = bwd_dims(a.L, a.N, a.P, a.R);
-    const int N = dm.N, P = dm.P, R = dm.R, half = dm.half, Cb = dm.Cb, T = dm.T, nch = dm.nch, npb = dm.npb;
+    const BwdDims dm = bwd_dims(a.L, a.N, a.P, R);
+    constexpr int Cb = kRowsB / R, T = Cb * R;  // tokens and rows per chunk (compile-time)
+    const int N = dm.N, P = dm.P, half = dm.half, nch = dm.nch, npb = dm.npb;
+    const int NS = dm.NS, PS = dm.PS, HS = dm.HS;
+    constexpr int NT = kChainThreads;
+    const FDiv fN((uint32_t)N), fP((uint32_t)P), fH((uint32_t)half), fP4((uint32_t)(P / 4));
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x;
     const int64_t bi = bh / a.H, hi = bh % a.H;
@@ -106,168 +131,220 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs ba) {
     const int64_t L = a.L, H = a.H, G = a.G;
 
     extern __shared__ float sm[];
-    float *dS = sm;                          // [N][P] adjoint of the carried state
-    float *U = dS + N * P;                   // aliased region
-    float *Bb = U + alias_floats(dm);        // [T][N] rotated B
-    float *Cc = Bb + T * N;                  // [T][N] rotated C
-    float *dCo = Cc + T * N;                 // [T][N] dC_bar from the carried-state output term
-    float *Xs = dCo + T * N;                 // [T][P]
-    float *dYs = Xs + T * P;                 // [T][P]
-    float *Phi = dYs + T * P;                // [Cb][half] cumulative angle, revolutions
-    float *Qp = Phi + Cb * half;             // [T][npb]
-    float *lcs = Qp + T * npb;               // [Cb] chunk-local cumulative dt A
-    float *wgt = lcs + Cb;                   // [Cb] folded weight w
-    float *gam = wgt + Cb;                   // [Cb]
-    float *dtv = gam + Cb;                   // [Cb]
-    float *dcs = dtv + Cb;                   // [Cb] gradient of cs
-    float *dwv = dcs + Cb;                   // [Cb]
-    float *dgv = dwv + Cb;                   // [Cb]
-    float *dthv = dgv + Cb;                  // [Cb] angle term of d dt
-    float *rsB = dthv + Cb;                  // [T]
+    float *dS = sm;                          // [N][PS] adjoint of the carried state
+    float *U = dS + N * PS;                  // aliased region
+    float *Bb = U + alias_floats(dm);        // [T][NS] rotated B (raw rows first)
+    float *Cc = Bb + T * NS;                 // [T][NS] rotated C
+    float *dCo = Cc + T * NS;                // [T][NS] dC_bar from the carried-state output term
+    float *Xs = dCo + T * NS;                // [T][PS]
+    float *dYs = Xs + T * PS;                // [T][PS]
+    float *Phi = dYs + T * PS;               // [Cb][half] angle increments, then cumulative angle (revolutions)
+    float *thv = Phi + Cb * half;            // [Cb][half] theta of the chunk's tokens
+    float *Qp = thv + Cb * half;             // [T][npb]
+    float *dtv = Qp + T * npb;               // [Cb+1] dt (the extra one: the token after the chunk)
+    float *lamv = dtv + (Cb + 1);            // [Cb+1] lam
+    float *Av = lamv + (Cb + 1);             // [Cb+1] A
+    float *lcs = Av + (Cb + 1);              // [Cb+1] chunk-local cumulative dt A
+    float *wgt = lcs + (Cb + 1);             // [Cb+1] folded weight w
+    float *gam = wgt + (Cb + 1);             // [Cb+1]
+    float *ecs = gam + (Cb + 1);             // [Cb+1] e^{cs_t}
+    float *Ew = ecs + (Cb + 1);              // [Cb+1] e^{cs_end - cs_t} w_t
+    float *Ee = Ew + (Cb + 1);               // [Cb+1] e^{cs_end - cs_t}
+    float *dcs = Ee + (Cb + 1);              // [Cb+1] gradient of cs
+    float *dwv = dcs + (Cb + 1);             // [Cb+1]
+    float *dgv = dwv + (Cb + 1);             // [Cb+1]
+    float *dthv = dgv + (Cb + 1);            // [Cb+1] (spare)
+    float *sp2 = dthv + (Cb + 1);            // [Cb+1] (spare)
+    float *rsB = sp2 + (Cb + 1);             // [T]
     float *rsC = rsB + T;                    // [T]
     float *carry = rsC + T;                  // [half] angle before the chunk, revolutions
     float *rcar = carry + half;              // [half] suffix sum of d Phi after the chunk (radians)
-    float *red = rcar + half;                // [kThreads] reduction scratch
-    float *misc = red + kThreads;            // [4]
+    float *red = rcar + half;                // [NT] reduction scratch
+    float *misc = red + NT;                  // [4]
     // reverse-sweep views of U
     float *Sc = U;                           // [T][T] C_bar . B_bar
     float *dP = Sc + T * T;                  // [T][T] dy . x
     float *Mk = dP + T * T;                  // [Cb][Cb] mask m(t, s)
     float *dMk = Mk + Cb * Cb;               // [Cb][Cb] gradient of the mask entry
-    float *offp = dMk + Cb * Cb;             // [Cb][half] partial d cs from the output term
-    float *dPh = offp + Cb * half;           // [Cb][half] d Phi (radians), then theta * suffix
+    float *offp = dMk + Cb * Cb;             // [Cb][HS] partial d cs from the output term
+    float *dPh = offp + Cb * HS;             // [Cb][HS] d Phi (radians), then theta * suffix
+    (void)dthv;
+    (void)sp2;
 
     float *chk = ba.chk + bh * (int64_t)(nch + 1) * dm.slot;
     const float *wB = a.B_normw, *wC = a.C_normw;
 
-    // ---- per-chunk helpers ---------------------------------------------------
-    auto token_scalars = [&](int64_t c0, int nv) {
+    // ---- per-chunk staging (every global load in parallel, every serial walk in LDS)
+    // phase 1: token scalars (and the one after the chunk), raw B / C rows, x / dy rows,
+    // angle increments
+    auto stage_loads = [&](int64_t c0, int nv, bool withC) {
+        for (int t = tid; t <= Cb; t += NT) {
+            float d = 0.f, lm = 0.f, av = 0.f;
+            if (t <= nv && c0 + t < L) {
+                const int64_t o = (bi * L + c0 + t) * H + hi;
+                d = a.dt[o];
+                lm = a.lam[o];
+                av = a.A[o];
+            }
+            dtv[t] = d;
+            lamv[t] = lm;
+            Av[t] = av;
+        }
+        for (int e = tid; e < T * N; e += NT) {
+            const int rho = fN.q(e), n = e - rho * N;
+            const int t = rho / R, r = rho % R;
+            float vb = 0.f, vc = 0.f;
+            if (t < nv) {
+                const int64_t row = (((bi * L + c0 + t) * G + g) * R + r) * N;
+                vb = ld_io<BF16>(a.Braw, row + n);
+                if (withC) vc = ld_io<BF16>(a.Craw, row + n);
+            }
+            Bb[rho * NS + n] = vb;
+            if (withC) Cc[rho * NS + n] = vc;
+        }
+        for (int e = tid; e < T * P; e += NT) {
+            const int rho = fP.q(e), p = e - rho * P;
+            const int t = rho / R, r = rho % R;
+            const int64_t o = (((bi * L + c0 + t) * H + hi) * R + r) * P + p;
+            Xs[rho * PS + p] = (t < nv) ? ld_io<BF16>(a.x, o) : 0.f;
+            if (withC) dYs[rho * PS + p] = (t < nv) ? ld_io<BF16>(ba.dy, o) : 0.f;
+        }
+        for (int e = tid; e < Cb * half; e += NT) {
+            const int t = fH.q(e), i = e - t * half;
+            float v = 0.f, th = 0.f;
+            if (t < nv) {
+                const int64_t tok = bi * L + c0 + t;
+                th = a.theta[(tok * G + g) * half + i];
+                v = a.dt[tok * H + hi] * th * kInv2Pi;
+            }
+            Phi[e] = v;
+            thv[e] = th;
+        }
+    };
+    // phase 2: prefix sums (decay: one thread; angles: one thread per channel), row norms
+    // (groups of 8 lanes per row)
+    auto stage_scans = [&](int64_t c0, int nv, bool withC) {
         if (tid == 0) {
             float run = 0.f;
             for (int t = 0; t < Cb; ++t) {
                 if (t < nv) {
-                    const int64_t o = (bi * L + c0 + t) * H + hi;
-                    const float d = a.dt[o], lm = a.lam[o];
-                    run += d * a.A[o];
-                    const float look = (c0 + t + 1 < L) ? (1.0f - a.lam[o + H]) * a.dt[o + H] : 0.f;
+                    run += dtv[t] * Av[t];
+                    const float look = (c0 + t + 1 < L) ? (1.0f - lamv[t + 1]) * dtv[t + 1] : 0.f;
                     lcs[t] = run;
-                    gam[t] = lm * d;
-                    wgt[t] = lm * d + look;
-                    dtv[t] = d;
+                    gam[t] = lamv[t] * dtv[t];
+                    wgt[t] = lamv[t] * dtv[t] + look;
                 } else {
                     lcs[t] = run;
                     gam[t] = 0.f;
                     wgt[t] = 0.f;
-                    dtv[t] = 0.f;
                 }
             }
         }
-    };
-    auto angles = [&](int64_t c0, int nv) {  // needs carry
-        for (int i = tid; i < half; i += kThreads) {
+        for (int i = tid - 64; i >= 0 && i < half; i += NT) {  // threads 64.. : angle prefix
             float ph = carry[i];
             for (int t = 0; t < nv; ++t) {
-                const int64_t tok = bi * L + c0 + t;
-                ph += a.dt[tok * H + hi] * a.theta[(tok * G + g) * half + i] * kInv2Pi;
+                ph += Phi[t * half + i];
                 Phi[t * half + i] = ph;
             }
         }
-    };
-    auto row_norms = [&](int64_t c0, int nv, bool withC) {
-        for (int rho = tid; rho < T; rho += kThreads) {
-            const int t = rho / R, r = rho % R;
-            float sb = 0.f, sc = 0.f;
-            if (t < nv) {
-                const int64_t row = (((bi * L + c0 + t) * G + g) * R + r) * N;
-                for (int n = 0; n < N; ++n) {
-                    const float vb = ld_io<BF16>(a.Braw, row + n);
-                    sb += vb * vb;
-                    if (withC) {
-                        const float vc = ld_io<BF16>(a.Craw, row + n);
-                        sc += vc * vc;
-                    }
-                }
-            }
-            rsB[rho] = 1.0f / sqrtf(sb / (float)N + a.eps);
-            rsC[rho] = 1.0f / sqrtf(sc / (float)N + a.eps);
+        const int nrow = withC ? 2 * T : T;
+        for (int grp = tid / 8; grp < nrow; grp += NT / 8) {  // the 8 lanes of a group run together
+            const int lane8 = tid % 8;
+            const bool isC = grp >= T;
+            const int rho = isC ? grp - T : grp;
+            const float *row = (isC ? Cc : Bb) + rho * NS;
+            float ss = 0.f;
+            for (int n = lane8; n < N; n += 8) ss += row[n] * row[n];
+            ss = group_sum<8>(ss);
+            if (lane8 == 0) (isC ? rsC : rsB)[rho] = 1.0f / sqrtf(ss / (float)N + a.eps);
         }
     };
-    // rotated, normalised, biased rows of B (and C) and the rows of x (and dy)
-    auto rows = [&](int64_t c0, int nv, bool withC) {
-        for (int e = tid; e < T * half; e += kThreads) {
-            const int rho = e / half, i = e % half;
+    // phase 3: exponentials of the decay; normalise, bias and rotate B / C in place
+    auto stage_rows = [&](int nv, bool withC) {
+        const float cse = lcs[nv - 1];
+        for (int t = tid; t < Cb; t += NT) {
+            ecs[t] = expf(lcs[t]);
+            Ee[t] = (t < nv) ? expf(cse - lcs[t]) : 0.f;
+            Ew[t] = Ee[t] * wgt[t];
+        }
+        for (int e = tid; e < T * half; e += NT) {
+            const int rho = fH.q(e), i = e - rho * half;
             const int t = rho / R, r = rho % R;
             float bl = 0.f, bhv = 0.f, cl = 0.f, chv = 0.f;
             if (t < nv) {
-                const int64_t row = (((bi * L + c0 + t) * G + g) * R + r) * N;
                 const float *bb = a.B_bias + (hi * R + r) * N;
                 float sn, cs;
                 sincospif(2.f * Phi[t * half + i], &sn, &cs);
-                const float B0 = ld_io<BF16>(a.Braw, row + i) * rsB[rho] * (wB ? wB[i] : 1.f) + bb[i];
-                const float B1 =
-                    ld_io<BF16>(a.Braw, row + i + half) * rsB[rho] * (wB ? wB[i + half] : 1.f) + bb[i + half];
+                const float B0 = Bb[rho * NS + i] * rsB[rho] * (wB ? wB[i] : 1.f) + bb[i];
+                const float B1 = Bb[rho * NS + i + half] * rsB[rho] * (wB ? wB[i + half] : 1.f) + bb[i + half];
                 bl = cs * B0 + sn * B1;
                 bhv = -sn * B0 + cs * B1;
                 if (withC) {
                     const float *cb = a.C_bias + (hi * R + r) * N;
-                    const float C0 = ld_io<BF16>(a.Craw, row + i) * rsC[rho] * (wC ? wC[i] : 1.f) + cb[i];
-                    const float C1 =
-                        ld_io<BF16>(a.Craw, row + i + half) * rsC[rho] * (wC ? wC[i + half] : 1.f) + cb[i + half];
+                    const float C0 = Cc[rho * NS + i] * rsC[rho] * (wC ? wC[i] : 1.f) + cb[i];
+                    const float C1 = Cc[rho * NS + i + half] * rsC[rho] * (wC ? wC[i + half] : 1.f) + cb[i + half];
                     cl = cs * C0 + sn * C1;
                     chv = -sn * C0 + cs * C1;
                 }
             }
-            Bb[rho * N + i] = bl;
-            Bb[rho * N + i + half] = bhv;
+            Bb[rho * NS + i] = bl;
+            Bb[rho * NS + i + half] = bhv;
             if (withC) {
-                Cc[rho * N + i] = cl;
-                Cc[rho * N + i + half] = chv;
+                Cc[rho * NS + i] = cl;
+                Cc[rho * NS + i + half] = chv;
             }
         }
-        for (int e = tid; e < T * P; e += kThreads) {
-            const int rho = e / P, p = e % P;
-            const int t = rho / R, r = rho % R;
-            const int64_t o = (((bi * L + c0 + t) * H + hi) * R + r) * P + p;
-            Xs[e] = (t < nv) ? ld_io<BF16>(a.x, o) : 0.f;
-            if (withC) dYs[e] = (t < nv) ? ld_io<BF16>(ba.dy, o) : 0.f;
-        }
+    };
+    auto stage_chunk = [&](int64_t c0, int nv, bool withC) {
+        stage_loads(c0, nv, withC);
+        __syncthreads();
+        stage_scans(c0, nv, withC);
+        __syncthreads();
+        stage_rows(nv, withC);
+        __syncthreads();
     };
 
     // ---- initial state: h0 (physical = rotated frame before token 0) + fold
-    float *S = U;  // forward-sweep state lives in the aliased region
-    for (int e = tid; e < N * P; e += kThreads) {
+    float *S = U;  // forward-sweep state lives in the aliased region, [N][PS]
+    for (int e = tid; e < N * P; e += NT) {
         const int n = e / P, p = e % P;
-        S[e] = a.h0 ? a.h0[(bh * P + p) * N + n] : 0.f;
+        S[n * PS + p] = a.h0 ? a.h0[(bh * P + p) * N + n] : 0.f;
     }
-    for (int i = tid; i < half; i += kThreads) carry[i] = 0.f;
+    for (int i = tid; i < half; i += NT) carry[i] = 0.f;
     const float fold_f = (a.has_prev && L > 0) ? (1.0f - a.lam[bi * L * H + hi]) * a.dt[bi * L * H + hi] : 0.f;
-    // previous token's normalised, biased B rows ([R][N], in the dCo region) and x rows ([R][P], in Xs)
+    // previous token's normalised, biased B rows ([R][NS], in dCo) and x rows ([R][PS], in Xs)
     auto prev_rows = [&]() {
-        for (int r = tid; r < R; r += kThreads) {
-            const int64_t row = ((bi * G + g) * R + r) * N;
-            float ss = 0.f;
-            for (int n = 0; n < N; ++n) {
-                const float v = ld_io<BF16>(a.Braw_prev, row + n);
-                ss += v * v;
-            }
-            rsB[r] = 1.0f / sqrtf(ss / (float)N + a.eps);
+        for (int e = tid; e < R * N; e += NT) {
+            const int r = e / N, n = e % N;
+            dCo[r * NS + n] = ld_io<BF16>(a.Braw_prev, ((bi * G + g) * R + r) * N + n);
+        }
+        for (int e = tid; e < R * P; e += NT) {
+            const int r = e / P, p = e % P;
+            Xs[r * PS + p] = ld_io<BF16>(a.x_prev, ((bi * H + hi) * R + r) * P + p);
         }
         __syncthreads();
-        for (int e = tid; e < R * N; e += kThreads) {
-            const int r = e / N, n = e % N;
-            dCo[e] = ld_io<BF16>(a.Braw_prev, ((bi * G + g) * R + r) * N + n) * rsB[r] * (wB ? wB[n] : 1.f) +
-                     a.B_bias[(hi * R + r) * N + n];
+        for (int grp = tid / 8; grp < R; grp += NT / 8) {
+            const int lane8 = tid % 8;
+            float ss = 0.f;
+            for (int n = lane8; n < N; n += 8) ss += dCo[grp * NS + n] * dCo[grp * NS + n];
+            ss = group_sum<8>(ss);
+            if (lane8 == 0) rsB[grp] = 1.0f / sqrtf(ss / (float)N + a.eps);
         }
-        for (int e = tid; e < R * P; e += kThreads) Xs[e] = ld_io<BF16>(a.x_prev, ((bi * H + hi) * R) * P + e);
+        __syncthreads();
+        for (int e = tid; e < R * N; e += NT) {
+            const int r = e / N, n = e % N;
+            dCo[r * NS + n] = dCo[r * NS + n] * rsB[r] * (wB ? wB[n] : 1.f) + a.B_bias[(hi * R + r) * N + n];
+        }
         __syncthreads();
     };
     if (a.has_prev && L > 0) {
+        __syncthreads();
         prev_rows();
-        for (int e = tid; e < N * P; e += kThreads) {
+        for (int e = tid; e < N * P; e += NT) {
             const int n = e / P, p = e % P;
             float acc = 0.f;
-            for (int r = 0; r < R; ++r) acc += dCo[r * N + n] * Xs[r * P + p];
-            S[e] += fold_f * acc;
+            for (int r = 0; r < R; ++r) acc += dCo[r * NS + n] * Xs[r * PS + p];
+            S[n * PS + p] += fold_f * acc;
         }
     }
     __syncthreads();
@@ -277,36 +354,30 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs ba) {
         const int64_t c0 = (int64_t)k * Cb;
         const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
         float *slot = chk + (int64_t)k * dm.slot;
-        for (int e = tid; e < N * P; e += kThreads) slot[e] = S[e];
-        for (int i = tid; i < half; i += kThreads) slot[N * P + i] = carry[i];
-        token_scalars(c0, nv);
-        angles(c0, nv);
-        row_norms(c0, nv, false);
-        __syncthreads();
-        rows(c0, nv, false);
-        __syncthreads();
-        const float cse = lcs[nv - 1];
-        const float dec = expf(cse);
-        for (int e = tid; e < N * P; e += kThreads) {
-            const int n = e / P, p = e % P;
-            float acc = 0.f;
-            for (int sg = 0; sg < T; ++sg) {
-                const int s = sg / R;
-                acc += Bb[sg * N + n] * (expf(cse - lcs[s]) * wgt[s]) * Xs[sg * P + p];
-            }
-            S[e] = dec * S[e] + acc;
+        for (int e = tid; e < N * P; e += NT) {
+            const int n = fP.q(e);
+            slot[e] = S[n * PS + e - n * P];
         }
-        for (int i = tid; i < half; i += kThreads) carry[i] = __builtin_amdgcn_fractf(Phi[(nv - 1) * half + i]);
+        for (int i = tid; i < half; i += NT) slot[N * P + i] = carry[i];
+        stage_chunk(c0, nv, false);
+        const float dec = expf(lcs[nv - 1]);
+        for (int e = tid; e < N * (P / 4); e += NT) {
+            const int n = fP4.q(e), p = 4 * (e - n * (P / 4));
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int sg = 0; sg < nv * R; ++sg) acc += (Bb[sg * NS + n] * Ew[sg / R]) * ld4(&Xs[sg * PS + p]);
+            *reinterpret_cast<f4 *>(&S[n * PS + p]) = dec * ld4(&S[n * PS + p]) + acc;
+        }
+        for (int i = tid; i < half; i += NT) carry[i] = __builtin_amdgcn_fractf(Phi[(nv - 1) * half + i]);
         __syncthreads();
     }
     {
         float *slot = chk + (int64_t)nch * dm.slot;
-        for (int e = tid; e < N * P; e += kThreads) slot[e] = S[e];
-        for (int i = tid; i < half; i += kThreads) slot[N * P + i] = carry[i];
+        for (int e = tid; e < N * P; e += NT) slot[e] = S[(e / P) * PS + e % P];
+        for (int i = tid; i < half; i += NT) slot[N * P + i] = carry[i];
     }
 
-    // ---- reverse sweep: dS = R(-Phi_end) dh_final; angle gradient of h_final
-    for (int e = tid; e < half * P; e += kThreads) {
+    // ---- reverse sweep: dS = R(-Phi_end) dh_final
+    for (int e = tid; e < half * P; e += NT) {
         const int i = e / P, p = e % P;
         float dlo = 0.f, dhi = 0.f;
         if (ba.dh_final) {
@@ -316,19 +387,19 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs ba) {
             dlo = cs * hl + sn * hh;
             dhi = -sn * hl + cs * hh;
         }
-        dS[i * P + p] = dlo;
-        dS[(i + half) * P + p] = dhi;
+        dS[i * PS + p] = dlo;
+        dS[(i + half) * PS + p] = dhi;
     }
     // d Phi_end[i] = sum_p (-dh_lo h_hi + dh_hi h_lo) with h = h_final = R(Phi_end) S_final:
     // one thread per channel pair, fixed order
-    for (int i = tid; i < half; i += kThreads) {
+    for (int i = tid; i < half; i += NT) {
         float rg = 0.f;
         if (ba.dh_final) {
             float sn, cs;
             sincospif(2.f * carry[i], &sn, &cs);
             for (int p = 0; p < P; ++p) {
                 const float hl = ba.dh_final[(bh * P + p) * N + i], hh = ba.dh_final[(bh * P + p) * N + i + half];
-                const float su = S[i * P + p], sv = S[(i + half) * P + p];
+                const float su = S[i * PS + p], sv = S[(i + half) * PS + p];
                 rg += -hl * (sn * su + cs * sv) + hh * (cs * su - sn * sv);
             }
         }
@@ -341,54 +412,54 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs ba) {
         const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
         const float *slot = chk + (int64_t)k * dm.slot;
         const float *slot1 = chk + (int64_t)(k + 1) * dm.slot;
-        for (int i = tid; i < half; i += kThreads) carry[i] = slot[N * P + i];
-        token_scalars(c0, nv);
-        row_norms(c0, nv, true);
-        __syncthreads();
-        angles(c0, nv);
-        __syncthreads();
-        rows(c0, nv, true);
-        for (int e = tid; e < N * P; e += kThreads) U[e] = slot[e];
-        __syncthreads();
-
+        for (int i = tid; i < half; i += NT) carry[i] = slot[N * P + i];
+        for (int e = tid; e < N * P; e += NT) {
+            const int n = fP.q(e);
+            U[n * PS + e - n * P] = slot[e];
+        }
+        stage_chunk(c0, nv, true);
         const float cse = lcs[nv - 1];
+
         // P2: dC_bar from the carried-state output term; <S_out, dS> partials
-        for (int e = tid; e < T * N; e += kThreads) {
-            const int rho = e / N, n = e % N;
+        for (int e = tid; e < T * N; e += NT) {
+            const int rho = fN.q(e), n = e - rho * N;
             const int t = rho / R;
             float acc = 0.f;
             if (t < nv) {
-                for (int p = 0; p < P; ++p) acc += U[n * P + p] * dYs[rho * P + p];
-                acc *= expf(lcs[t]);
+                for (int p = 0; p < P; p += 4) acc = dot4(ld4(&U[n * PS + p]), ld4(&dYs[rho * PS + p]), acc);
+                acc *= ecs[t];
             }
-            dCo[e] = acc;
+            dCo[rho * NS + n] = acc;
         }
         {
             float part = 0.f;
-            for (int e = tid; e < N * P; e += kThreads) part += slot1[e] * dS[e];
+            for (int e = tid; e < N * P; e += NT) {
+                const int n = fP.q(e);
+                part += slot1[e] * dS[n * PS + e - n * P];
+            }
             red[tid] = part;
         }
         __syncthreads();
         // P3: scores and dy . x (U is free now)
-        for (int e = tid; e < T * T; e += kThreads) {
+        for (int e = tid; e < T * T; e += NT) {
             const int rho = e / T, sg = e % T;
             const int t = rho / R, s = sg / R;
             float sc = 0.f, dp = 0.f;
             if (s <= t && t < nv) {
-                for (int n = 0; n < N; ++n) sc += Cc[rho * N + n] * Bb[sg * N + n];
-                for (int p = 0; p < P; ++p) dp += dYs[rho * P + p] * Xs[sg * P + p];
+                for (int n = 0; n < N; n += 4) sc = dot4(ld4(&Cc[rho * NS + n]), ld4(&Bb[sg * NS + n]), sc);
+                for (int p = 0; p < P; p += 4) dp = dot4(ld4(&dYs[rho * PS + p]), ld4(&Xs[sg * PS + p]), dp);
             }
             Sc[e] = sc;
             dP[e] = dp;
         }
         if (tid == 0) {
             float sod = 0.f;
-            for (int j = 0; j < kThreads; ++j) sod += red[j];
+            for (int j = 0; j < NT; ++j) sod += red[j];
             misc[0] = sod;
         }
         __syncthreads();
         // P4: mask entries and their gradients per token pair
-        for (int e = tid; e < Cb * Cb; e += kThreads) {
+        for (int e = tid; e < Cb * Cb; e += NT) {
             const int t = e / Cb, s = e % Cb;
             float m = 0.f, dmv = 0.f;
             if (s <= t && t < nv) {
@@ -403,60 +474,70 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs ba) {
             dMk[e] = dmv;
         }
         __syncthreads();
+        // fold the mask into the tiles: Sc <- m o Sc (= P), dP <- m o dP (= d S_bar)
+        for (int e = tid; e < T * T; e += NT) {
+            const float m = Mk[(e / T / R) * Cb + (e % T) / R];
+            Sc[e] *= m;
+            dP[e] *= m;
+        }
+        __syncthreads();
         // P5: dx rows (items (sigma, block of 8 p)) and per (token, pair) items
         const int nD = T * npb;
-        for (int e = tid; e < nD + Cb * half; e += kThreads) {
+        for (int e = tid; e < nD + Cb * half; e += NT) {
             if (e < nD) {
-                const int sg = e / npb, pb = e % npb;
+                const int sg = fP4.q(e), pb = e - sg * npb;  // npb = P / 4
                 const int s = sg / R;
                 if (s >= nv) {
                     Qp[sg * npb + pb] = 0.f;
                     continue;
                 }
-                const float Es = expf(cse - lcs[s]) * wgt[s];
-                float q = 0.f;
-                const int p1 = (8 * pb + 8 < P) ? 8 * pb + 8 : P;
-                for (int p = 8 * pb; p < p1; ++p) {
-                    float intra = 0.f;
-                    for (int rho = s * R; rho < nv * R; ++rho) intra += Mk[(rho / R) * Cb + s] * Sc[rho * T + sg] * dYs[rho * P + p];
-                    float st = 0.f;
-                    for (int n = 0; n < N; ++n) st += dS[n * P + p] * Bb[sg * N + n];
-                    q += Xs[sg * P + p] * st;
-                    ba.dx[(((bi * L + c0 + s) * H + hi) * R + sg % R) * P + p] = intra + Es * st;
-                }
-                Qp[sg * npb + pb] = q;
+                const float Es = Ew[s];
+                const int p0 = 4 * pb;  // 4 columns per item
+                f4 intra = {0.f, 0.f, 0.f, 0.f}, st = {0.f, 0.f, 0.f, 0.f};
+                for (int rho = s * R; rho < nv * R; ++rho)
+                    intra += Sc[rho * T + sg] * ld4(&dYs[rho * PS + p0]);
+                for (int n = 0; n < N; ++n) st += Bb[sg * NS + n] * ld4(&dS[n * PS + p0]);
+                const f4 xv = ld4(&Xs[sg * PS + p0]);
+                Qp[sg * npb + pb] = dot4(xv, st, 0.f);
+                float *dxo = ba.dx + (((bi * L + c0 + s) * H + hi) * R + sg % R) * P + p0;
+                const f4 dxv = intra + Es * st;
+                dxo[0] = dxv[0];
+                dxo[1] = dxv[1];
+                dxo[2] = dxv[2];
+                dxo[3] = dxv[3];
             } else {
                 const int e2 = e - nD;
-                const int t = e2 / half, i = e2 % half;
+                const int t = fH.q(e2), i = e2 - t * half;
                 float dphi = 0.f, off = 0.f;
                 if (t < nv) {
-                    const float Et = expf(cse - lcs[t]) * wgt[t];
+                    const float Et = Ew[t];
                     float sn, cs;
                     sincospif(2.f * Phi[t * half + i], &sn, &cs);
                     for (int r = 0; r < R; ++r) {
                         const int rho = t * R + r;
-                        float dcl = dCo[rho * N + i], dch = dCo[rho * N + i + half];
-                        off += Cc[rho * N + i] * dcl + Cc[rho * N + i + half] * dch;
+                        float dcl = dCo[rho * NS + i], dch = dCo[rho * NS + i + half];
+                        off += Cc[rho * NS + i] * dcl + Cc[rho * NS + i + half] * dch;
                         for (int sg = 0; sg < (t + 1) * R; ++sg) {
-                            const float f = Mk[t * Cb + sg / R] * dP[rho * T + sg];
-                            dcl += f * Bb[sg * N + i];
-                            dch += f * Bb[sg * N + i + half];
+                            const float f = dP[rho * T + sg];
+                            dcl += f * Bb[sg * NS + i];
+                            dch += f * Bb[sg * NS + i + half];
                         }
                         float dbl = 0.f, dbh = 0.f;
                         for (int r2 = t * R; r2 < nv * R; ++r2) {
-                            const float f = Mk[(r2 / R) * Cb + t] * dP[r2 * T + rho];
-                            dbl += f * Cc[r2 * N + i];
-                            dbh += f * Cc[r2 * N + i + half];
+                            const float f = dP[r2 * T + rho];
+                            dbl += f * Cc[r2 * NS + i];
+                            dbh += f * Cc[r2 * NS + i + half];
                         }
                         float sl = 0.f, sh = 0.f;
-                        for (int p = 0; p < P; ++p) {
-                            sl += dS[i * P + p] * Xs[rho * P + p];
-                            sh += dS[(i + half) * P + p] * Xs[rho * P + p];
+                        for (int p = 0; p < P; p += 4) {
+                            const f4 xv = ld4(&Xs[rho * PS + p]);
+                            sl = dot4(ld4(&dS[i * PS + p]), xv, sl);
+                            sh = dot4(ld4(&dS[(i + half) * PS + p]), xv, sh);
                         }
                         dbl += Et * sl;
                         dbh += Et * sh;
-                        dphi += dbl * Bb[rho * N + i + half] - dbh * Bb[rho * N + i] + dcl * Cc[rho * N + i + half] -
-                                dch * Cc[rho * N + i];
+                        dphi += dbl * Bb[rho * NS + i + half] - dbh * Bb[rho * NS + i] +
+                                dcl * Cc[rho * NS + i + half] - dch * Cc[rho * NS + i];
                         // back to the physical frame: d B = R(Phi) d B_bar
                         const int64_t o = (((bi * L + c0 + t) * H + hi) * R + r) * N;
                         ba.gB[o + i] = cs * dbl - sn * dbh;
@@ -465,13 +546,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs ba) {
                         ba.gC[o + i + half] = sn * dcl + cs * dch;
                     }
                 }
-                offp[t * half + i] = off;
-                dPh[t * half + i] = dphi;
+                offp[t * HS + i] = off;
+                dPh[t * HS + i] = dphi;
             }
         }
         __syncthreads();
         // P6: per-token scalar gradients; suffix sums of d Phi per channel
-        for (int j = tid; j < Cb + half; j += kThreads) {
+        for (int j = tid; j < Cb + half; j += NT) {
             if (j < Cb) {
                 const int t = j;
                 float dc = 0.f, dw = 0.f, dg = 0.f;
@@ -479,15 +560,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs ba) {
                     float Qt = 0.f;
                     for (int r = 0; r < R; ++r)
                         for (int pb = 0; pb < npb; ++pb) Qt += Qp[(t * R + r) * npb + pb];
-                    for (int i = 0; i < half; ++i) dc += offp[t * half + i];
+                    for (int i = 0; i < half; ++i) dc += offp[t * HS + i];
                     for (int s = 0; s < t; ++s) dc += dMk[t * Cb + s] * Mk[t * Cb + s];
                     for (int t2 = t + 1; t2 < nv; ++t2) {
                         dc -= dMk[t2 * Cb + t] * Mk[t2 * Cb + t];
                         dw += dMk[t2 * Cb + t] * expf(lcs[t2] - lcs[t]);
                     }
-                    const float Et = expf(cse - lcs[t]);
-                    dc -= Et * wgt[t] * Qt;
-                    dw += Et * Qt;
+                    dc -= Ew[t] * Qt;
+                    dw += Ee[t] * Qt;
                     if (t == nv - 1) dc += misc[0];
                     dg = dMk[t * Cb + t];
                 }
@@ -498,21 +578,21 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs ba) {
                 const int i = j - Cb;
                 float rc = rcar[i];
                 for (int t = nv - 1; t >= 0; --t) {
-                    rc += dPh[t * half + i];
+                    rc += dPh[t * HS + i];
                     const int64_t tok = bi * L + c0 + t;
                     ba.gth[(tok * H + hi) * half + i] = dtv[t] * rc;
-                    dPh[t * half + i] = a.theta[(tok * G + g) * half + i] * rc;
+                    dPh[t * HS + i] = thv[t * half + i] * rc;
                 }
                 rcar[i] = rc;
             }
         }
         __syncthreads();
         // P7: token records (suffix sums of d cs give d(dt A)); dS back to the chunk start
-        for (int t = tid; t < nv; t += kThreads) {
+        for (int t = tid; t < nv; t += NT) {
             float da = 0.f;
             for (int t2 = t; t2 < nv; ++t2) da += dcs[t2];
             float dth = 0.f;
-            for (int i = 0; i < half; ++i) dth += dPh[t * half + i];
+            for (int i = 0; i < half; ++i) dth += dPh[t * HS + i];
             float *rec = ba.tok + ((bi * L + c0 + t) * H + hi) * 4;
             rec[0] = da;
             rec[1] = dwv[t];
@@ -520,49 +600,49 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BwdArgs ba) {
             rec[3] = dth;
         }
         const float dec = expf(cse);
-        for (int e = tid; e < N * P; e += kThreads) {
-            const int n = e / P, p = e % P;
-            float acc = 0.f;
-            for (int rho = 0; rho < nv * R; ++rho) acc += expf(lcs[rho / R]) * Cc[rho * N + n] * dYs[rho * P + p];
-            dS[e] = dec * dS[e] + acc;
+        for (int e = tid; e < N * (P / 4); e += NT) {
+            const int n = fP4.q(e), p = 4 * (e - n * (P / 4));
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int rho = 0; rho < nv * R; ++rho) acc += (ecs[rho / R] * Cc[rho * NS + n]) * ld4(&dYs[rho * PS + p]);
+            *reinterpret_cast<f4 *>(&dS[n * PS + p]) = dec * ld4(&dS[n * PS + p]) + acc;
         }
         __syncthreads();
     }
 
     // ---- chain start: dh0 and the previous token's fold
     if (ba.dh0) {
-        for (int e = tid; e < N * P; e += kThreads) {
+        for (int e = tid; e < N * P; e += NT) {
             const int p = e / N, n = e % N;
-            ba.dh0[(bh * P + p) * N + n] = dS[n * P + p];
+            ba.dh0[(bh * P + p) * N + n] = dS[n * PS + p];
         }
     }
     if (a.has_prev && L > 0) {
         prev_rows();  // dCo <- B_{-1} rows, Xs <- x_{-1} rows
-        for (int e = tid; e < R * N; e += kThreads) {
+        for (int e = tid; e < R * N; e += NT) {
             const int r = e / N, n = e % N;
             float acc = 0.f;
-            for (int p = 0; p < P; ++p) acc += dS[n * P + p] * Xs[r * P + p];
+            for (int p = 0; p < P; ++p) acc += dS[n * PS + p] * Xs[r * PS + p];
             ba.gBp[(bh * R + r) * N + n] = fold_f * acc;
         }
-        for (int e = tid; e < R * P; e += kThreads) {
+        for (int e = tid; e < R * P; e += NT) {
             const int r = e / P, p = e % P;
             float acc = 0.f;
-            for (int n = 0; n < N; ++n) acc += dS[n * P + p] * dCo[r * N + n];
+            for (int n = 0; n < N; ++n) acc += dS[n * PS + p] * dCo[r * NS + n];
             ba.dx_prev[(bh * R + r) * P + p] = fold_f * acc;
         }
         // d f = <dS, sum_r B_{-1}[r] x_{-1}[r]^T>
         float part = 0.f;
-        for (int e = tid; e < N * P; e += kThreads) {
+        for (int e = tid; e < N * P; e += NT) {
             const int n = e / P, p = e % P;
             float v = 0.f;
-            for (int r = 0; r < R; ++r) v += dCo[r * N + n] * Xs[r * P + p];
-            part += dS[e] * v;
+            for (int r = 0; r < R; ++r) v += dCo[r * NS + n] * Xs[r * PS + p];
+            part += dS[n * PS + p] * v;
         }
         red[tid] = part;
         __syncthreads();
         if (tid == 0) {
             float s = 0.f;
-            for (int j = 0; j < kThreads; ++j) s += red[j];
+            for (int j = 0; j < NT; ++j) s += red[j];
             ba.fold[bh] = s;
         }
     }
@@ -726,6 +806,18 @@ __global__ __launch_bounds__(kThreads) void bwd_token_kernel(BwdArgs ba, float *
     }
 }
 
+template <int R>
+hipError_t launch_chain(const BwdArgs &ba, int64_t chains, size_t smem, hipStream_t st) {
+    const void *fn = ba.f.bf16 ? (const void *)bwd_chain_kernel<true, R> : (const void *)bwd_chain_kernel<false, R>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    if (ba.f.bf16)
+        hipLaunchKernelGGL((bwd_chain_kernel<true, R>), dim3((unsigned)chains), dim3(kChainThreads), smem, st, ba);
+    else
+        hipLaunchKernelGGL((bwd_chain_kernel<false, R>), dim3((unsigned)chains), dim3(kChainThreads), smem, st, ba);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t scan_bwd_workspace_bytes(const ScanArgs &a, int64_t *nsplit_out) {
@@ -788,14 +880,14 @@ hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, hipStre
 
     hipError_t e;
     const size_t smem = sizeof(float) * chain_smem_floats(d);
-    const void *fn = a.bf16 ? (const void *)bwd_chain_kernel<true> : (const void *)bwd_chain_kernel<false>;
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    switch (a.R) {
+        case 1: e = launch_chain<1>(ba, chains, smem, st); break;
+        case 2: e = launch_chain<2>(ba, chains, smem, st); break;
+        case 3: e = launch_chain<3>(ba, chains, smem, st); break;
+        case 4: e = launch_chain<4>(ba, chains, smem, st); break;
+        default: e = hipErrorInvalidValue;
+    }
     if (e != hipSuccess) return e;
-    if (a.bf16)
-        hipLaunchKernelGGL(bwd_chain_kernel<true>, dim3((unsigned)chains), dim3(kThreads), smem, st, ba);
-    else
-        hipLaunchKernelGGL(bwd_chain_kernel<false>, dim3((unsigned)chains), dim3(kThreads), smem, st, ba);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
 
     const unsigned nrow = (unsigned)(a.b * a.L * a.G);
     if (nrow > 0) {

@@ -214,3 +214,53 @@ def test_plans_for_workloads(m3):
     s = m3.make_shape(tiny.batch, tiny.seqlen, tiny.nheads, tiny.ngroups, tiny.headdim, tiny.dstate,
                       tiny.rank, tiny.chunk, m3.M3_F32, tiny.eps)
     assert m3.plan(s).kernel == 0
+
+
+def _fake_grads(m3, io, base=0x400000, drop=None):
+    g = m3.ScanGrads()
+    for i, (name, _) in enumerate(m3.ScanGrads._fields_):
+        if name in ("dh_final", "dh0"):
+            continue
+        if name == "dB_normw" and not io.B_normw or name == "dC_normw" and not io.C_normw:
+            continue
+        if name in ("dx_prev", "dBraw_prev") and not io.x_prev:
+            continue
+        setattr(g, name, base + 0x1000 * (i + 1))
+    if drop:
+        setattr(g, drop, None)
+    return g
+
+
+def _bwd(m3, s, io, g, ws=None, wsb=0):
+    return m3.lib.m3_scan_bwd(ctypes.byref(s), ctypes.byref(io), ctypes.byref(g), ws, wsb, None)
+
+
+def test_backward_validated_on_host(m3):
+    s = _shape(m3, rank=2, chunk=32)
+    io = _fake_io(m3)
+    assert m3.lib.m3_scan_bwd_workspace_bytes(ctypes.byref(s)) > 0
+    # every required gradient
+    for name in ("dy", "dx", "dBraw", "dCraw", "ddt", "dA", "dlam", "dtheta", "dB_bias", "dC_bias"):
+        assert _bwd(m3, s, io, _fake_grads(m3, io, drop=name)) == -1, name
+    # gain gradients exactly when the gains exist; previous-token gradients likewise
+    g = _fake_grads(m3, io)
+    g.dB_normw = 0x900000
+    assert _bwd(m3, s, io, g) == -1
+    io2 = _fake_io(m3)
+    io2.x_prev, io2.Braw_prev = 0x910000, 0x920000
+    assert _bwd(m3, s, io2, _fake_grads(m3, io)) == -1
+    # workspace
+    assert _bwd(m3, s, io, _fake_grads(m3, io)) == -4
+    # alignment
+    g = _fake_grads(m3, io)
+    g.dx = g.dx + 4
+    assert _bwd(m3, s, io, g) == -3
+    # the fused form and the epilogue are not differentiated
+    io3 = _fake_io(m3, fused=True)
+    assert _bwd(m3, s, io3, _fake_grads(m3, io)) == -2
+    io4 = _fake_io(m3)
+    io4.D = 0x930000
+    assert _bwd(m3, s, io4, _fake_grads(m3, io)) == -2
+    assert _bwd(m3, _shape(m3, flags=m3.M3_FLAG_OUT_NORM), io, _fake_grads(m3, io)) == -2
+    # shapes beyond the LDS tiles
+    assert _bwd(m3, _shape(m3, dstate=256, headdim=16), io, _fake_grads(m3, io)) == -2
