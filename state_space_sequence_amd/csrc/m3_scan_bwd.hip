@@ -115,13 +115,14 @@ struct BwdArgs {
     float *fold;  // [b,H]       gradient of the fold factor (1 - lam_0) dt_0
 };
 
-template <bool BF16, int R>
+// NF, PF: N and P fixed at compile time (0: taken from the arguments)
+template <bool BF16, int R, int NF, int PF>
 __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs ba) {
     const ScanArgs &a = ba.f;
-    const BwdDims dm = bwd_dims(a.L, a.N, a.P, R);
+    const BwdDims dm = bwd_dims(a.L, NF ? NF : a.N, PF ? PF : a.P, R);
     constexpr int Cb = kRowsB / R, T = Cb * R;  // tokens and rows per chunk (compile-time)
-    const int N = dm.N, P = dm.P, half = dm.half, nch = dm.nch, npb = dm.npb;
-    const int NS = dm.NS, PS = dm.PS, HS = dm.HS;
+    const int N = NF ? NF : dm.N, P = PF ? PF : dm.P, half = N / 2, nch = dm.nch, npb = P / 4;
+    const int NS = N + 4, PS = P + 4, HS = half + 1;
     constexpr int NT = kChainThreads;
     const FDiv fN((uint32_t)N), fP((uint32_t)P), fH((uint32_t)half), fP4((uint32_t)(P / 4));
     const int tid = threadIdx.x;
@@ -806,16 +807,26 @@ __global__ __launch_bounds__(kThreads) void bwd_token_kernel(BwdArgs ba, float *
     }
 }
 
-template <int R>
-hipError_t launch_chain(const BwdArgs &ba, int64_t chains, size_t smem, hipStream_t st) {
-    const void *fn = ba.f.bf16 ? (const void *)bwd_chain_kernel<true, R> : (const void *)bwd_chain_kernel<false, R>;
+template <int R, int NF, int PF>
+hipError_t launch_chain_np(const BwdArgs &ba, int64_t chains, size_t smem, hipStream_t st) {
+    const void *fn = ba.f.bf16 ? (const void *)bwd_chain_kernel<true, R, NF, PF>
+                               : (const void *)bwd_chain_kernel<false, R, NF, PF>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     if (ba.f.bf16)
-        hipLaunchKernelGGL((bwd_chain_kernel<true, R>), dim3((unsigned)chains), dim3(kChainThreads), smem, st, ba);
+        hipLaunchKernelGGL((bwd_chain_kernel<true, R, NF, PF>), dim3((unsigned)chains), dim3(kChainThreads), smem,
+                           st, ba);
     else
-        hipLaunchKernelGGL((bwd_chain_kernel<false, R>), dim3((unsigned)chains), dim3(kChainThreads), smem, st, ba);
+        hipLaunchKernelGGL((bwd_chain_kernel<false, R, NF, PF>), dim3((unsigned)chains), dim3(kChainThreads), smem,
+                           st, ba);
     return hipGetLastError();
+}
+
+// the 1.5B-scale head shape (N = 128, P = 64) gets a compile-time instance
+template <int R>
+hipError_t launch_chain(const BwdArgs &ba, int64_t chains, size_t smem, hipStream_t st) {
+    if (ba.f.N == 128 && ba.f.P == 64) return launch_chain_np<R, 128, 64>(ba, chains, smem, st);
+    return launch_chain_np<R, 0, 0>(ba, chains, smem, st);
 }
 
 }  // namespace
