@@ -649,6 +649,641 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs ba) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core chain kernel for N = 128, P = 64 and R in {1, 2, 4} (32 rows per
+// chunk): the same algebra as bwd_chain_kernel, every contraction on
+// v_mfma_f32_16x16x4_f32 (fp32 in, fp32 accumulate, so the fp32 bar holds).
+// Operand layout: lane l supplies A[i = l%16][k] and B[k][j = l%16]; in a
+// 16-wide K block starting at k0, lane group g = l/16 takes k = k0 + 4g + j for
+// the block's MFMA j, so a K-contiguous operand row is one 16-byte read and a
+// strided one four 4-byte reads. The accumulator holds rows 4g..4g+3 of column
+// l%16. The state S (forward sweep) and its adjoint dS (reverse sweep) live in
+// accumulators: wave w owns rows n = 16w..16w+15 and all 64 columns p.
+namespace mf {
+constexpr int N = 128, P = 64, HALF = 64, T = 32;
+constexpr int NS = N + 4, PS = P + 4, TS = T + 4;  // 16-byte aligned rows, shifted 4 banks each
+constexpr int NT = kChainThreads;
+
+__device__ __forceinline__ f4 mfma4(f4 a, f4 b, f4 c) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+    return c;
+}
+// four strided values at k0 + 4g + j, j = 0..3 (row stride in floats)
+__device__ __forceinline__ f4 ld_str(const float *p, int stride) {
+    return f4{p[0], p[stride], p[2 * stride], p[3 * stride]};
+}
+// sum over the 16 lanes of a DPP row; lane 15 of each row ends with the total
+__device__ __forceinline__ float row_sum16(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
+    return v;
+}
+
+__host__ __device__ constexpr size_t smem_floats() {
+    return (size_t)N * PS            // dSl: dS (reverse) / S (forward set-up), [n][p]
+           + 2 * (size_t)T * NS      // Bb, Cc
+           + 2 * (size_t)T * PS      // Xs, dYs
+           + 2 * (size_t)T * TS      // Sc, dP (mask folded in)
+           + 2 * (size_t)T * HALF    // Phi, theta (at most 32 tokens)
+           + (size_t)T * (HALF + 1)  // dPh
+           + (size_t)T * T           // Mk, dMk (tokens <= 32: two [Cb][Cb] <= 32*32 halves)
+           + (size_t)T * T
+           + 8 * (size_t)T           // offq [T][4], Qp [T][4]
+           + 13 * (size_t)(T + 1)    // token scalars
+           + 2 * (size_t)T           // 1/rms rows
+           + 2 * (size_t)HALF        // carry, rcar
+           + NT + 4;
+}
+}  // namespace mf
+
+template <bool BF16, int R>
+__global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs ba) {
+    using namespace mf;
+    static_assert(R == 1 || R == 2 || R == 4, "32 rows per chunk");
+    constexpr int Cb = T / R;
+    const ScanArgs &a = ba.f;
+    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+    const int lr = l & 15, lg = l >> 4;
+    const int64_t bh = blockIdx.x;
+    const int64_t bi = bh / a.H, hi = bh % a.H;
+    const int64_t g = hi / (a.H / a.G);
+    const int64_t L = a.L, H = a.H, G = a.G;
+    const int nch = (int)((L + Cb - 1) / Cb);
+    const int64_t slotf = (int64_t)N * P + HALF;
+
+    extern __shared__ float sm[];
+    float *dSl = sm;                  // [N][PS]
+    float *Bb = dSl + N * PS;         // [T][NS]
+    float *Cc = Bb + T * NS;          // [T][NS]
+    float *Xs = Cc + T * NS;          // [T][PS]
+    float *dYs = Xs + T * PS;         // [T][PS]
+    float *Sc = dYs + T * PS;         // [T][TS]
+    float *dP = Sc + T * TS;          // [T][TS]
+    float *Phi = dP + T * TS;         // [Cb][HALF]
+    float *thv = Phi + T * HALF;      // [Cb][HALF]
+    float *dPh = thv + T * HALF;      // [Cb][HALF + 1]
+    float *Mk = dPh + T * (HALF + 1); // [Cb][Cb]
+    float *dMk = Mk + T * T;          // [Cb][Cb]
+    float *offq = dMk + T * T;        // [T][4]
+    float *Qp = offq + 4 * T;         // [T][4]
+    float *dtv = Qp + 4 * T;          // [Cb+1]
+    float *lamv = dtv + (T + 1);
+    float *Av = lamv + (T + 1);
+    float *lcs = Av + (T + 1);
+    float *wgt = lcs + (T + 1);
+    float *gam = wgt + (T + 1);
+    float *ecs = gam + (T + 1);
+    float *Ew = ecs + (T + 1);
+    float *Ee = Ew + (T + 1);
+    float *dcs = Ee + (T + 1);
+    float *dwv = dcs + (T + 1);
+    float *dgv = dwv + (T + 1);
+    float *spare = dgv + (T + 1);
+    float *rsB = spare + (T + 1);     // [T]
+    float *rsC = rsB + T;             // [T]
+    float *carry = rsC + T;           // [HALF]
+    float *rcar = carry + HALF;       // [HALF]
+    float *red = rcar + HALF;         // [NT]
+    float *misc = red + NT;           // [4]
+    (void)spare;
+
+    float *chk = ba.chk + bh * (int64_t)(nch + 1) * slotf;
+    const float *wB = a.B_normw, *wC = a.C_normw;
+
+    // ---- staging (as in bwd_chain_kernel, with N, P fixed)
+    auto stage_chunk = [&](int64_t c0, int nv, bool withC) {
+        for (int t = tid; t <= Cb; t += NT) {
+            float d = 0.f, lm = 0.f, av = 0.f;
+            if (t <= nv && c0 + t < L) {
+                const int64_t o = (bi * L + c0 + t) * H + hi;
+                d = a.dt[o];
+                lm = a.lam[o];
+                av = a.A[o];
+            }
+            dtv[t] = d;
+            lamv[t] = lm;
+            Av[t] = av;
+        }
+        for (int e = tid; e < T * N; e += NT) {
+            const int rho = e / N, n = e % N;
+            const int t = rho / R, r = rho % R;
+            float vb = 0.f, vc = 0.f;
+            if (t < nv) {
+                const int64_t row = (((bi * L + c0 + t) * G + g) * R + r) * N;
+                vb = ld_io<BF16>(a.Braw, row + n);
+                if (withC) vc = ld_io<BF16>(a.Craw, row + n);
+            }
+            Bb[rho * NS + n] = vb;
+            Cc[rho * NS + n] = vc;
+        }
+        for (int e = tid; e < T * P; e += NT) {
+            const int rho = e / P, p = e % P;
+            const int t = rho / R, r = rho % R;
+            const int64_t o = (((bi * L + c0 + t) * H + hi) * R + r) * P + p;
+            Xs[rho * PS + p] = (t < nv) ? ld_io<BF16>(a.x, o) : 0.f;
+            dYs[rho * PS + p] = (withC && t < nv) ? ld_io<BF16>(ba.dy, o) : 0.f;
+        }
+        for (int e = tid; e < Cb * HALF; e += NT) {
+            const int t = e / HALF, i = e % HALF;
+            float v = 0.f, th = 0.f;
+            if (t < nv) {
+                const int64_t tok = bi * L + c0 + t;
+                th = a.theta[(tok * G + g) * HALF + i];
+                v = a.dt[tok * H + hi] * th * kInv2Pi;
+            }
+            Phi[e] = v;
+            thv[e] = th;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float run = 0.f;
+            for (int t = 0; t < Cb; ++t) {
+                if (t < nv) {
+                    run += dtv[t] * Av[t];
+                    const float look = (c0 + t + 1 < L) ? (1.0f - lamv[t + 1]) * dtv[t + 1] : 0.f;
+                    lcs[t] = run;
+                    gam[t] = lamv[t] * dtv[t];
+                    wgt[t] = lamv[t] * dtv[t] + look;
+                } else {
+                    lcs[t] = run;
+                    gam[t] = 0.f;
+                    wgt[t] = 0.f;
+                }
+            }
+        }
+        for (int i = tid - 64; i >= 0 && i < HALF; i += NT) {
+            float ph = carry[i];
+            for (int t = 0; t < nv; ++t) {
+                ph += Phi[t * HALF + i];
+                Phi[t * HALF + i] = ph;
+            }
+        }
+        const int nrow = withC ? 2 * T : T;
+        for (int grp = tid / 8; grp < nrow; grp += NT / 8) {
+            const int lane8 = tid % 8;
+            const bool isC = grp >= T;
+            const int rho = isC ? grp - T : grp;
+            const float *row = (isC ? Cc : Bb) + rho * NS;
+            float ss = 0.f;
+            for (int n = lane8; n < N; n += 8) ss += row[n] * row[n];
+            ss = group_sum<8>(ss);
+            if (lane8 == 0) (isC ? rsC : rsB)[rho] = 1.0f / sqrtf(ss / (float)N + a.eps);
+        }
+        __syncthreads();
+        const float cse = lcs[nv - 1];
+        for (int t = tid; t < Cb; t += NT) {
+            ecs[t] = expf(lcs[t]);
+            Ee[t] = (t < nv) ? expf(cse - lcs[t]) : 0.f;
+            Ew[t] = Ee[t] * wgt[t];
+        }
+        for (int e = tid; e < T * HALF; e += NT) {
+            const int rho = e / HALF, i = e % HALF;
+            const int t = rho / R, r = rho % R;
+            float bl = 0.f, bhv = 0.f, cl = 0.f, chv = 0.f;
+            if (t < nv) {
+                const float *bb = a.B_bias + (hi * R + r) * N;
+                float sn, cs;
+                sincospif(2.f * Phi[t * HALF + i], &sn, &cs);
+                const float B0 = Bb[rho * NS + i] * rsB[rho] * (wB ? wB[i] : 1.f) + bb[i];
+                const float B1 = Bb[rho * NS + i + HALF] * rsB[rho] * (wB ? wB[i + HALF] : 1.f) + bb[i + HALF];
+                bl = cs * B0 + sn * B1;
+                bhv = -sn * B0 + cs * B1;
+                if (withC) {
+                    const float *cb = a.C_bias + (hi * R + r) * N;
+                    const float C0 = Cc[rho * NS + i] * rsC[rho] * (wC ? wC[i] : 1.f) + cb[i];
+                    const float C1 = Cc[rho * NS + i + HALF] * rsC[rho] * (wC ? wC[i + HALF] : 1.f) + cb[i + HALF];
+                    cl = cs * C0 + sn * C1;
+                    chv = -sn * C0 + cs * C1;
+                }
+            }
+            Bb[rho * NS + i] = bl;
+            Bb[rho * NS + i + HALF] = bhv;
+            Cc[rho * NS + i] = cl;
+            Cc[rho * NS + i + HALF] = chv;
+        }
+        __syncthreads();
+    };
+
+    // previous token's normalised, biased B rows ([R][NS] in Sc) and x rows ([R][PS] in dP)
+    float *pB = Sc, *pX = dP;
+    auto prev_rows = [&]() {
+        for (int e = tid; e < R * N; e += NT) {
+            const int r = e / N, n = e % N;
+            pB[r * NS + n] = ld_io<BF16>(a.Braw_prev, ((bi * G + g) * R + r) * N + n);
+        }
+        for (int e = tid; e < R * P; e += NT) {
+            const int r = e / P, p = e % P;
+            pX[r * PS + p] = ld_io<BF16>(a.x_prev, ((bi * H + hi) * R + r) * P + p);
+        }
+        __syncthreads();
+        for (int grp = tid / 8; grp < R; grp += NT / 8) {
+            const int lane8 = tid % 8;
+            float ss = 0.f;
+            for (int n = lane8; n < N; n += 8) ss += pB[grp * NS + n] * pB[grp * NS + n];
+            ss = group_sum<8>(ss);
+            if (lane8 == 0) rsB[grp] = 1.0f / sqrtf(ss / (float)N + a.eps);
+        }
+        __syncthreads();
+        for (int e = tid; e < R * N; e += NT) {
+            const int r = e / N, n = e % N;
+            pB[r * NS + n] = pB[r * NS + n] * rsB[r] * (wB ? wB[n] : 1.f) + a.B_bias[(hi * R + r) * N + n];
+        }
+        __syncthreads();
+    };
+
+    // ---- initial state into LDS, then into the accumulators (rows 16w + 4lg + jj, column 16pt + lr)
+    for (int e = tid; e < N * P; e += NT) {
+        const int p = e / N, n = e % N;  // coalesced over h0's n
+        dSl[n * PS + p] = a.h0 ? a.h0[(bh * P + p) * N + n] : 0.f;
+    }
+    for (int i = tid; i < HALF; i += NT) carry[i] = 0.f;
+    const float fold_f = (a.has_prev && L > 0) ? (1.0f - a.lam[bi * L * H + hi]) * a.dt[bi * L * H + hi] : 0.f;
+    if (a.has_prev && L > 0) {
+        __syncthreads();
+        prev_rows();
+        for (int e = tid; e < N * P; e += NT) {
+            const int n = e / P, p = e % P;
+            float acc = 0.f;
+            for (int r = 0; r < R; ++r) acc += pB[r * NS + n] * pX[r * PS + p];
+            dSl[n * PS + p] += fold_f * acc;
+        }
+    }
+    __syncthreads();
+    f4 acc[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[pt][jj] = dSl[(16 * w + 4 * lg + jj) * PS + 16 * pt + lr];
+
+    // ---- forward sweep
+    for (int k = 0; k < nch; ++k) {
+        const int64_t c0 = (int64_t)k * Cb;
+        const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
+        float *slot = chk + (int64_t)k * slotf;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) slot[(16 * w + 4 * lg + jj) * P + 16 * pt + lr] = acc[pt][jj];
+        for (int i = tid; i < HALF; i += NT) slot[N * P + i] = carry[i];
+        stage_chunk(c0, nv, false);
+        // S <- e^{cs_end} S + sum_sigma (E B_bar)^T x: A[n][sigma] = E_s B_bar[sigma][n], B[sigma][p] = x
+        const float dec = expf(lcs[nv - 1]);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] *= dec;
+#pragma unroll
+        for (int k0 = 0; k0 < T; k0 += 16) {
+            const int kk = k0 + 4 * lg;
+            f4 av = ld_str(&Bb[kk * NS + 16 * w + lr], NS);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) av[j] *= Ew[(kk + j) / R];
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma4(av, ld_str(&Xs[kk * PS + 16 * pt + lr], PS), acc[pt]);
+        }
+        for (int i = tid; i < HALF; i += NT) carry[i] = __builtin_amdgcn_fractf(Phi[(nv - 1) * HALF + i]);
+        __syncthreads();
+    }
+    {
+        float *slot = chk + (int64_t)nch * slotf;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                slot[(16 * w + 4 * lg + jj) * P + 16 * pt + lr] = acc[pt][jj];
+                dSl[(16 * w + 4 * lg + jj) * PS + 16 * pt + lr] = acc[pt][jj];  // S_final
+            }
+        for (int i = tid; i < HALF; i += NT) slot[N * P + i] = carry[i];
+    }
+    __syncthreads();
+    // ---- d Phi_end[i] = sum_p (-dh_lo h_hi + dh_hi h_lo), h = R(Phi_end) S_final
+    for (int i = tid; i < HALF; i += NT) {
+        float rg = 0.f;
+        if (ba.dh_final) {
+            float sn, cs;
+            sincospif(2.f * carry[i], &sn, &cs);
+            for (int p = 0; p < P; ++p) {
+                const float hl = ba.dh_final[(bh * P + p) * N + i], hh = ba.dh_final[(bh * P + p) * N + i + HALF];
+                const float su = dSl[i * PS + p], sv = dSl[(i + HALF) * PS + p];
+                rg += -hl * (sn * su + cs * sv) + hh * (cs * su - sn * sv);
+            }
+        }
+        rcar[i] = rg;
+    }
+    __syncthreads();
+    // dS = R(-Phi_end) dh_final
+    for (int e = tid; e < HALF * P; e += NT) {
+        const int p = e / HALF, i = e % HALF;
+        float dlo = 0.f, dhi = 0.f;
+        if (ba.dh_final) {
+            float sn, cs;
+            sincospif(2.f * carry[i], &sn, &cs);
+            const float hl = ba.dh_final[(bh * P + p) * N + i], hh = ba.dh_final[(bh * P + p) * N + i + HALF];
+            dlo = cs * hl + sn * hh;
+            dhi = -sn * hl + cs * hh;
+        }
+        dSl[i * PS + p] = dlo;
+        dSl[(i + HALF) * PS + p] = dhi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[pt][jj] = dSl[(16 * w + 4 * lg + jj) * PS + 16 * pt + lr];
+
+    // wave roles for the [T][N] tiles: rows 16*rt.., columns 16*nt0.. and 16*(nt0+4).. (a rotation pair)
+    const int rt = w >> 2, nt0 = w & 3;
+    for (int k = nch - 1; k >= 0; --k) {
+        const int64_t c0 = (int64_t)k * Cb;
+        const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
+        const float *slot = chk + (int64_t)k * slotf;
+        const float *slot1 = chk + (int64_t)(k + 1) * slotf;
+        for (int i = tid; i < HALF; i += NT) carry[i] = slot[N * P + i];
+        // <S_out, dS> from the accumulators
+        {
+            float part = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) part += acc[pt][jj] * slot1[(16 * w + 4 * lg + jj) * P + 16 * pt + lr];
+            red[tid] = part;
+        }
+        stage_chunk(c0, nv, true);
+        const float cse = lcs[nv - 1];
+
+        // (1) dC_bar from the carried-state output term: e^{cs_t} sum_p dY[rho][p] S_in[n][p]
+        f4 dC[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int nt = nt0 + 4 * q;
+            f4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < P; k0 += 16) {
+                const int kk = k0 + 4 * lg;
+                const f4 av = ld4(&dYs[(16 * rt + lr) * PS + kk]);
+                const f4 bv = *reinterpret_cast<const f4 *>(&slot[(16 * nt + lr) * P + kk]);
+                c = mfma4(av, bv, c);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) c[jj] *= ecs[(16 * rt + 4 * lg + jj) / R];
+            dC[q] = c;
+        }
+        // off-term part of d cs: sum_n C_bar[rho][n] dCoff[rho][n], per row, this wave's 32 columns
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int rho = 16 * rt + 4 * lg + jj;
+            float v = Cc[rho * NS + 16 * nt0 + lr] * dC[0][jj] + Cc[rho * NS + 16 * (nt0 + 4) + lr] * dC[1][jj];
+            v = row_sum16(v);
+            if (lr == 15) offq[rho * 4 + nt0] = v;
+        }
+        // (2) scores and dy . x on waves 0..5: tiles (0,0), (1,0), (1,1)
+        if (w < 6) {
+            const int tix = (w < 3) ? w : w - 3;
+            const int ta = (tix == 0) ? 0 : 1, tb = (tix == 2) ? 1 : 0;
+            f4 c = {0.f, 0.f, 0.f, 0.f};
+            if (w < 3) {
+#pragma unroll
+                for (int k0 = 0; k0 < N; k0 += 16)
+                    c = mfma4(ld4(&Cc[(16 * ta + lr) * NS + k0 + 4 * lg]), ld4(&Bb[(16 * tb + lr) * NS + k0 + 4 * lg]), c);
+            } else {
+#pragma unroll
+                for (int k0 = 0; k0 < P; k0 += 16)
+                    c = mfma4(ld4(&dYs[(16 * ta + lr) * PS + k0 + 4 * lg]), ld4(&Xs[(16 * tb + lr) * PS + k0 + 4 * lg]), c);
+            }
+            float *dst = (w < 3) ? Sc : dP;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dst[(16 * ta + 4 * lg + jj) * TS + 16 * tb + lr] = c[jj];
+        } else {
+            // the tile above the diagonal is zero
+            for (int e = tid - 384; e < 256; e += 128) {
+                const int rr = e / 16, cc = e % 16;
+                Sc[rr * TS + 16 + cc] = 0.f;
+                dP[rr * TS + 16 + cc] = 0.f;
+            }
+        }
+        if (tid == 0) {
+            float sod = 0.f;
+            for (int j = 0; j < NT; ++j) sod += red[j];
+            misc[0] = sod;
+        }
+        __syncthreads();
+        // (3) mask per token pair, its gradient, and the mask folded into Sc and dP
+        for (int e = tid; e < Cb * Cb; e += NT) {
+            const int t = e / Cb, s = e % Cb;
+            float m = 0.f, dmv = 0.f;
+            if (s <= t && t < nv) {
+                m = (s == t) ? gam[t] : expf(lcs[t] - lcs[s]) * wgt[s];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int r2 = 0; r2 < R; ++r2) {
+                        const int idx = (t * R + r) * TS + s * R + r2;
+                        dmv += dP[idx] * Sc[idx];
+                    }
+            }
+            Mk[e] = m;
+            dMk[e] = dmv;
+        }
+        __syncthreads();
+        for (int e = tid; e < T * T; e += NT) {
+            const int rho = e / T, sg = e % T;
+            const float m = Mk[(rho / R) * Cb + sg / R];
+            Sc[rho * TS + sg] *= m;
+            dP[rho * TS + sg] *= m;
+        }
+        __syncthreads();
+        // (4) dx tile (rows sigma 16*st.., columns 16*pt..): intra sum_rho MSc[rho][sigma] dY[rho][p]
+        //     + E_sigma sum_n B_bar[sigma][n] dS[n][p]; Q_sigma partial = sum_p x[sigma][p] (state part)
+        {
+            const int st = w >> 2, pt = w & 3;
+            f4 ci = {0.f, 0.f, 0.f, 0.f}, cs_ = {0.f, 0.f, 0.f, 0.f};
+            for (int k0 = 16 * st; k0 < T; k0 += 16) {
+                const int kk = k0 + 4 * lg;
+                ci = mfma4(ld_str(&Sc[kk * TS + 16 * st + lr], TS), ld_str(&dYs[kk * PS + 16 * pt + lr], PS), ci);
+            }
+#pragma unroll
+            for (int k0 = 0; k0 < N; k0 += 16) {
+                const int kk = k0 + 4 * lg;
+                cs_ = mfma4(ld4(&Bb[(16 * st + lr) * NS + kk]), ld_str(&dSl[kk * PS + 16 * pt + lr], PS), cs_);
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int sg = 16 * st + 4 * lg + jj, s = sg / R;
+                const float q = row_sum16(Xs[sg * PS + 16 * pt + lr] * cs_[jj]);
+                if (lr == 15) Qp[sg * 4 + pt] = q;
+                if (s < nv)
+                    ba.dx[(((bi * L + c0 + s) * H + hi) * R + sg % R) * P + 16 * pt + lr] = ci[jj] + Ew[s] * cs_[jj];
+            }
+        }
+        // (5) dC_bar += MdP B_bar, dB_bar = MdP^T C_bar + E_sigma x dS^T, for the column pair
+        {
+            f4 dB[2], dBs[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int nt = nt0 + 4 * q;
+                f4 c = dC[q], b = {0.f, 0.f, 0.f, 0.f}, bs = {0.f, 0.f, 0.f, 0.f};
+                for (int k0 = 0; k0 < 16 * (rt + 1); k0 += 16) {  // sigma <= rho
+                    const int kk = k0 + 4 * lg;
+                    c = mfma4(ld4(&dP[(16 * rt + lr) * TS + kk]), ld_str(&Bb[kk * NS + 16 * nt + lr], NS), c);
+                }
+                for (int k0 = 16 * rt; k0 < T; k0 += 16) {  // rho >= sigma
+                    const int kk = k0 + 4 * lg;
+                    b = mfma4(ld_str(&dP[kk * TS + 16 * rt + lr], TS), ld_str(&Cc[kk * NS + 16 * nt + lr], NS), b);
+                }
+#pragma unroll
+                for (int k0 = 0; k0 < P; k0 += 16) {
+                    const int kk = k0 + 4 * lg;
+                    bs = mfma4(ld4(&Xs[(16 * rt + lr) * PS + kk]), ld4(&dSl[(16 * nt + lr) * PS + kk]), bs);
+                }
+                dC[q] = c;
+                dB[q] = b;
+                dBs[q] = bs;
+            }
+            const int i = 16 * nt0 + lr;  // channel of the pair (i, i + 64)
+            float dphi_tok[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int rho = 16 * rt + 4 * lg + jj, t = rho / R, r = rho % R;
+                const float E = Ew[t];
+                const float dbl = dB[0][jj] + E * dBs[0][jj], dbh = dB[1][jj] + E * dBs[1][jj];
+                const float dcl = dC[0][jj], dch = dC[1][jj];
+                dphi_tok[jj] = dbl * Bb[rho * NS + i + HALF] - dbh * Bb[rho * NS + i] + dcl * Cc[rho * NS + i + HALF] -
+                               dch * Cc[rho * NS + i];
+                if (t < nv) {
+                    float sn, cs;
+                    sincospif(2.f * Phi[t * HALF + i], &sn, &cs);
+                    const int64_t o = (((bi * L + c0 + t) * H + hi) * R + r) * N;
+                    ba.gB[o + i] = cs * dbl - sn * dbh;
+                    ba.gB[o + i + HALF] = sn * dbl + cs * dbh;
+                    ba.gC[o + i] = cs * dcl - sn * dch;
+                    ba.gC[o + i + HALF] = sn * dcl + cs * dch;
+                }
+            }
+            // the lane's 4 rows are 4/R whole tokens: sum the ranks of each token
+#pragma unroll
+            for (int u = 0; u < 4 / R; ++u) {
+                float v = 0.f;
+#pragma unroll
+                for (int r = 0; r < R; ++r) v += dphi_tok[u * R + r];
+                dPh[((16 * rt + 4 * lg) / R + u) * (HALF + 1) + i] = v;
+            }
+        }
+        // (6) dS <- e^{cs_end} dS + sum_rho e^{cs_t} C_bar[rho]^T dY[rho] (accumulators; the LDS copy is
+        //     still read above by other waves, so it is rewritten after the barrier)
+        {
+            const float dec = expf(cse);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) acc[pt] *= dec;
+#pragma unroll
+            for (int k0 = 0; k0 < T; k0 += 16) {
+                const int kk = k0 + 4 * lg;
+                const f4 av = ld_str(&Cc[kk * NS + 16 * w + lr], NS);
+                f4 sc4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sc4[j] = ecs[(kk + j) / R];
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma4(av, ld_str(&dYs[kk * PS + 16 * pt + lr], PS) * sc4, acc[pt]);
+            }
+        }
+        __syncthreads();
+        // (7) token scalars, suffix sums of d Phi, and the new dS into LDS
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dSl[(16 * w + 4 * lg + jj) * PS + 16 * pt + lr] = acc[pt][jj];
+        for (int j = tid; j < Cb + HALF; j += NT) {
+            if (j < Cb) {
+                const int t = j;
+                float dc = 0.f, dw = 0.f, dg = 0.f;
+                if (t < nv) {
+                    float Qt = 0.f, off = 0.f;
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            Qt += Qp[(t * R + r) * 4 + q];
+                            off += offq[(t * R + r) * 4 + q];
+                        }
+                    dc = off;
+                    for (int s = 0; s < t; ++s) dc += dMk[t * Cb + s] * Mk[t * Cb + s];
+                    for (int t2 = t + 1; t2 < nv; ++t2) {
+                        dc -= dMk[t2 * Cb + t] * Mk[t2 * Cb + t];
+                        dw += dMk[t2 * Cb + t] * expf(lcs[t2] - lcs[t]);
+                    }
+                    dc -= Ew[t] * Qt;
+                    dw += Ee[t] * Qt;
+                    if (t == nv - 1) dc += misc[0];
+                    dg = dMk[t * Cb + t];
+                }
+                dcs[t] = dc;
+                dwv[t] = dw;
+                dgv[t] = dg;
+            } else {
+                const int i = j - Cb;
+                float rc = rcar[i];
+                for (int t = nv - 1; t >= 0; --t) {
+                    rc += dPh[t * (HALF + 1) + i];
+                    const int64_t tok = bi * L + c0 + t;
+                    ba.gth[(tok * H + hi) * HALF + i] = dtv[t] * rc;
+                    dPh[t * (HALF + 1) + i] = thv[t * HALF + i] * rc;
+                }
+                rcar[i] = rc;
+            }
+        }
+        __syncthreads();
+        for (int t = tid; t < nv; t += NT) {
+            float da = 0.f;
+            for (int t2 = t; t2 < nv; ++t2) da += dcs[t2];
+            float dth = 0.f;
+            for (int i = 0; i < HALF; ++i) dth += dPh[t * (HALF + 1) + i];
+            float *rec = ba.tok + ((bi * L + c0 + t) * H + hi) * 4;
+            rec[0] = da;
+            rec[1] = dwv[t];
+            rec[2] = dgv[t];
+            rec[3] = dth;
+        }
+        __syncthreads();
+    }
+
+    // ---- chain start: dh0 and the previous token's fold (dS is in dSl)
+    if (ba.dh0) {
+        for (int e = tid; e < N * P; e += NT) {
+            const int p = e / N, n = e % N;
+            ba.dh0[(bh * P + p) * N + n] = dSl[n * PS + p];
+        }
+    }
+    if (a.has_prev && L > 0) {
+        prev_rows();
+        for (int e = tid; e < R * N; e += NT) {
+            const int r = e / N, n = e % N;
+            float s = 0.f;
+            for (int p = 0; p < P; ++p) s += dSl[n * PS + p] * pX[r * PS + p];
+            ba.gBp[(bh * R + r) * N + n] = fold_f * s;
+        }
+        for (int e = tid; e < R * P; e += NT) {
+            const int r = e / P, p = e % P;
+            float s = 0.f;
+            for (int n = 0; n < N; ++n) s += dSl[n * PS + p] * pB[r * NS + n];
+            ba.dx_prev[(bh * R + r) * P + p] = fold_f * s;
+        }
+        float part = 0.f;
+        for (int e = tid; e < N * P; e += NT) {
+            const int n = e / P, p = e % P;
+            float v = 0.f;
+            for (int r = 0; r < R; ++r) v += pB[r * NS + n] * pX[r * PS + p];
+            part += dSl[n * PS + p] * v;
+        }
+        red[tid] = part;
+        __syncthreads();
+        if (tid == 0) {
+            float s = 0.f;
+            for (int j = 0; j < NT; ++j) s += red[j];
+            ba.fold[bh] = s;
+        }
+    }
+}
+
 // Sum the per-head dB / dC / d theta of a token over the heads of its group and
 // take BCNorm's backward: with v = Braw rs w + bias, rs = (mean Braw^2 + eps)^-1/2,
 //   dBraw = rs w dv - Braw rs^3 / N sum_n (Braw w dv).
@@ -822,10 +1457,26 @@ hipError_t launch_chain_np(const BwdArgs &ba, int64_t chains, size_t smem, hipSt
     return hipGetLastError();
 }
 
-// the 1.5B-scale head shape (N = 128, P = 64) gets a compile-time instance
+template <int R>
+hipError_t launch_chain_mfma(const BwdArgs &ba, int64_t chains, hipStream_t st) {
+    const size_t smem = sizeof(float) * mf::smem_floats();
+    const void *fn = ba.f.bf16 ? (const void *)bwd_chain_mfma_kernel<true, R> : (const void *)bwd_chain_mfma_kernel<false, R>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    if (ba.f.bf16)
+        hipLaunchKernelGGL((bwd_chain_mfma_kernel<true, R>), dim3((unsigned)chains), dim3(kChainThreads), smem, st, ba);
+    else
+        hipLaunchKernelGGL((bwd_chain_mfma_kernel<false, R>), dim3((unsigned)chains), dim3(kChainThreads), smem, st, ba);
+    return hipGetLastError();
+}
+
+// the 1.5B-scale head shape (N = 128, P = 64) runs on the matrix cores for R in {1, 2, 4}
 template <int R>
 hipError_t launch_chain(const BwdArgs &ba, int64_t chains, size_t smem, hipStream_t st) {
-    if (ba.f.N == 128 && ba.f.P == 64) return launch_chain_np<R, 128, 64>(ba, chains, smem, st);
+    if (ba.f.N == 128 && ba.f.P == 64) {
+        if constexpr (R == 1 || R == 2 || R == 4) return launch_chain_mfma<R>(ba, chains, st);
+        return launch_chain_np<R, 128, 64>(ba, chains, smem, st);
+    }
     return launch_chain_np<R, 0, 0>(ba, chains, smem, st);
 }
 

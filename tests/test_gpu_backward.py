@@ -38,6 +38,10 @@ CASES = [
     (1, 100, 2, 1, 64, 128, 4, "bf16", True, True, False, True, True),
     (2, 64, 2, 1, 64, 128, 1, "bf16", False, False, False, False, False),
     (1, 1, 2, 1, 16, 32, 2, "f32", True, True, True, True, False),
+    # the head shape N = 128, P = 64 runs on the matrix cores (R in {1, 2, 4})
+    (2, 77, 2, 1, 64, 128, 2, "f32", True, True, True, True, True),
+    (1, 40, 3, 3, 64, 128, 1, "f32", False, True, False, True, False),
+    (1, 5, 2, 1, 64, 128, 4, "bf16", True, False, True, False, False),
 ]
 
 
@@ -63,8 +67,9 @@ def test_backward_matches_oracle(case):
     assert worst < TOL_BWD
 
 
-def test_backward_is_deterministic():
-    shape = Shape(2, 90, 3, 1, 32, 64, 2, 32, "f32")
+@pytest.mark.parametrize("N,P", [(64, 32), (128, 64)])
+def test_backward_is_deterministic(N, P):
+    shape = Shape(2, 90, 3, 1, P, N, 2, 32, "f32")
     inp = make_scan_inputs(shape, seed=53, with_h0=True, with_prev=True, with_normw=True)
     dy, dh = upstream(shape, 54, True, "f32")
     g1 = gpu_scan_bwd(inp, shape, dy, dh)
