@@ -682,6 +682,39 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
+// a value the compiler cannot see through: lane-derived addresses computed from it
+// inside the chunk loops are rebuilt each chunk instead of being hoisted and kept
+// live (or spilled) across the loop
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+template <int K>
+__device__ __forceinline__ float shr(float v) {  // row_shr:K (lanes without a source in their row read 0)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + K, 0xf, 0xf, false));
+}
+// inclusive prefix sum over aligned groups of G lanes (G in {8, 16, 32}); ln = lane index
+template <int G>
+__device__ __forceinline__ float group_scan(float v, int ln) {
+    static_assert(G == 8 || G == 16 || G == 32, "groups of 8, 16 or 32 lanes");
+    const int q = ln & (G - 1);
+    float s;
+    s = shr<1>(v);
+    v += (q >= 1) ? s : 0.f;
+    s = shr<2>(v);
+    v += (q >= 2) ? s : 0.f;
+    s = shr<4>(v);
+    v += (q >= 4) ? s : 0.f;
+    if constexpr (G >= 16) {
+        s = shr<8>(v);
+        v += (q >= 8) ? s : 0.f;
+    }
+    if constexpr (G >= 32)  // row_bcast:15 into rows 1 and 3
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    return v;
+}
+
 __host__ __device__ constexpr size_t smem_floats() {
     return (size_t)N * PS            // dSl: dS (reverse) / S (forward set-up), [n][p]
            + 2 * (size_t)T * NS      // Bb, Cc
@@ -693,6 +726,7 @@ __host__ __device__ constexpr size_t smem_floats() {
            + (size_t)T * T
            + 8 * (size_t)T           // offq [T][4], Qp [T][4]
            + 13 * (size_t)(T + 1)    // token scalars
+           + 8 * (size_t)T           // per-wave partial sums of theta * suffix, per token
            + 2 * (size_t)T           // 1/rms rows
            + 2 * (size_t)HALF        // carry, rcar
            + NT + 4;
@@ -741,14 +775,14 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     float *dcs = Ee + (T + 1);
     float *dwv = dcs + (T + 1);
     float *dgv = dwv + (T + 1);
-    float *spare = dgv + (T + 1);
-    float *rsB = spare + (T + 1);     // [T]
+    float *dcr = dgv + (T + 1);       // [Cb+1] d cs: mask terms (row and column sums)
+    float *dthp = dcr + (T + 1);      // [8][T] per-wave partial angle terms of dt
+    float *rsB = dthp + 8 * T;        // [T]
     float *rsC = rsB + T;             // [T]
     float *carry = rsC + T;           // [HALF]
     float *rcar = carry + HALF;       // [HALF]
     float *red = rcar + HALF;         // [NT]
     float *misc = red + NT;           // [4]
-    (void)spare;
 
     float *chk = ba.chk + bh * (int64_t)(nch + 1) * slotf;
     const float *wB = a.B_normw, *wC = a.C_normw;
@@ -798,28 +832,25 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             thv[e] = th;
         }
         __syncthreads();
-        if (tid == 0) {
-            float run = 0.f;
-            for (int t = 0; t < Cb; ++t) {
-                if (t < nv) {
-                    run += dtv[t] * Av[t];
-                    const float look = (c0 + t + 1 < L) ? (1.0f - lamv[t + 1]) * dtv[t + 1] : 0.f;
-                    lcs[t] = run;
-                    gam[t] = lamv[t] * dtv[t];
-                    wgt[t] = lamv[t] * dtv[t] + look;
-                } else {
-                    lcs[t] = run;
-                    gam[t] = 0.f;
-                    wgt[t] = 0.f;
-                }
+        // decay prefix over the tokens (wave 0, lane t) and angle prefixes (every wave, two
+        // channels per pass, lanes 32h + t): DPP scans instead of serial walks
+        if (w == 0 && l < 32) {
+            const int t = l;
+            const bool v_ = t < nv;
+            const float run = group_scan<32>(v_ ? dtv[t] * Av[t] : 0.f, l);
+            if (t < Cb) {
+                const float look = (v_ && c0 + t + 1 < L) ? (1.0f - lamv[t + 1]) * dtv[t + 1] : 0.f;
+                lcs[t] = run;
+                gam[t] = v_ ? lamv[t] * dtv[t] : 0.f;
+                wgt[t] = v_ ? lamv[t] * dtv[t] + look : 0.f;
             }
         }
-        for (int i = tid - 64; i >= 0 && i < HALF; i += NT) {
-            float ph = carry[i];
-            for (int t = 0; t < nv; ++t) {
-                ph += Phi[t * HALF + i];
-                Phi[t * HALF + i] = ph;
-            }
+#pragma unroll
+        for (int m = 0; m < HALF / 16; ++m) {
+            const int i = 8 * w + 2 * m + (l >> 5), t = l & 31;
+            float v = (t < nv) ? Phi[t * HALF + i] : 0.f;
+            v = group_scan<32>(v, l) + carry[i];
+            if (t < nv) Phi[t * HALF + i] = v;
         }
         const int nrow = withC ? 2 * T : T;
         for (int grp = tid / 8; grp < nrow; grp += NT / 8) {
@@ -920,6 +951,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
 
     // ---- forward sweep
     for (int k = 0; k < nch; ++k) {
+        const int l = opaque(tid & 63), lr = l & 15, lg = l >> 4;
         const int64_t c0 = (int64_t)k * Cb;
         const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
         float *slot = chk + (int64_t)k * slotf;
@@ -995,6 +1027,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     // wave roles for the [T][N] tiles: rows 16*rt.., columns 16*nt0.. and 16*(nt0+4).. (a rotation pair)
     const int rt = w >> 2, nt0 = w & 3;
     for (int k = nch - 1; k >= 0; --k) {
+        const int l = opaque(tid & 63), lr = l & 15, lg = l >> 4;
         const int64_t c0 = (int64_t)k * Cb;
         const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
         const float *slot = chk + (int64_t)k * slotf;
@@ -1029,6 +1062,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             for (int jj = 0; jj < 4; ++jj) c[jj] *= ecs[(16 * rt + 4 * lg + jj) / R];
             dC[q] = c;
         }
+        __builtin_amdgcn_sched_barrier(0);
         // off-term part of d cs: sum_n C_bar[rho][n] dCoff[rho][n], per row, this wave's 32 columns
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -1037,17 +1071,18 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             v = row_sum16(v);
             if (lr == 15) offq[rho * 4 + nt0] = v;
         }
+        __builtin_amdgcn_sched_barrier(0);
         // (2) scores and dy . x on waves 0..5: tiles (0,0), (1,0), (1,1)
         if (w < 6) {
             const int tix = (w < 3) ? w : w - 3;
             const int ta = (tix == 0) ? 0 : 1, tb = (tix == 2) ? 1 : 0;
             f4 c = {0.f, 0.f, 0.f, 0.f};
             if (w < 3) {
-#pragma unroll
+#pragma unroll 2
                 for (int k0 = 0; k0 < N; k0 += 16)
                     c = mfma4(ld4(&Cc[(16 * ta + lr) * NS + k0 + 4 * lg]), ld4(&Bb[(16 * tb + lr) * NS + k0 + 4 * lg]), c);
             } else {
-#pragma unroll
+#pragma unroll 2
                 for (int k0 = 0; k0 < P; k0 += 16)
                     c = mfma4(ld4(&dYs[(16 * ta + lr) * PS + k0 + 4 * lg]), ld4(&Xs[(16 * tb + lr) * PS + k0 + 4 * lg]), c);
             }
@@ -1068,10 +1103,13 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             misc[0] = sod;
         }
         __syncthreads();
-        // (3) mask per token pair, its gradient, and the mask folded into Sc and dP
-        for (int e = tid; e < Cb * Cb; e += NT) {
-            const int t = e / Cb, s = e % Cb;
-            float m = 0.f, dmv = 0.f;
+        // (3) mask per token pair m(t,s) and its gradient dm = sum over the rank block of dP Sc;
+        //     the gradient's sums go straight to the tokens (groups of Cb lanes hold one row, or
+        //     one column): d cs_t += sum_{s<t} dm m - sum_{t2>t} dm(t2,t) m(t2,t),
+        //     dw_t = sum_{t2>t} dm(t2,t) e^{cs_t2 - cs_t}, dgamma_t = dm(t,t)
+        auto mask_at = [&](int t, int s, float &m, float &dmv) {
+            m = 0.f;
+            dmv = 0.f;
             if (s <= t && t < nv) {
                 m = (s == t) ? gam[t] : expf(lcs[t] - lcs[s]) * wgt[s];
 #pragma unroll
@@ -1082,8 +1120,28 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                         dmv += dP[idx] * Sc[idx];
                     }
             }
+        };
+        for (int e = tid; e < Cb * Cb; e += NT) {  // rows: lane s of the group
+            const int t = e / Cb, s = e % Cb;
+            float m, dmv;
+            mask_at(t, s, m, dmv);
             Mk[e] = m;
             dMk[e] = dmv;
+            const float rs_ = group_sum<Cb>((s < t) ? dmv * m : 0.f);
+            if (s == 0) dcr[t] = rs_;
+            if (s == t) dgv[t] = dmv;
+        }
+        for (int e = tid; e < Cb * Cb; e += NT) {  // columns: lane t2 of the group
+            const int t = e / Cb, t2 = e % Cb;
+            float m, dmv;
+            mask_at(t2, t, m, dmv);
+            const bool after = t2 > t;
+            const float cc = group_sum<Cb>(after ? -dmv * m : 0.f);
+            const float cw = group_sum<Cb>(after ? dmv * expf(lcs[t2] - lcs[t]) : 0.f);
+            if (t2 == 0) {
+                dcs[t] = cc;
+                dwv[t] = cw;
+            }
         }
         __syncthreads();
         for (int e = tid; e < T * T; e += NT) {
@@ -1102,7 +1160,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                 const int kk = k0 + 4 * lg;
                 ci = mfma4(ld_str(&Sc[kk * TS + 16 * st + lr], TS), ld_str(&dYs[kk * PS + 16 * pt + lr], PS), ci);
             }
-#pragma unroll
+#pragma unroll 2
             for (int k0 = 0; k0 < N; k0 += 16) {
                 const int kk = k0 + 4 * lg;
                 cs_ = mfma4(ld4(&Bb[(16 * st + lr) * NS + kk]), ld_str(&dSl[kk * PS + 16 * pt + lr], PS), cs_);
@@ -1116,6 +1174,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                     ba.dx[(((bi * L + c0 + s) * H + hi) * R + sg % R) * P + 16 * pt + lr] = ci[jj] + Ew[s] * cs_[jj];
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
         // (5) dC_bar += MdP B_bar, dB_bar = MdP^T C_bar + E_sigma x dS^T, for the column pair
         {
             f4 dB[2], dBs[2];
@@ -1131,7 +1190,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                     const int kk = k0 + 4 * lg;
                     b = mfma4(ld_str(&dP[kk * TS + 16 * rt + lr], TS), ld_str(&Cc[kk * NS + 16 * nt + lr], NS), b);
                 }
-#pragma unroll
+#pragma unroll 2
                 for (int k0 = 0; k0 < P; k0 += 16) {
                     const int kk = k0 + 4 * lg;
                     bs = mfma4(ld4(&Xs[(16 * rt + lr) * PS + kk]), ld4(&dSl[(16 * nt + lr) * PS + kk]), bs);
@@ -1169,6 +1228,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                 dPh[((16 * rt + 4 * lg) / R + u) * (HALF + 1) + i] = v;
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
         // (6) dS <- e^{cs_end} dS + sum_rho e^{cs_t} C_bar[rho]^T dY[rho] (accumulators; the LDS copy is
         //     still read above by other waves, so it is rewritten after the barrier)
         {
@@ -1192,58 +1252,61 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) dSl[(16 * w + 4 * lg + jj) * PS + 16 * pt + lr] = acc[pt][jj];
-        for (int j = tid; j < Cb + HALF; j += NT) {
-            if (j < Cb) {
-                const int t = j;
-                float dc = 0.f, dw = 0.f, dg = 0.f;
-                if (t < nv) {
-                    float Qt = 0.f, off = 0.f;
+        // angle gradients: per channel, the suffix over the chunk's tokens (lanes 32h + t) plus the
+        // carry from later chunks; d theta = dt * suffix; the dt term sum_i theta * suffix per token
+        {
+            float dth_acc = 0.f;
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            Qt += Qp[(t * R + r) * 4 + q];
-                            off += offq[(t * R + r) * 4 + q];
-                        }
-                    dc = off;
-                    for (int s = 0; s < t; ++s) dc += dMk[t * Cb + s] * Mk[t * Cb + s];
-                    for (int t2 = t + 1; t2 < nv; ++t2) {
-                        dc -= dMk[t2 * Cb + t] * Mk[t2 * Cb + t];
-                        dw += dMk[t2 * Cb + t] * expf(lcs[t2] - lcs[t]);
-                    }
-                    dc -= Ew[t] * Qt;
-                    dw += Ee[t] * Qt;
-                    if (t == nv - 1) dc += misc[0];
-                    dg = dMk[t * Cb + t];
-                }
-                dcs[t] = dc;
-                dwv[t] = dw;
-                dgv[t] = dg;
-            } else {
-                const int i = j - Cb;
-                float rc = rcar[i];
-                for (int t = nv - 1; t >= 0; --t) {
-                    rc += dPh[t * (HALF + 1) + i];
+            for (int m = 0; m < HALF / 16; ++m) {
+                const int i = 8 * w + 2 * m + (l >> 5), t = l & 31;
+                const bool v_ = t < nv;
+                const float d = v_ ? dPh[t * (HALF + 1) + i] : 0.f;
+                const float incl = group_scan<32>(d, l);
+                const float tot = group_sum<32>(d);
+                const float rc = rcar[i] + tot - incl + d;  // sum over tokens >= t
+                if (v_) {
                     const int64_t tok = bi * L + c0 + t;
                     ba.gth[(tok * H + hi) * HALF + i] = dtv[t] * rc;
-                    dPh[t * (HALF + 1) + i] = thv[t * HALF + i] * rc;
+                    dth_acc += thv[t * HALF + i] * rc;
                 }
-                rcar[i] = rc;
+                if (t == 0) rcar[i] += tot;
+            }
+            // lanes t and 32 + t hold different channels of the same token
+            const float other = __shfl_xor(dth_acc, 32);
+            if (l < 32) dthp[w * T + l] = dth_acc + other;
+        }
+        __syncthreads();
+        // token scalars and records: wave 0, lane t; suffix sums of d cs in registers
+        if (w == 0 && l < 32) {
+            const int t = l;
+            const bool v_ = t < nv;
+            float dc = 0.f, dw = 0.f, dg = 0.f, dth = 0.f;
+            if (v_) {
+                float Qt = 0.f, off = 0.f;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        Qt += Qp[(t * R + r) * 4 + q];
+                        off += offq[(t * R + r) * 4 + q];
+                    }
+                dc = off + dcr[t] + dcs[t] - Ew[t] * Qt;
+                if (t == nv - 1) dc += misc[0];
+                dw = dwv[t] + Ee[t] * Qt;
+                dg = dgv[t];
+#pragma unroll
+                for (int ww = 0; ww < 8; ++ww) dth += dthp[ww * T + t];
+            }
+            const float incl = group_scan<32>(dc, l);
+            const float da = group_sum<32>(dc) - incl + dc;  // sum over tokens >= t
+            if (v_) {
+                float *rec = ba.tok + ((bi * L + c0 + t) * H + hi) * 4;
+                rec[0] = da;
+                rec[1] = dw;
+                rec[2] = dg;
+                rec[3] = dth;
             }
         }
-        __syncthreads();
-        for (int t = tid; t < nv; t += NT) {
-            float da = 0.f;
-            for (int t2 = t; t2 < nv; ++t2) da += dcs[t2];
-            float dth = 0.f;
-            for (int i = 0; i < HALF; ++i) dth += dPh[t * (HALF + 1) + i];
-            float *rec = ba.tok + ((bi * L + c0 + t) * H + hi) * 4;
-            rec[0] = da;
-            rec[1] = dwv[t];
-            rec[2] = dgv[t];
-            rec[3] = dth;
-        }
-        __syncthreads();
     }
 
     // ---- chain start: dh0 and the previous token's fold (dS is in dSl)
