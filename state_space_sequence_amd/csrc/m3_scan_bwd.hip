@@ -727,6 +727,7 @@ __host__ __device__ constexpr size_t smem_floats() {
            + 8 * (size_t)T           // offq [T][4], Qp [T][4]
            + 13 * (size_t)(T + 1)    // token scalars
            + 8 * (size_t)T           // per-wave partial sums of theta * suffix, per token
+           + 4 * 2 * (size_t)N + 2 * (size_t)N  // biases [2][R][N] (R <= 4) and gains [2][N]
            + 2 * (size_t)T           // 1/rms rows
            + 2 * (size_t)HALF        // carry, rcar
            + NT + 4;
@@ -783,9 +784,19 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     float *rcar = carry + HALF;       // [HALF]
     float *red = rcar + HALF;         // [NT]
     float *misc = red + NT;           // [4]
+    float *sbias = misc + 4;          // [2][R][N] B / C bias of this head
+    float *sgain = sbias + 8 * N;     // [2][N] BCNorm gains (ones when absent)
 
     float *chk = ba.chk + bh * (int64_t)(nch + 1) * slotf;
-    const float *wB = a.B_normw, *wC = a.C_normw;
+    for (int e = tid; e < 2 * R * N; e += NT) {
+        const int which = e / (R * N), rem = e % (R * N);
+        sbias[e] = (which == 0 ? a.B_bias : a.C_bias)[hi * R * N + rem];
+    }
+    for (int e = tid; e < 2 * N; e += NT) {
+        const float *src = (e < N) ? a.B_normw : a.C_normw;
+        sgain[e] = src ? src[e % N] : 1.f;
+    }
+    __syncthreads();
 
     // ---- staging (as in bwd_chain_kernel, with N, P fixed)
     auto stage_chunk = [&](int64_t c0, int nv, bool withC) {
@@ -875,17 +886,17 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             const int t = rho / R, r = rho % R;
             float bl = 0.f, bhv = 0.f, cl = 0.f, chv = 0.f;
             if (t < nv) {
-                const float *bb = a.B_bias + (hi * R + r) * N;
+                const float *bb = sbias + r * N;
                 float sn, cs;
                 sincospif(2.f * Phi[t * HALF + i], &sn, &cs);
-                const float B0 = Bb[rho * NS + i] * rsB[rho] * (wB ? wB[i] : 1.f) + bb[i];
-                const float B1 = Bb[rho * NS + i + HALF] * rsB[rho] * (wB ? wB[i + HALF] : 1.f) + bb[i + HALF];
+                const float B0 = Bb[rho * NS + i] * rsB[rho] * sgain[i] + bb[i];
+                const float B1 = Bb[rho * NS + i + HALF] * rsB[rho] * sgain[i + HALF] + bb[i + HALF];
                 bl = cs * B0 + sn * B1;
                 bhv = -sn * B0 + cs * B1;
                 if (withC) {
-                    const float *cb = a.C_bias + (hi * R + r) * N;
-                    const float C0 = Cc[rho * NS + i] * rsC[rho] * (wC ? wC[i] : 1.f) + cb[i];
-                    const float C1 = Cc[rho * NS + i + HALF] * rsC[rho] * (wC ? wC[i + HALF] : 1.f) + cb[i + HALF];
+                    const float *cb = sbias + (R + r) * N;
+                    const float C0 = Cc[rho * NS + i] * rsC[rho] * sgain[N + i] + cb[i];
+                    const float C1 = Cc[rho * NS + i + HALF] * rsC[rho] * sgain[N + i + HALF] + cb[i + HALF];
                     cl = cs * C0 + sn * C1;
                     chv = -sn * C0 + cs * C1;
                 }
@@ -920,7 +931,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         __syncthreads();
         for (int e = tid; e < R * N; e += NT) {
             const int r = e / N, n = e % N;
-            pB[r * NS + n] = pB[r * NS + n] * rsB[r] * (wB ? wB[n] : 1.f) + a.B_bias[(hi * R + r) * N + n];
+            pB[r * NS + n] = pB[r * NS + n] * rsB[r] * sgain[n] + sbias[r * N + n];
         }
         __syncthreads();
     };
@@ -1026,21 +1037,42 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
 
     // wave roles for the [T][N] tiles: rows 16*rt.., columns 16*nt0.. and 16*(nt0+4).. (a rotation pair)
     const int rt = w >> 2, nt0 = w & 3;
+    // S_out of the chunk being processed, in the fragment layout of (1): rows n = 16 (nt0 + 4q) + lr,
+    // columns p = 16 kb + 4 lg + j. The first is S_final; after that, the previous chunk's S_in.
+    f4 uprev[2][4];
+    {
+        const float *slotf_ = chk + (int64_t)nch * slotf;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                uprev[q][kb] = *reinterpret_cast<const f4 *>(&slotf_[(16 * (nt0 + 4 * q) + lr) * P + 16 * kb + 4 * lg]);
+    }
     for (int k = nch - 1; k >= 0; --k) {
         const int l = opaque(tid & 63), lr = l & 15, lg = l >> 4;
         const int64_t c0 = (int64_t)k * Cb;
         const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
         const float *slot = chk + (int64_t)k * slotf;
-        const float *slot1 = chk + (int64_t)(k + 1) * slotf;
+        // S_in fragments of (1), in flight during the staging
+        f4 uin[2][4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                uin[q][kb] = *reinterpret_cast<const f4 *>(&slot[(16 * (nt0 + 4 * q) + lr) * P + 16 * kb + 4 * lg]);
         for (int i = tid; i < HALF; i += NT) carry[i] = slot[N * P + i];
-        // <S_out, dS> from the accumulators
+        // <S_out, dS>: S_out fragments in registers, dS in LDS (waves 4..7 hold the same fragments)
         {
             float part = 0.f;
+            if (rt == 0) {
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
+                for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) part += acc[pt][jj] * slot1[(16 * w + 4 * lg + jj) * P + 16 * pt + lr];
-            red[tid] = part;
+                    for (int kb = 0; kb < 4; ++kb)
+                        part = dot4(uprev[q][kb], ld4(&dSl[(16 * (nt0 + 4 * q) + lr) * PS + 16 * kb + 4 * lg]), part);
+            }
+            part = wave_sum(part);
+            if (l == 0) red[w] = part;
         }
         stage_chunk(c0, nv, true);
         const float cse = lcs[nv - 1];
@@ -1052,16 +1084,16 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             const int nt = nt0 + 4 * q;
             f4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k0 = 0; k0 < P; k0 += 16) {
-                const int kk = k0 + 4 * lg;
-                const f4 av = ld4(&dYs[(16 * rt + lr) * PS + kk]);
-                const f4 bv = *reinterpret_cast<const f4 *>(&slot[(16 * nt + lr) * P + kk]);
-                c = mfma4(av, bv, c);
-            }
+            for (int kb = 0; kb < 4; ++kb) c = mfma4(ld4(&dYs[(16 * rt + lr) * PS + 16 * kb + 4 * lg]), uin[q][kb], c);
+            (void)nt;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) c[jj] *= ecs[(16 * rt + 4 * lg + jj) / R];
             dC[q] = c;
         }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) uprev[q][kb] = uin[q][kb];
         __builtin_amdgcn_sched_barrier(0);
         // off-term part of d cs: sum_n C_bar[rho][n] dCoff[rho][n], per row, this wave's 32 columns
 #pragma unroll
@@ -1099,7 +1131,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         }
         if (tid == 0) {
             float sod = 0.f;
-            for (int j = 0; j < NT; ++j) sod += red[j];
+            for (int j = 0; j < NT / 64; ++j) sod += red[j];
             misc[0] = sod;
         }
         __syncthreads();
