@@ -798,50 +798,104 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     }
     __syncthreads();
 
-    // ---- staging (as in bwd_chain_kernel, with N, P fixed)
-    auto stage_chunk = [&](int64_t c0, int nv, bool withC) {
-        for (int t = tid; t <= Cb; t += NT) {
-            float d = 0.f, lm = 0.f, av = 0.f;
-            if (t <= nv && c0 + t < L) {
-                const int64_t o = (bi * L + c0 + t) * H + hi;
-                d = a.dt[o];
-                lm = a.lam[o];
-                av = a.A[o];
+    // ---- staging (as in bwd_chain_kernel, with N, P fixed). Every global load of a chunk is
+    // issued before any of them is stored to LDS, so the chunk waits for memory once.
+    constexpr int KBC = T * N / NT, KXY = T * P / NT, KPH = (T * HALF + NT - 1) / NT;
+    struct StageRegs {
+        float vb[KBC], vc[KBC], vx[KXY], vy[KXY], vph[KPH], vth[KPH];
+        float d, lm, av;
+    };
+    // loads of a chunk's inputs into registers (they can be in flight during other work)
+    auto stage_issue = [&](int64_t c0, int nv, bool withC, StageRegs &sr) {
+        sr.d = 0.f;
+        sr.lm = 0.f;
+        sr.av = 0.f;
+        if (tid <= Cb && tid <= nv && c0 + tid < L) {
+            const int64_t o = (bi * L + c0 + tid) * H + hi;
+            sr.d = a.dt[o];
+            sr.lm = a.lam[o];
+            sr.av = a.A[o];
+        }
+        // The loads of a thread step through the chunk with a fixed token stride: row
+        // rho = rho0 + (NT / N) kk, i.e. token t0 + (NT / N / R) kk, same rank (R divides NT / N).
+        // Rows past the chunk's last token read that token's row instead (always in bounds)
+        // and are zeroed afterwards: no branch around a load, so the loads stay in flight
+        // together instead of each being waited for at the end of its own branch.
+        {
+            constexpr int DT = NT / N / R;
+            const int rho0 = tid / N, n = tid % N, t0 = rho0 / R, r = rho0 % R;
+            const int64_t rowb = ((bi * L + c0) * G + g) * R + r;  // row of token 0, rank r
+#pragma unroll
+            for (int kk = 0; kk < KBC; ++kk) {
+                const int t = t0 + DT * kk;
+                const bool v_ = t < nv;
+                const int64_t o = (rowb + (int64_t)(v_ ? t : nv - 1) * G * R) * N + n;
+                const float fb = ld_io<BF16>(a.Braw, o);
+                const float fc = withC ? ld_io<BF16>(a.Craw, o) : 0.f;
+                sr.vb[kk] = v_ ? fb : 0.f;
+                sr.vc[kk] = v_ ? fc : 0.f;
             }
-            dtv[t] = d;
-            lamv[t] = lm;
-            Av[t] = av;
         }
-        for (int e = tid; e < T * N; e += NT) {
-            const int rho = e / N, n = e % N;
-            const int t = rho / R, r = rho % R;
-            float vb = 0.f, vc = 0.f;
-            if (t < nv) {
-                const int64_t row = (((bi * L + c0 + t) * G + g) * R + r) * N;
-                vb = ld_io<BF16>(a.Braw, row + n);
-                if (withC) vc = ld_io<BF16>(a.Craw, row + n);
+        {
+            constexpr int DT = NT / P / R;
+            const int rho0 = tid / P, p = tid % P, t0 = rho0 / R, r = rho0 % R;
+            const int64_t rowb = ((bi * L + c0) * H + hi) * R + r;
+#pragma unroll
+            for (int kk = 0; kk < KXY; ++kk) {
+                const int t = t0 + DT * kk;
+                const bool v_ = t < nv;
+                const int64_t o = (rowb + (int64_t)(v_ ? t : nv - 1) * H * R) * P + p;
+                const float fx = ld_io<BF16>(a.x, o);
+                const float fy = withC ? ld_io<BF16>(ba.dy, o) : 0.f;
+                sr.vx[kk] = v_ ? fx : 0.f;
+                sr.vy[kk] = v_ ? fy : 0.f;
             }
-            Bb[rho * NS + n] = vb;
-            Cc[rho * NS + n] = vc;
         }
-        for (int e = tid; e < T * P; e += NT) {
-            const int rho = e / P, p = e % P;
-            const int t = rho / R, r = rho % R;
-            const int64_t o = (((bi * L + c0 + t) * H + hi) * R + r) * P + p;
-            Xs[rho * PS + p] = (t < nv) ? ld_io<BF16>(a.x, o) : 0.f;
-            dYs[rho * PS + p] = (withC && t < nv) ? ld_io<BF16>(ba.dy, o) : 0.f;
-        }
-        for (int e = tid; e < Cb * HALF; e += NT) {
-            const int t = e / HALF, i = e % HALF;
-            float v = 0.f, th = 0.f;
-            if (t < nv) {
-                const int64_t tok = bi * L + c0 + t;
-                th = a.theta[(tok * G + g) * HALF + i];
-                v = a.dt[tok * H + hi] * th * kInv2Pi;
+        {
+            constexpr int DT = NT / HALF;
+            const int t0 = tid / HALF, i = tid % HALF;
+#pragma unroll
+            for (int kk = 0; kk < KPH; ++kk) {
+                const int t = t0 + DT * kk;
+                const bool v_ = t < nv;
+                const int64_t tok = bi * L + c0 + (v_ ? t : nv - 1);
+                const float th = a.theta[(tok * G + g) * HALF + i];
+                const float d = a.dt[tok * H + hi];
+                sr.vth[kk] = v_ ? th : 0.f;
+                sr.vph[kk] = v_ ? d : 0.f;  // dt of the token (the product is formed when stored)
             }
-            Phi[e] = v;
-            thv[e] = th;
         }
+    };
+    // the registers into LDS
+    auto stage_put = [&](int nv, const StageRegs &sr) {
+        if (tid <= Cb) {
+            dtv[tid] = sr.d;
+            lamv[tid] = sr.lm;
+            Av[tid] = sr.av;
+        }
+#pragma unroll
+        for (int kk = 0; kk < KBC; ++kk) {
+            const int e = tid + kk * NT;
+            Bb[(e / N) * NS + e % N] = sr.vb[kk];
+            Cc[(e / N) * NS + e % N] = sr.vc[kk];
+        }
+#pragma unroll
+        for (int kk = 0; kk < KXY; ++kk) {
+            const int e = tid + kk * NT;
+            Xs[(e / P) * PS + e % P] = sr.vx[kk];
+            dYs[(e / P) * PS + e % P] = sr.vy[kk];
+        }
+#pragma unroll
+        for (int kk = 0; kk < KPH; ++kk) {
+            const int e = tid + kk * NT;
+            if (e < Cb * HALF) {
+                Phi[e] = sr.vph[kk] * sr.vth[kk] * kInv2Pi;
+                thv[e] = sr.vth[kk];
+            }
+        }
+    };
+    // prefix scans, row norms, rotation (three barriers)
+    auto stage_finish = [&](int64_t c0, int nv, bool withC) {
         __syncthreads();
         // decay prefix over the tokens (wave 0, lane t) and angle prefixes (every wave, two
         // channels per pass, lanes 32h + t): DPP scans instead of serial walks
@@ -908,6 +962,12 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         }
         __syncthreads();
     };
+    auto stage_chunk = [&](int64_t c0, int nv, bool withC) {
+        StageRegs sr;
+        stage_issue(c0, nv, withC, sr);
+        stage_put(nv, sr);
+        stage_finish(c0, nv, withC);
+    };
 
     // previous token's normalised, biased B rows ([R][NS] in Sc) and x rows ([R][PS] in dP)
     float *pB = Sc, *pX = dP;
@@ -960,18 +1020,25 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) acc[pt][jj] = dSl[(16 * w + 4 * lg + jj) * PS + 16 * pt + lr];
 
-    // ---- forward sweep
+    // ---- forward sweep (each chunk's inputs are loaded during the previous chunk)
+    StageRegs fsr;
+    if (nch > 0) stage_issue(0, (int)(L < Cb ? L : Cb), false, fsr);
     for (int k = 0; k < nch; ++k) {
         const int l = opaque(tid & 63), lr = l & 15, lg = l >> 4;
         const int64_t c0 = (int64_t)k * Cb;
         const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
         float *slot = chk + (int64_t)k * slotf;
+        stage_put(nv, fsr);
+        if (k + 1 < nch) {
+            const int64_t c1 = c0 + Cb;
+            stage_issue(c1, (int)((L - c1) < Cb ? (L - c1) : Cb), false, fsr);
+        }
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) slot[(16 * w + 4 * lg + jj) * P + 16 * pt + lr] = acc[pt][jj];
         for (int i = tid; i < HALF; i += NT) slot[N * P + i] = carry[i];
-        stage_chunk(c0, nv, false);
+        stage_finish(c0, nv, false);
         // S <- e^{cs_end} S + sum_sigma (E B_bar)^T x: A[n][sigma] = E_s B_bar[sigma][n], B[sigma][p] = x
         const float dec = expf(lcs[nv - 1]);
 #pragma unroll
