@@ -682,6 +682,14 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
+// sine and cosine of an angle given in revolutions, by the hardware v_sin / v_cos
+// (which take revolutions) after reducing to [0, 1)
+__device__ __forceinline__ void sincos_rev(float x, float *sn, float *cs) {
+    const float r = __builtin_amdgcn_fractf(x);
+    *sn = __builtin_amdgcn_sinf(r);
+    *cs = __builtin_amdgcn_cosf(r);
+}
+
 // a value the compiler cannot see through: lane-derived addresses computed from it
 // inside the chunk loops are rebuilt each chunk instead of being hoisted and kept
 // live (or spilled) across the loop
@@ -942,7 +950,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             if (t < nv) {
                 const float *bb = sbias + r * N;
                 float sn, cs;
-                sincospif(2.f * Phi[t * HALF + i], &sn, &cs);
+                sincos_rev(Phi[t * HALF + i], &sn, &cs);
                 const float B0 = Bb[rho * NS + i] * rsB[rho] * sgain[i] + bb[i];
                 const float B1 = Bb[rho * NS + i + HALF] * rsB[rho] * sgain[i + HALF] + bb[i + HALF];
                 bl = cs * B0 + sn * B1;
@@ -1072,7 +1080,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         float rg = 0.f;
         if (ba.dh_final) {
             float sn, cs;
-            sincospif(2.f * carry[i], &sn, &cs);
+            sincos_rev(carry[i], &sn, &cs);
             for (int p = 0; p < P; ++p) {
                 const float hl = ba.dh_final[(bh * P + p) * N + i], hh = ba.dh_final[(bh * P + p) * N + i + HALF];
                 const float su = dSl[i * PS + p], sv = dSl[(i + HALF) * PS + p];
@@ -1088,7 +1096,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         float dlo = 0.f, dhi = 0.f;
         if (ba.dh_final) {
             float sn, cs;
-            sincospif(2.f * carry[i], &sn, &cs);
+            sincos_rev(carry[i], &sn, &cs);
             const float hl = ba.dh_final[(bh * P + p) * N + i], hh = ba.dh_final[(bh * P + p) * N + i + HALF];
             dlo = cs * hl + sn * hh;
             dhi = -sn * hl + cs * hh;
@@ -1310,7 +1318,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                                dch * Cc[rho * NS + i];
                 if (t < nv) {
                     float sn, cs;
-                    sincospif(2.f * Phi[t * HALF + i], &sn, &cs);
+                    sincos_rev(Phi[t * HALF + i], &sn, &cs);
                     const int64_t o = (((bi * L + c0 + t) * H + hi) * R + r) * N;
                     ba.gB[o + i] = cs * dbl - sn * dbh;
                     ba.gB[o + i + HALF] = sn * dbl + cs * dbh;
