@@ -113,6 +113,7 @@ struct BwdArgs {
     float *tok;   // [b,L,H,4]   d(dt A), dw, dgamma, dt's angle term
     float *gBp;   // [b,H,R,N]   previous token's dB (per head)
     float *fold;  // [b,H]       gradient of the fold factor (1 - lam_0) dt_0
+    float *bpart; // [b,H][2][R][2][N] matrix-core chain kernel: per-chain bias sums (row tile, rank, B / C)
 };
 
 // NF, PF: N and P fixed at compile time (0: taken from the arguments)
@@ -738,7 +739,8 @@ __host__ __device__ constexpr size_t smem_floats() {
            + 4 * 2 * (size_t)N + 2 * (size_t)N  // biases [2][R][N] (R <= 4) and gains [2][N]
            + 2 * (size_t)T           // 1/rms rows
            + 2 * (size_t)HALF        // carry, rcar
-           + NT + 4;
+           + NT + 4
+           + 4 * (size_t)NT;         // per-lane bias sums [R][NT]
 }
 }  // namespace mf
 
@@ -794,6 +796,9 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     float *misc = red + NT;           // [4]
     float *sbias = misc + 4;          // [2][R][N] B / C bias of this head
     float *sgain = sbias + 8 * N;     // [2][N] BCNorm gains (ones when absent)
+    float *sbacc = sgain + 2 * N;     // [R][NT] this lane's bias sums over the chunks done so far
+#pragma unroll
+    for (int r = 0; r < R; ++r) sbacc[r * NT + tid] = 0.f;
 
     float *chk = ba.chk + bh * (int64_t)(nch + 1) * slotf;
     for (int e = tid; e < 2 * R * N; e += NT) {
@@ -1308,6 +1313,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             }
             const int i = 16 * nt0 + lr;  // channel of the pair (i, i + 64)
             float dphi_tok[4] = {0.f, 0.f, 0.f, 0.f};
+            float bsum[R][4] = {};  // per rank (rho % R == jj % R): B lo, B hi, C lo, C hi
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int rho = 16 * rt + 4 * lg + jj, t = rho / R, r = rho % R;
@@ -1320,10 +1326,28 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                     float sn, cs;
                     sincos_rev(Phi[t * HALF + i], &sn, &cs);
                     const int64_t o = (((bi * L + c0 + t) * H + hi) * R + r) * N;
-                    ba.gB[o + i] = cs * dbl - sn * dbh;
-                    ba.gB[o + i + HALF] = sn * dbl + cs * dbh;
-                    ba.gC[o + i] = cs * dcl - sn * dch;
-                    ba.gC[o + i + HALF] = sn * dcl + cs * dch;
+                    const float gbl = cs * dbl - sn * dbh, gbh = sn * dbl + cs * dbh;
+                    const float gcl = cs * dcl - sn * dch, gch = sn * dcl + cs * dch;
+                    ba.gB[o + i] = gbl;
+                    ba.gB[o + i + HALF] = gbh;
+                    ba.gC[o + i] = gcl;
+                    ba.gC[o + i + HALF] = gch;
+                    bsum[jj % R][0] += gbl;
+                    bsum[jj % R][1] += gbh;
+                    bsum[jj % R][2] += gcl;
+                    bsum[jj % R][3] += gch;
+                }
+            }
+            // bias sums: the four lane groups of the wave hold the same channels on
+            // different rows; a reduce-scatter over them leaves component lg (B lo,
+            // B hi, C lo, C hi) summed over the wave's 16 rows in lane group lg
+            {
+                const bool hi2 = (lg & 2) != 0, lo1 = (lg & 1) != 0;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float k0 = (hi2 ? bsum[r][2] : bsum[r][0]) + __shfl_xor(hi2 ? bsum[r][0] : bsum[r][2], 32);
+                    const float k1 = (hi2 ? bsum[r][3] : bsum[r][1]) + __shfl_xor(hi2 ? bsum[r][1] : bsum[r][3], 32);
+                    sbacc[r * NT + tid] += (lo1 ? k1 : k0) + __shfl_xor(lo1 ? k0 : k1, 16);
                 }
             }
             // the lane's 4 rows are 4/R whole tokens: sum the ranks of each token
@@ -1416,6 +1440,15 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         }
     }
 
+    // the chain's bias sums: lane group lg of wave w holds component lg of row tile
+    // rt over channel 16 nt0 + lr (+ 64 for the high halves)
+    {
+        const int n = 16 * nt0 + lr + HALF * (lg & 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            ba.bpart[(((bh * 2 + rt) * R + r) * 2 + (lg >> 1)) * N + n] = sbacc[r * NT + tid];
+    }
+
     // ---- chain start: dh0 and the previous token's fold (dS is in dSl)
     if (ba.dh0) {
         for (int e = tid; e < N * P; e += NT) {
@@ -1460,94 +1493,79 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
 // Also writes, per row, Braw rs dv (the gain's gradient terms, summed later).
 // One workgroup per (row block): rows are (batch, token, group) for the
 // sequence, or (batch, group) for the previous token (prev = true).
+// BCNorm's backward per raw row ((batch, token), group, rank), one wave per row and
+// two adjacent channels per lane: dB and dC are first summed over the heads of the
+// group (eight heads of loads in flight per lane), then
+//   d Braw = rs w dB - Braw rs^3 / N * sum_n(Braw w dB),   rs = 1 / sqrt(mean(Braw^2) + eps)
+// and the gain term Braw rs dB is kept per row for the column sums. The previous
+// token's rows (prev) read the per-head fold rows instead and have no C part.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void bwd_group_kernel(BwdArgs ba, bool prev, float *gWB, float *gWC,
-                                                             float *dBraw_out, float *dCraw_out) {
+__global__ __launch_bounds__(kThreads) void bwd_group_kernel(BwdArgs ba, bool prev, int64_t nrows, float *gWB,
+                                                             float *gWC, float *dBraw_out, float *dCraw_out) {
     const ScanArgs &a = ba.f;
-    const int N = (int)a.N, R = (int)a.R, half = N / 2;
-    const int64_t H = a.H, G = a.G, hpg = H / G;
-    const int64_t row = blockIdx.x;  // (b, t, g) or (b, g)
-    const int tid = threadIdx.x;
-    __shared__ float red[2][kThreads];
-    __shared__ float tot[2];
-    const int64_t g = row % G;
-    const int64_t bt = row / G;  // b * L + t, or b
-    for (int r = 0; r < R; ++r) {
-        // one pass per rank row: N channels over the threads
-        const int64_t rawrow = (row * R + r) * N;
-        float ssb = 0.f, ssc = 0.f;
-        for (int n = tid; n < N; n += kThreads) {
-            const float vb = ld_io<BF16>(prev ? a.Braw_prev : a.Braw, rawrow + n);
-            ssb += vb * vb;
+    const int N = (int)a.N;
+    const int64_t R = a.R, H = a.H, G = a.G, hpg = H / G;
+    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (row >= nrows) return;  // a whole wave; the kernel has no barrier
+    const int l = threadIdx.x & 63;
+    const int64_t r = row % R, bg = row / R, g = bg % G, bt = bg / G;
+    const int n = 2 * l;
+    const bool on = n < N;  // N is even
+    const int nc = on ? n : 0;
+    const int64_t h0 = ((bt * H + g * hpg) * R + r) * N + nc, hstride = R * N;
+    const float *pB = (prev ? ba.gBp : ba.gB) + h0;
+    const float *pC = ba.gC + h0;
+    float2 sb = {0.f, 0.f}, sc = {0.f, 0.f};
+    int64_t h = 0;
+    for (; h + 8 <= hpg; h += 8) {
+        float2 vb[8], vc[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            vb[k] = *reinterpret_cast<const float2 *>(pB + (h + k) * hstride);
+            if (!prev) vc[k] = *reinterpret_cast<const float2 *>(pC + (h + k) * hstride);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            sb.x += vb[k].x;
+            sb.y += vb[k].y;
             if (!prev) {
-                const float vc = ld_io<BF16>(a.Craw, rawrow + n);
-                ssc += vc * vc;
+                sc.x += vc[k].x;
+                sc.y += vc[k].y;
             }
         }
-        red[0][tid] = ssb;
-        red[1][tid] = ssc;
-        __syncthreads();
-        if (tid == 0) {
-            float s0 = 0.f, s1 = 0.f;
-            for (int j = 0; j < kThreads; ++j) {
-                s0 += red[0][j];
-                s1 += red[1][j];
-            }
-            tot[0] = 1.0f / sqrtf(s0 / (float)N + a.eps);
-            tot[1] = 1.0f / sqrtf(s1 / (float)N + a.eps);
-        }
-        __syncthreads();
-        const float rsb = tot[0], rsc = tot[1];
-        float db_keep[4] = {0.f, 0.f, 0.f, 0.f}, dc_keep[4] = {0.f, 0.f, 0.f, 0.f};  // N <= 4 * kThreads / 2
-        float pb = 0.f, pc = 0.f;
-        int kk = 0;
-        for (int n = tid; n < N; n += kThreads, ++kk) {
-            float sb = 0.f, sc = 0.f;
-            for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {
-                if (prev) {
-                    sb += ba.gBp[((bt * H + h) * R + r) * N + n];
-                } else {
-                    const int64_t o = ((bt * H + h) * R + r) * N + n;
-                    sb += ba.gB[o];
-                    sc += ba.gC[o];
-                }
-            }
-            db_keep[kk] = sb;
-            dc_keep[kk] = sc;
-            const float wbn = a.B_normw ? a.B_normw[n] : 1.f, wcn = a.C_normw ? a.C_normw[n] : 1.f;
-            const float vb = ld_io<BF16>(prev ? a.Braw_prev : a.Braw, rawrow + n);
-            pb += vb * wbn * sb;
-            if (!prev) pc += ld_io<BF16>(a.Craw, rawrow + n) * wcn * sc;
-        }
-        __syncthreads();
-        red[0][tid] = pb;
-        red[1][tid] = pc;
-        __syncthreads();
-        if (tid == 0) {
-            float s0 = 0.f, s1 = 0.f;
-            for (int j = 0; j < kThreads; ++j) {
-                s0 += red[0][j];
-                s1 += red[1][j];
-            }
-            tot[0] = s0;
-            tot[1] = s1;
-        }
-        __syncthreads();
-        kk = 0;
-        for (int n = tid; n < N; n += kThreads, ++kk) {
-            const float wbn = a.B_normw ? a.B_normw[n] : 1.f, wcn = a.C_normw ? a.C_normw[n] : 1.f;
-            const float vb = ld_io<BF16>(prev ? a.Braw_prev : a.Braw, rawrow + n);
-            dBraw_out[rawrow + n] = rsb * wbn * db_keep[kk] - vb * rsb * rsb * rsb / (float)N * tot[0];
-            gWB[rawrow + n] = vb * rsb * db_keep[kk];
-            if (!prev) {
-                const float vc = ld_io<BF16>(a.Craw, rawrow + n);
-                dCraw_out[rawrow + n] = rsc * wcn * dc_keep[kk] - vc * rsc * rsc * rsc / (float)N * tot[1];
-                gWC[rawrow + n] = vc * rsc * dc_keep[kk];
-            }
-        }
-        __syncthreads();
     }
-    (void)half;
+    for (; h < hpg; ++h) {
+        const float2 vb = *reinterpret_cast<const float2 *>(pB + h * hstride);
+        sb.x += vb.x;
+        sb.y += vb.y;
+        if (!prev) {
+            const float2 vc = *reinterpret_cast<const float2 *>(pC + h * hstride);
+            sc.x += vc.x;
+            sc.y += vc.y;
+        }
+    }
+    const int64_t raw = row * N + nc;
+    const void *Bsrc = prev ? a.Braw_prev : a.Braw;
+    const float b0 = on ? ld_io<BF16>(Bsrc, raw) : 0.f, b1 = on ? ld_io<BF16>(Bsrc, raw + 1) : 0.f;
+    const float wb0 = a.B_normw ? a.B_normw[nc] : 1.f, wb1 = a.B_normw ? a.B_normw[nc + 1] : 1.f;
+    const float rsb = 1.0f / sqrtf(wave_sum(b0 * b0 + b1 * b1) / (float)N + a.eps);
+    const float kb = wave_sum(b0 * wb0 * sb.x + b1 * wb1 * sb.y) * rsb * rsb * rsb / (float)N;
+    float c0 = 0.f, c1 = 0.f, wc0 = 1.f, wc1 = 1.f, rsc = 0.f, kc = 0.f;
+    if (!prev) {
+        c0 = on ? ld_io<BF16>(a.Craw, raw) : 0.f;
+        c1 = on ? ld_io<BF16>(a.Craw, raw + 1) : 0.f;
+        wc0 = a.C_normw ? a.C_normw[nc] : 1.f;
+        wc1 = a.C_normw ? a.C_normw[nc + 1] : 1.f;
+        rsc = 1.0f / sqrtf(wave_sum(c0 * c0 + c1 * c1) / (float)N + a.eps);
+        kc = wave_sum(c0 * wc0 * sc.x + c1 * wc1 * sc.y) * rsc * rsc * rsc / (float)N;
+    }
+    if (!on) return;
+    *reinterpret_cast<float2 *>(dBraw_out + raw) = float2{rsb * wb0 * sb.x - b0 * kb, rsb * wb1 * sb.y - b1 * kb};
+    *reinterpret_cast<float2 *>(gWB + raw) = float2{b0 * rsb * sb.x, b1 * rsb * sb.y};
+    if (!prev) {
+        *reinterpret_cast<float2 *>(dCraw_out + raw) = float2{rsc * wc0 * sc.x - c0 * kc, rsc * wc1 * sc.y - c1 * kc};
+        *reinterpret_cast<float2 *>(gWC + raw) = float2{c0 * rsc * sc.x, c1 * rsc * sc.y};
+    }
 }
 
 // d theta[b,t,g,i] = sum over the heads of group g of the per-head terms
@@ -1586,6 +1604,24 @@ __global__ __launch_bounds__(kThreads) void colsum_final_kernel(const float *par
     float s = 0.f;
     for (int64_t k = 0; k < nsplit; ++k) s += part[k * cols + c];
     dst[c] = s;
+}
+
+// Bias gradients from the matrix-core chain kernel's per-chain sums:
+//   d bias[h][r][n] = sum over batches of both row tiles' sums (B and C), plus the
+//   previous token's per-head rows for B; a fixed order, so the result is deterministic.
+__global__ __launch_bounds__(kThreads) void bwd_bias_kernel(BwdArgs ba, bool prev, float *dB_bias, float *dC_bias) {
+    const ScanArgs &a = ba.f;
+    const int64_t R = a.R, N = a.N, H = a.H, cols = H * R * N;
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= 2 * cols) return;
+    const int64_t arr = e / cols, c = e % cols;  // c = (h R + r) N + n
+    const int64_t n = c % N, h = c / (R * N), r = (c / N) % R;
+    float s = 0.f;
+    for (int64_t b = 0; b < a.b; ++b) {
+        for (int rt = 0; rt < 2; ++rt) s += ba.bpart[((((b * H + h) * 2 + rt) * R + r) * 2 + arr) * N + n];
+        if (arr == 0 && prev) s += ba.gBp[c + b * cols];
+    }
+    (arr ? dC_bias : dB_bias)[c] = s;
 }
 
 // dt, A, lam per (batch, token, head) from the token records:
@@ -1641,10 +1677,14 @@ hipError_t launch_chain_mfma(const BwdArgs &ba, int64_t chains, hipStream_t st) 
 }
 
 // the 1.5B-scale head shape (N = 128, P = 64) runs on the matrix cores for R in {1, 2, 4}
+inline bool chain_on_mfma(const ScanArgs &a) { return a.N == 128 && a.P == 64 && (a.R == 1 || a.R == 2 || a.R == 4); }
+
 template <int R>
 hipError_t launch_chain(const BwdArgs &ba, int64_t chains, size_t smem, hipStream_t st) {
     if (ba.f.N == 128 && ba.f.P == 64) {
-        if constexpr (R == 1 || R == 2 || R == 4) return launch_chain_mfma<R>(ba, chains, st);
+        if constexpr (R == 1 || R == 2 || R == 4) {
+            if (chain_on_mfma(ba.f)) return launch_chain_mfma<R>(ba, chains, st);
+        }
         return launch_chain_np<R, 128, 64>(ba, chains, smem, st);
     }
     return launch_chain_np<R, 0, 0>(ba, chains, smem, st);
@@ -1668,6 +1708,7 @@ size_t scan_bwd_workspace_bytes(const ScanArgs &a, int64_t *nsplit_out) {
     s += al(sizeof(float) * a.b * a.L * a.H * 4);                // tok
     s += al(sizeof(float) * chains * a.R * a.N);                 // gBp
     s += al(sizeof(float) * chains);                             // fold
+    s += al(sizeof(float) * chains * 2 * a.R * 2 * a.N);         // bpart
     s += 2 * al(sizeof(float) * (rowsBC + rows_prev) * a.N);     // gWB, gWC
     s += al(sizeof(float) * nsplit * cols_max);                  // column-sum partials
     return s;
@@ -1704,6 +1745,8 @@ hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, hipStre
     p += al(sizeof(float) * chains * a.R * a.N);
     ba.fold = reinterpret_cast<float *>(p);
     p += al(sizeof(float) * chains);
+    ba.bpart = reinterpret_cast<float *>(p);
+    p += al(sizeof(float) * chains * 2 * a.R * 2 * a.N);
     float *gWB = reinterpret_cast<float *>(p);
     p += al(sizeof(float) * (rowsBC + rows_prev) * a.N);
     float *gWC = reinterpret_cast<float *>(p);
@@ -1721,27 +1764,19 @@ hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, hipStre
     }
     if (e != hipSuccess) return e;
 
-    const unsigned nrow = (unsigned)(a.b * a.L * a.G);
-    if (nrow > 0) {
+    auto group = [&](bool prv, int64_t rows, float *wb, float *wc, float *ob, float *oc) -> hipError_t {
+        if (rows == 0) return hipSuccess;
+        const unsigned nb = (unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64));
         if (a.bf16)
-            hipLaunchKernelGGL(bwd_group_kernel<true>, dim3(nrow), dim3(kThreads), 0, st, ba, false, gWB, gWC, io.dBraw,
-                               io.dCraw);
+            hipLaunchKernelGGL(bwd_group_kernel<true>, dim3(nb), dim3(kThreads), 0, st, ba, prv, rows, wb, wc, ob, oc);
         else
-            hipLaunchKernelGGL(bwd_group_kernel<false>, dim3(nrow), dim3(kThreads), 0, st, ba, false, gWB, gWC,
-                               io.dBraw, io.dCraw);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+            hipLaunchKernelGGL(bwd_group_kernel<false>, dim3(nb), dim3(kThreads), 0, st, ba, prv, rows, wb, wc, ob, oc);
+        return hipGetLastError();
+    };
+    if ((e = group(false, rowsBC, gWB, gWC, io.dBraw, io.dCraw)) != hipSuccess) return e;
     float *gWBp = gWB + rowsBC * a.N;
-    if (a.has_prev && a.L > 0) {
-        const unsigned np = (unsigned)(a.b * a.G);
-        if (a.bf16)
-            hipLaunchKernelGGL(bwd_group_kernel<true>, dim3(np), dim3(kThreads), 0, st, ba, true, gWBp, nullptr,
-                               io.dBraw_prev, nullptr);
-        else
-            hipLaunchKernelGGL(bwd_group_kernel<false>, dim3(np), dim3(kThreads), 0, st, ba, true, gWBp, nullptr,
-                               io.dBraw_prev, nullptr);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    if (a.has_prev && a.L > 0 && (e = group(true, rows_prev, gWBp, nullptr, io.dBraw_prev, nullptr)) != hipSuccess)
+        return e;
     {
         const int64_t tot = a.b * a.L * a.G * (a.N / 2);
         const unsigned nb = (unsigned)((tot + kThreads - 1) / kThreads < 65536 ? (tot + kThreads - 1) / kThreads : 65536);
@@ -1766,9 +1801,16 @@ hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, hipStre
     };
     const int64_t cols_bias = a.H * a.R * a.N;
     const bool prev = a.has_prev && a.L > 0;
-    if ((e = colsum(ba.gB, a.b * a.L, prev ? ba.gBp : nullptr, prev ? a.b : 0, cols_bias, io.dB_bias)) != hipSuccess)
-        return e;
-    if ((e = colsum(ba.gC, a.b * a.L, nullptr, 0, cols_bias, io.dC_bias)) != hipSuccess) return e;
+    if (chain_on_mfma(a)) {  // the chain kernel summed its own tokens
+        const unsigned nb = (unsigned)((2 * cols_bias + kThreads - 1) / kThreads);
+        hipLaunchKernelGGL(bwd_bias_kernel, dim3(nb), dim3(kThreads), 0, st, ba, prev, io.dB_bias, io.dC_bias);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        if ((e = colsum(ba.gB, a.b * a.L, prev ? ba.gBp : nullptr, prev ? a.b : 0, cols_bias, io.dB_bias)) !=
+            hipSuccess)
+            return e;
+        if ((e = colsum(ba.gC, a.b * a.L, nullptr, 0, cols_bias, io.dC_bias)) != hipSuccess) return e;
+    }
     if (io.dB_normw &&
         (e = colsum(gWB, rowsBC, prev ? gWBp : nullptr, prev ? rows_prev : 0, a.N, io.dB_normw)) != hipSuccess)
         return e;
