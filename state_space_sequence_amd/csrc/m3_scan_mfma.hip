@@ -229,47 +229,48 @@ struct ChunkRegs {
 
 // nv: tokens of the chunk; avail: tokens from the chunk's first one to the end
 // of the sequence (capped at C + 1).
-template <int MODE, int R, bool FUSED>
+// PART 1: raw B and C rows; PART 2: token scalars, theta, x (and z); 0: both.
+template <int MODE, int R, bool FUSED, int PART = 0>
 __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, int nv, int avail, int64_t G,
                                            int64_t H, ChunkRegs &cr) {
+    // Every load is unconditional, from a clamped index; the consumer zeroes what
+    // lies past the chunk. Offsets are all formed before the first load is issued:
+    // address arithmetic interleaved with the loads had let a 32-bit multiply-add
+    // take a just-loaded register as its unused high half, and the wave then
+    // waited for that load.
     // token scalars in row layout: lane l holds row l, i.e. token l / R
     const int ts = ln.l / R;
-    cr.d = 0.f;
-    cr.av = 0.f;
-    cr.lm = 0.f;
-    cr.dn = 0.f;
-    cr.lmn = 0.f;
-    if (ts < nv) {
-        const int o = ts * (int)H;
-        cr.d = cb.dt[o];
-        cr.av = cb.A[o];
-        cr.lm = cb.lam[o];
-        if (ts + 1 < avail) {
-            cr.dn = cb.dt[o + (int)H];
-            cr.lmn = cb.lam[o + (int)H];
+    const int tsc = ts < nv ? ts : nv - 1, tsn = ts + 1 < avail ? ts + 1 : avail - 1;
+    // fragment rows past the end read the last token's data: finite values whose
+    // weights, gamma, state weight and angle increment are all zero, and whose
+    // outputs are not stored
+    const int tr = ln.t_row < nv ? ln.t_row : nv - 1;
+    int o = tsc * (int)H, on = tsn * (int)H, orow = tr * (int)H;
+    int offBC = (tr * (int)G * R + ln.r_row) * kN + 8 * ln.lg;
+    int oth = tr * (int)G * kHalf;
+    int offx = FUSED ? tr * (int)H * kP : (tr * (int)H * R + ln.r_row) * kP;
+    asm volatile("" : "+v"(o), "+v"(on), "+v"(orow), "+v"(offBC), "+v"(oth), "+v"(offx));
+    if constexpr (PART != 2) {
+        const bf16x8 *pb = reinterpret_cast<const bf16x8 *>(cb.B + offBC);
+        const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + offBC);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            cr.rb[ks] = pb[4 * ks];
+            if constexpr (MODE != kPass1) cr.rc[ks] = pc[4 * ks];
         }
     }
-    // fragment rows past the end read the last token's data instead of zeros:
-    // finite values whose weights, gamma, state weight and angle increment are
-    // all zero, and whose outputs are not stored
-    const bool valid = ln.t_row < nv;
-    const int tr = valid ? ln.t_row : nv - 1;
-    const float dr = cb.dt[tr * (int)H];
-    cr.drow = valid ? dr : 0.f;
-    const int offBC = (tr * (int)G * R + ln.r_row) * kN + 8 * ln.lg;
-    const bf16x8 *pb = reinterpret_cast<const bf16x8 *>(cb.B + offBC);
-    const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + offBC);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        cr.rb[ks] = pb[4 * ks];
-        if constexpr (MODE != kPass1) cr.rc[ks] = pc[4 * ks];
-    }
-    const f32x4 *pt = reinterpret_cast<const f32x4 *>(cb.th + tr * (int)G * kHalf);
+    if constexpr (PART == 1) return;
+    cr.d = cb.dt[o];
+    cr.av = cb.A[o];
+    cr.lm = cb.lam[o];
+    cr.dn = cb.dt[on];
+    cr.lmn = cb.lam[on];
+    cr.drow = cb.dt[orow];
+    const f32x4 *pt = reinterpret_cast<const f32x4 *>(cb.th + oth);
     cr.th[0] = pt[2 * ln.lg];
     cr.th[1] = pt[2 * ln.lg + 1];
     cr.th[2] = pt[8 + 2 * ln.lg];
     cr.th[3] = pt[8 + 2 * ln.lg + 1];
-    const int offx = FUSED ? tr * (int)H * kP : (tr * (int)H * R + ln.r_row) * kP;
     const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + offx);
     cr.xf[0] = px[ln.lg];
     cr.xf[1] = px[4 + ln.lg];
@@ -433,7 +434,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 
         // ---- this chunk's inputs, loaded during the previous chunk
         const bool valid = t_row < nv;
-        const float d = cr.d, av = cr.av, lm = cr.lm, dn = cr.dn, lmn = cr.lmn, drow = cr.drow;
+        // the loads were unconditional: zero the scalars of tokens past the chunk
+        // (and the look-ahead past the sequence)
+        const int avail = (int)((L - c0) < C + 1 ? (L - c0) : C + 1);
+        const bool tin = l / R < nv, tnx = l / R + 1 < avail;
+        const float d = tin ? cr.d : 0.f, av = tin ? cr.av : 0.f, lm = tin ? cr.lm : 0.f;
+        const float dn = tnx ? cr.dn : 0.f, lmn = tnx ? cr.lmn : 0.f, drow = valid ? cr.drow : 0.f;
         bf16x8 rb[4], rc[4], xf[2];
         f32x4 th[4];
 #pragma unroll
@@ -461,15 +467,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 }
             }
         }
-        // ---- X^T through the matrix core: T = X-fragment x selection, exact for
-        // bf16 operands; the output lane holds rows 16w + 4lg..+3 of column lr
-#pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-            const f32x4 t = mfma(xf[pb >> 1], (pb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f});
-            const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
-            *reinterpret_cast<bf16x4 *>(&sm.Xt[(16 * pb + lr) * kLdR + 16 * w + 4 * lg]) = v;
-        }
-
         // ---- token scalars in row layout (lane l = row l, token l / R): decay
         // prefix over the tokens (one term per token), folded weights
         const float cs = wave_incl_scan((l % R == 0) ? d * av : 0.f);
@@ -545,6 +542,17 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             }
         }
         __syncthreads();  // B1
+
+        // ---- X^T through the matrix core: T = X-fragment x selection, exact for
+        // bf16 operands; the output lane holds rows 16w + 4lg..+3 of column lr.
+        // Written after B1, which every wave passes only once its state update of
+        // the previous chunk (a reader of every column of X^T) is done.
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+            const f32x4 t = mfma(xf[pb >> 1], (pb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f});
+            const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
+            *reinterpret_cast<bf16x4 *>(&sm.Xt[(16 * pb + lr) * kLdR + 16 * w + 4 * lg]) = v;
+        }
 
         // ---- rotate into the frame of the workgroup's first token: add the carry
         // and the totals of the earlier waves' rows. Branch-free (uniform 0/1
@@ -637,11 +645,16 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         __syncthreads();  // B2
 
         // ---- next chunk's inputs: in flight during this chunk's matrix work
-        if (c + 1 < pos.c_end) {
-            const int64_t c1 = c0 + C;
-            const int nv1 = (int)((L - c1) < C ? (L - c1) : C);
-            const int avail1 = (int)((L - c1) < C + 1 ? (L - c1) : C + 1);
-            load_chunk<MODE, R, FUSED>(chunk_base<R, FUSED>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
+        // the next chunk's inputs. A burst of every wave's loads right after B2
+        // filled the CU's queue of outstanding misses and blocked the issuing waves
+        // for a memory latency. Measured best: one burst before the state update
+        // for R = 1; for R > 1 the raw B, C rows here and the rest there.
+        const int64_t c1 = c0 + C;
+        const bool more = c + 1 < pos.c_end;
+        const int nv1 = (int)((L - c1) < C ? (L - c1) : C);
+        const int avail1 = (int)((L - c1) < C + 1 ? (L - c1) : C + 1);
+        if constexpr (R > 1) {
+            if (more) load_chunk<MODE, R, FUSED, 1>(chunk_base<R, FUSED>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
         }
 
         if constexpr (MODE != kPass1) {
@@ -790,6 +803,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             }
             __syncthreads();  // B3: St and Bb reads done
         }
+
+        if (more) load_chunk<MODE, R, FUSED, (R > 1 ? 2 : 0)>(chunk_base<R, FUSED>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
 
         // ---- state update: acc[q][pb] = exp(cs_end) acc + Bt-rows x Xt
         const float dec = __expf(cs_end);
