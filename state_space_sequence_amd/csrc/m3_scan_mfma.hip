@@ -223,8 +223,7 @@ struct ChunkRegs {
     bf16x4 zf[4];  // fused projections: Z' of the row's token at the lane's output columns
     f32x4 th[4];
     float d, av, lm;  // dt, A, lambda of the token of row l (lane l holds row l)
-    float dn, lmn;    // dt and lambda of the token after it (0 past the end)
-    float drow;       // dt of the token of this lane's fragment row (0 past the end)
+    float dnl, lmnl;  // dt and lambda of the token after the chunk's last (same in every lane)
 };
 
 // nv: tokens of the chunk; avail: tokens from the chunk's first one to the end
@@ -238,18 +237,23 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
     // address arithmetic interleaved with the loads had let a 32-bit multiply-add
     // take a just-loaded register as its unused high half, and the wave then
     // waited for that load.
-    // token scalars in row layout: lane l holds row l, i.e. token l / R
+    // token scalars in row layout: lane l holds row l, i.e. token l / R. Only
+    // dt, A, lambda of the lane's own token are loaded per lane (tokens are H
+    // floats apart, so each such load touches one cache line per token); the
+    // consumer takes the next token's values and the fragment rows' dt from
+    // other lanes.
     const int ts = ln.l / R;
-    const int tsc = ts < nv ? ts : nv - 1, tsn = ts + 1 < avail ? ts + 1 : avail - 1;
+    const int tsc = ts < nv ? ts : nv - 1;
+    const int onl = (avail > kRows / R ? kRows / R : avail - 1) * (int)H;
     // fragment rows past the end read the last token's data: finite values whose
     // weights, gamma, state weight and angle increment are all zero, and whose
     // outputs are not stored
     const int tr = ln.t_row < nv ? ln.t_row : nv - 1;
-    int o = tsc * (int)H, on = tsn * (int)H, orow = tr * (int)H;
+    int o = tsc * (int)H;
     int offBC = (tr * (int)G * R + ln.r_row) * kN + 8 * ln.lg;
     int oth = tr * (int)G * kHalf;
     int offx = FUSED ? tr * (int)H * kP : (tr * (int)H * R + ln.r_row) * kP;
-    asm volatile("" : "+v"(o), "+v"(on), "+v"(orow), "+v"(offBC), "+v"(oth), "+v"(offx));
+    asm volatile("" : "+v"(o), "+v"(offBC), "+v"(oth), "+v"(offx));
     if constexpr (PART != 2) {
         const bf16x8 *pb = reinterpret_cast<const bf16x8 *>(cb.B + offBC);
         const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + offBC);
@@ -263,9 +267,8 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
     cr.d = cb.dt[o];
     cr.av = cb.A[o];
     cr.lm = cb.lam[o];
-    cr.dn = cb.dt[on];
-    cr.lmn = cb.lam[on];
-    cr.drow = cb.dt[orow];
+    cr.dnl = cb.dt[onl];
+    cr.lmnl = cb.lam[onl];
     const f32x4 *pt = reinterpret_cast<const f32x4 *>(cb.th + oth);
     cr.th[0] = pt[2 * ln.lg];
     cr.th[1] = pt[2 * ln.lg + 1];
@@ -439,7 +442,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         const int avail = (int)((L - c0) < C + 1 ? (L - c0) : C + 1);
         const bool tin = l / R < nv, tnx = l / R + 1 < avail;
         const float d = tin ? cr.d : 0.f, av = tin ? cr.av : 0.f, lm = tin ? cr.lm : 0.f;
-        const float dn = tnx ? cr.dn : 0.f, lmn = tnx ? cr.lmn : 0.f, drow = valid ? cr.drow : 0.f;
+        // the next token's dt and lambda sit R lanes on, except for the chunk's last
+        // token; the fragment row's dt sits in lane `row` of the row layout
+        const bool lastt = l + R >= kRows;
+        const float dsh = __shfl_down(d, R), lsh = __shfl_down(lm, R);
+        const float dn = tnx ? (lastt ? cr.dnl : dsh) : 0.f, lmn = tnx ? (lastt ? cr.lmnl : lsh) : 0.f;
+        const float drow = __shfl(d, row);  // zero past the end, as d is
         bf16x8 rb[4], rc[4], xf[2];
         f32x4 th[4];
 #pragma unroll
