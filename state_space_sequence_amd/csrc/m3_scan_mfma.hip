@@ -118,6 +118,8 @@ struct alignas(16) Smem {
     alignas(16) float cstt[kRows];        // per row: exp(cs_end - cs) w (state-input weight)
     alignas(16) float ftab[kRows];        // per row t >= 16: exp(cs_t - cs_ref), ref = last row of the block before t's
     alignas(16) float tw[3][kRows];       // [w-1][s]: exp(cs_ref(w) - cs_s) w_s for s < 16w, else 0
+    alignas(16) float tok[3][kRows];      // dt, A, lambda of each row's token (next chunk's, staged)
+    alignas(16) float tokn[4];            // dt, lambda of the token after that chunk
     alignas(16) float angtot[4][kHalf];   // per wave: angle total of its rows (revolutions)
     alignas(16) float carry[kHalf];       // cumulative angle before the current chunk, mod 1 revolution
     alignas(16) float bias[2][4][kN];     // B / C bias of this head, per rank
@@ -222,13 +224,11 @@ struct ChunkRegs {
     bf16x8 rb[4], rc[4], xf[2];
     bf16x4 zf[4];  // fused projections: Z' of the row's token at the lane's output columns
     f32x4 th[4];
-    float d, av, lm;  // dt, A, lambda of the token of row l (lane l holds row l)
-    float dnl, lmnl;  // dt and lambda of the token after the chunk's last (same in every lane)
 };
 
 // nv: tokens of the chunk; avail: tokens from the chunk's first one to the end
 // of the sequence (capped at C + 1).
-// PART 1: raw B and C rows; PART 2: token scalars, theta, x (and z); 0: both.
+// PART 1: raw B and C rows; PART 2: theta, x (and z); 0: both.
 template <int MODE, int R, bool FUSED, int PART = 0>
 __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, int nv, int avail, int64_t G,
                                            int64_t H, ChunkRegs &cr) {
@@ -237,23 +237,14 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
     // address arithmetic interleaved with the loads had let a 32-bit multiply-add
     // take a just-loaded register as its unused high half, and the wave then
     // waited for that load.
-    // token scalars in row layout: lane l holds row l, i.e. token l / R. Only
-    // dt, A, lambda of the lane's own token are loaded per lane (tokens are H
-    // floats apart, so each such load touches one cache line per token); the
-    // consumer takes the next token's values and the fragment rows' dt from
-    // other lanes.
-    const int ts = ln.l / R;
-    const int tsc = ts < nv ? ts : nv - 1;
-    const int onl = (avail > kRows / R ? kRows / R : avail - 1) * (int)H;
     // fragment rows past the end read the last token's data: finite values whose
     // weights, gamma, state weight and angle increment are all zero, and whose
     // outputs are not stored
     const int tr = ln.t_row < nv ? ln.t_row : nv - 1;
-    int o = tsc * (int)H;
     int offBC = (tr * (int)G * R + ln.r_row) * kN + 8 * ln.lg;
     int oth = tr * (int)G * kHalf;
     int offx = FUSED ? tr * (int)H * kP : (tr * (int)H * R + ln.r_row) * kP;
-    asm volatile("" : "+v"(o), "+v"(offBC), "+v"(oth), "+v"(offx));
+    asm volatile("" : "+v"(offBC), "+v"(oth), "+v"(offx));
     if constexpr (PART != 2) {
         const bf16x8 *pb = reinterpret_cast<const bf16x8 *>(cb.B + offBC);
         const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + offBC);
@@ -264,11 +255,6 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
         }
     }
     if constexpr (PART == 1) return;
-    cr.d = cb.dt[o];
-    cr.av = cb.A[o];
-    cr.lm = cb.lam[o];
-    cr.dnl = cb.dt[onl];
-    cr.lmnl = cb.lam[onl];
     const f32x4 *pt = reinterpret_cast<const f32x4 *>(cb.th + oth);
     cr.th[0] = pt[2 * ln.lg];
     cr.th[1] = pt[2 * ln.lg + 1];
@@ -283,6 +269,40 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) cr.zf[pb] = pz[4 * pb];
     }
+}
+
+// Token scalars of chunk cc for this wave's 16 rows, one load per lane: lane
+// groups 0, 1, 2 take dt, A, lambda of row 16w + lr (token (16w + lr) / R); lane
+// group 3 takes the dt (even lr) or lambda (odd lr) of the token after the chunk.
+// Tokens are H floats apart, so a per-lane load of all 64 rows by every wave
+// touched 4x the cache lines. Indices are clamped into the sequence; the reader
+// zeroes what lies past it.
+typedef __attribute__((address_space(1))) const float gfloat;  // global memory
+
+// sbase: this lane's array (scalar_base) offset to head hi.
+template <int R>
+__device__ __forceinline__ float load_scalars(const ScanArgs &a, gfloat *sbase, int64_t bi, int64_t cc,
+                                              const Lane &ln) {
+    constexpr int C = kRows / R;
+    const int64_t c0 = cc * C;
+    const int nv = (int)((a.L - c0) < C ? (a.L - c0) : C);
+    const int avail = (int)((a.L - c0) < C + 1 ? (a.L - c0) : C + 1);
+    const int t = ln.lg < 3 ? (ln.row / R < nv ? ln.row / R : nv - 1) : (C < avail ? C : avail - 1);
+    int ot = t * (int)a.H;
+    asm volatile("" : "+v"(ot));
+    return sbase[(bi * a.L + c0) * a.H + ot];
+}
+
+// The array a lane of load_scalars reads (dt, A or lambda), offset to head hi.
+// The three pointers pass through an empty asm so that the per-lane choice is a
+// register select: a short-circuit condition had been compiled to divergent
+// branches that left the odd lanes of group 3 on the dt pointer, and a plain
+// select to a per-lane load of the pointer from the argument block.
+__device__ __forceinline__ gfloat *scalar_base(const ScanArgs &a, int64_t hi, int lg, int lr) {
+    gfloat *pd = (gfloat *)a.dt, *pa = (gfloat *)a.A, *pl = (gfloat *)a.lam;
+    asm("" : "+s"(pd), "+s"(pa), "+s"(pl));
+    const int k = lg < 3 ? lg : 2 * (lr & 1);  // 0: dt, 1: A, 2: lambda
+    return (k == 0 ? pd : (k == 1 ? pa : pl)) + hi;
 }
 
 // bf16x8 fragment with a single 1.0 at slot j (none when j is outside 0..7)
@@ -413,6 +433,18 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
     // selection fragments for the transposes: E_h[k][c] = 1 when k == 16h + c,
     // with k = 8lg + slot and c = lr
     const bf16x8 e0 = unit_fragment(lr - 8 * lg), e1 = unit_fragment(16 + lr - 8 * lg);
+    // token scalars: the first chunk's staged now, the next one's in flight (each
+    // later chunk's are loaded two chunks ahead and staged before B2 of the chunk
+    // before it)
+    gfloat *const sbase = scalar_base(a, hi, lg, lr);
+    float scal = 0.f;
+    if (pos.c_begin < pos.c_end) {
+        const Lane ln0 = make_lane<R>(l, w, H);
+        const float s0 = load_scalars<R>(a, sbase, bi, pos.c_begin, ln0);
+        if (lg < 3) sm.tok[lg][ln0.row] = s0;
+        else if (w == 0 && lr < 2) sm.tokn[lr] = s0;
+        scal = load_scalars<R>(a, sbase, bi, pos.c_begin + 1 < pos.c_end ? pos.c_begin + 1 : pos.c_begin, ln0);
+    }
     __syncthreads();
 
     float logdecay_total = 0.f;
@@ -437,17 +469,19 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 
         // ---- this chunk's inputs, loaded during the previous chunk
         const bool valid = t_row < nv;
-        // the loads were unconditional: zero the scalars of tokens past the chunk
-        // (and the look-ahead past the sequence)
+        // token scalars (staged before B2 of the previous chunk): row l's token, the
+        // next token's (row l + R, or the token after the chunk), the fragment row's;
+        // zero for tokens past the chunk and a look-ahead past the sequence
         const int avail = (int)((L - c0) < C + 1 ? (L - c0) : C + 1);
         const bool tin = l / R < nv, tnx = l / R + 1 < avail;
-        const float d = tin ? cr.d : 0.f, av = tin ? cr.av : 0.f, lm = tin ? cr.lm : 0.f;
-        // the next token's dt and lambda sit R lanes on, except for the chunk's last
-        // token; the fragment row's dt sits in lane `row` of the row layout
         const bool lastt = l + R >= kRows;
-        const float dsh = __shfl_down(d, R), lsh = __shfl_down(lm, R);
-        const float dn = tnx ? (lastt ? cr.dnl : dsh) : 0.f, lmn = tnx ? (lastt ? cr.lmnl : lsh) : 0.f;
-        const float drow = __shfl(d, row);  // zero past the end, as d is
+        const int lnx = lastt ? kRows - 1 : l + R;
+        const float d0 = sm.tok[0][l], a0_ = sm.tok[1][l], l0 = sm.tok[2][l];
+        const float dsh = sm.tok[0][lnx], lsh = sm.tok[2][lnx], dnl = sm.tokn[0], lmnl = sm.tokn[1];
+        const float drw = sm.tok[0][row];
+        const float d = tin ? d0 : 0.f, av = tin ? a0_ : 0.f, lm = tin ? l0 : 0.f;
+        const float dn = tnx ? (lastt ? dnl : dsh) : 0.f, lmn = tnx ? (lastt ? lmnl : lsh) : 0.f;
+        const float drow = valid ? drw : 0.f;
         bf16x8 rb[4], rc[4], xf[2];
         f32x4 th[4];
 #pragma unroll
@@ -650,10 +684,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 *reinterpret_cast<bf16x4 *>(&sm.Bt[(16 * nb + lr) * kLdR + 16 * w + 4 * lg]) = v;
             }
         }
+        // the next chunk's token scalars (every wave read this chunk's before B1)
+        if (lg < 3) sm.tok[lg][row] = scal;
+        else if (w == 0 && lr < 2) sm.tokn[lr] = scal;
         __syncthreads();  // B2
 
-        // ---- next chunk's inputs: in flight during this chunk's matrix work
-        // the next chunk's inputs. A burst of every wave's loads right after B2
+        // ---- the next chunk's inputs. A burst of every wave's loads right after B2
         // filled the CU's queue of outstanding misses and blocked the issuing waves
         // for a memory latency. Measured best: one burst before the state update
         // for R = 1; for R > 1 the raw B, C rows here and the rest there.
@@ -813,6 +849,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         }
 
         if (more) load_chunk<MODE, R, FUSED, (R > 1 ? 2 : 0)>(chunk_base<R, FUSED>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
+        scal = load_scalars<R>(a, sbase, bi, c + 2 < pos.c_end ? c + 2 : pos.c_end - 1, ln);
 
         // ---- state update: acc[q][pb] = exp(cs_end) acc + Bt-rows x Xt
         const float dec = __expf(cs_end);
