@@ -218,47 +218,118 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
         }
     }
 
-    // ---- raw rows into LDS
+    // ---- set-up inputs: every global load is issued before the first LDS store,
+    // from clamped indices and with optional inputs read through a valid stand-in
+    // pointer (the value is masked afterwards), so that no load sits in a branch:
+    // the compiler ends such a branch by waiting for its loads, and a load-then-
+    // store loop per input had cost one memory round trip each.
+    constexpr int EBC = (R * N + kThreads - 1) / kThreads;  // B, C, bias elements per thread
     const int64_t rowBC = (bi * a.G + g) * R * N;
-    for (int e = tid; e < R * N; e += kThreads) {
-        sB[e] = ld_io<BF16>(a.Braw, rowBC + e);
-        sC[e] = ld_io<BF16>(a.Craw, rowBC + e);
-        sBp[e] = a.has_prev ? ld_io<BF16>(a.Braw_prev, rowBC + e) : 0.f;
-    }
     const int64_t rowX = (bi * a.H + hi) * R * P;
+    const int64_t rowP = (bi * a.H + hi) * P;
+    const bool hp = a.has_prev;
+    const void *srcBp = hp ? a.Braw_prev : a.Braw;
+    float rB[EBC], rC[EBC], rBp[EBC], rbb[EBC], rcb[EBC];
+#pragma unroll
+    for (int k = 0; k < EBC; ++k) {
+        int e = tid + k * kThreads;
+        e = e < R * N ? e : R * N - 1;
+        rB[k] = ld_io<BF16>(a.Braw, rowBC + e);
+        rC[k] = ld_io<BF16>(a.Craw, rowBC + e);
+        rBp[k] = ld_io<BF16>(srcBp, rowBC + e);
+        rbb[k] = a.B_bias[hi * R * N + e];
+        rcb[k] = a.C_bias[hi * R * N + e];
+    }
+    const int en = tid < N ? tid : N - 1, ei = tid < HALF ? tid : HALF - 1;
+    const float *pwb = a.B_normw ? a.B_normw : a.B_bias, *pwc = a.C_normw ? a.C_normw : a.C_bias;
+    const float rwb0 = pwb[en], rwc0 = pwc[en];
+    const float rth = a.theta[(bi * a.G + g) * HALF + ei];
+    const float d = a.dt[bh], Av = a.A[bh], lm = a.lam[bh];
+    // x and x_prev, first 2 * kThreads of the R P elements (with the fused
+    // projections X', Z' [P] and the weights [P][R], element e = p R + r)
+    const int EXN = R * P;
+    const int ex0 = tid < EXN ? tid : EXN - 1, ex1 = tid + kThreads < EXN ? tid + kThreads : EXN - 1;
+    const void *srcXp = hp ? a.x_prev : a.x;
     if (!a.fused) {
-        for (int e = tid; e < R * P; e += kThreads) {
-            // stored rank-minor, [p][r], so one row's ranks are adjacent
-            const int r = e / P, p = e % P;
-            sx[p * R + r] = ld_io<BF16>(a.x, rowX + e);
-            sxp[p * R + r] = a.has_prev ? ld_io<BF16>(a.x_prev, rowX + e) : 0.f;
+        float rx[2], rxp[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = k == 0 ? ex0 : ex1;
+            rx[k] = ld_io<BF16>(a.x, rowX + e);
+            rxp[k] = ld_io<BF16>(srcXp, rowX + e);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = tid + k * kThreads;
+            if (e < EXN) {
+                // stored rank-minor, [p][r], so one row's ranks are adjacent
+                const int r = e / P, pp = e % P;
+                sx[pp * R + r] = rx[k];
+                sxp[pp * R + r] = hp ? rxp[k] : 0.f;
+            }
         }
     } else {
-        // W is [H][P][R]: e = p R + r is already the table order
-        const int64_t rowP = (bi * a.H + hi) * P;
-        const float *wx = a.W_X + hi * R * P, *wz = a.W_Z + hi * R * P, *wo = a.W_O + hi * R * P;
-        for (int e = tid; e < R * P; e += kThreads) {
-            const int p = e / R;
-            sx[e] = wx[e] * ld_io<BF16>(a.x, rowP + p);
-            sxp[e] = a.has_prev ? wx[e] * ld_io<BF16>(a.x_prev, rowP + p) : 0.f;
-            const float zz = wz[e] * ld_io<BF16>(a.z, rowP + p);
-            sgt[e] = wo[e] * (zz / (1.f + expf(-zz)));
+        float rx[2], rxp[2], rz[2], rwx[2], rwz[2], rwo[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = k == 0 ? ex0 : ex1, pp = e / R;
+            rx[k] = ld_io<BF16>(a.x, rowP + pp);
+            rxp[k] = ld_io<BF16>(srcXp, rowP + pp);
+            rz[k] = ld_io<BF16>(a.z, rowP + pp);
+            rwx[k] = a.W_X[hi * R * P + e];
+            rwz[k] = a.W_Z[hi * R * P + e];
+            rwo[k] = a.W_O[hi * R * P + e];
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = tid + k * kThreads;
+            if (e < EXN) {
+                // W is [H][P][R]: e = p R + r is already the table order
+                sx[e] = rwx[k] * rx[k];
+                sxp[e] = hp ? rwx[k] * rxp[k] : 0.f;
+                const float zz = rwz[k] * rz[k];
+                sgt[e] = rwo[k] * (zz / (1.f + expf(-zz)));
+            }
         }
     }
-    for (int e = tid; e < R * N; e += kThreads) {
-        sbb[e] = a.B_bias[hi * R * N + e];
-        scb[e] = a.C_bias[hi * R * N + e];
+    const float rwb = a.B_normw ? rwb0 : 1.f, rwc = a.C_normw ? rwc0 : 1.f;
+
+    // ---- into LDS
+#pragma unroll
+    for (int k = 0; k < EBC; ++k) {
+        const int e = tid + k * kThreads;
+        if (e < R * N) {
+            sB[e] = rB[k];
+            sC[e] = rC[k];
+            sBp[e] = hp ? rBp[k] : 0.f;
+            sbb[e] = rbb[k];
+            scb[e] = rcb[k];
+        }
     }
-    for (int e = tid; e < N; e += kThreads) {
-        swb[e] = a.B_normw ? a.B_normw[e] : 1.f;
-        swc[e] = a.C_normw ? a.C_normw[e] : 1.f;
+    // x elements past the first 2 * kThreads (R P > 512: large heads only)
+    for (int e = tid + 2 * kThreads; e < EXN; e += kThreads) {
+        if (!a.fused) {
+            const int r = e / P, pp = e % P;
+            sx[pp * R + r] = ld_io<BF16>(a.x, rowX + e);
+            sxp[pp * R + r] = a.has_prev ? ld_io<BF16>(a.x_prev, rowX + e) : 0.f;
+        } else {
+            const int pp = e / R;
+            const float wx = a.W_X[hi * R * P + e];
+            sx[e] = wx * ld_io<BF16>(a.x, rowP + pp);
+            sxp[e] = a.has_prev ? wx * ld_io<BF16>(a.x_prev, rowP + pp) : 0.f;
+            const float zz = a.W_Z[hi * R * P + e] * ld_io<BF16>(a.z, rowP + pp);
+            sgt[e] = a.W_O[hi * R * P + e] * (zz / (1.f + expf(-zz)));
+        }
     }
-    const float d = a.dt[bh], Av = a.A[bh], lm = a.lam[bh];
-    for (int i = tid; i < HALF; i += kThreads) {
-        float s, c;
-        sincosf(d * a.theta[(bi * a.G + g) * HALF + i], &s, &c);
-        scs[i] = c;
-        ssn[i] = s;
+    if (tid < N) {
+        swb[tid] = rwb;
+        swc[tid] = rwc;
+    }
+    if (tid < HALF) {
+        float sv, cv;
+        sincosf(d * rth, &sv, &cv);
+        scs[tid] = cv;
+        ssn[tid] = sv;
     }
     __syncthreads();
 
