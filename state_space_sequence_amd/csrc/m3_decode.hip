@@ -180,17 +180,15 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     extern __shared__ float sm[];
     // every array below starts on a 16-byte boundary (sizes are multiples of 4
     // floats) except the last two, which are only read as scalars
-    float *sB = sm;              // [R][N]   raw, then gamma * normalised B_t
-    float *sC = sB + R * N;      // [R][N]   raw, then normalised C_t
-    float *sBp = sC + R * N;     // [R][N]   raw, then beta * normalised B_{t-1}
-    float *sbb = sBp + R * N;    // [R][N]   B bias of this head
-    float *scb = sbb + R * N;    // [R][N]   C bias
-    float *swb = scb + R * N;    // [N]      B gain (ones when absent)
+    float *sB = sm;              // [R][N]   gamma * normalised B_t (+ bias)
+    float *sC = sB + R * N;      // [R][N]   normalised C_t (+ bias)
+    float *sBp = sC + R * N;     // [R][N]   beta * normalised B_{t-1} (+ bias)
+    float *swb = sBp + R * N;    // [N]      B gain (ones when absent)
     float *swc = swb + N;        // [N]      C gain
     float *scs = swc + N;        // [HALF]   cos
     float *ssn = scs + HALF;     // [HALF]   sin
-    float *srs = ssn + HALF;     // [4R]     1/rms per row
-    float *sx = srs + 4 * R;     // [P][R]
+    float *spart = ssn + HALF;   // [3][R][4] BCNorm: sums of squares of row segments (B, C, B_prev)
+    float *sx = spart + 12 * R;  // [P][R]
     float *sxp = sx + R * a.P;   // [P][R]
     float *sgt = sxp + R * a.P;  // [P][R]   fused: W_O SiLU(W_Z Z')
     float *sy = sgt + (a.fused ? R * a.P : 0);  // [R][P] output norm: rows before the norm
@@ -294,16 +292,21 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     }
     const float rwb = a.B_normw ? rwb0 : 1.f, rwc = a.C_normw ? rwc0 : 1.f;
 
-    // ---- into LDS
+    // ---- BCNorm sums of squares straight from the registers: row r holds the
+    // elements [rN, (r+1)N), and a segment of SG = min(N, 64) consecutive elements
+    // lies in one wave, so an SG-lane group sum is that segment's total
+    constexpr int SG = N < 64 ? N : 64;
 #pragma unroll
     for (int k = 0; k < EBC; ++k) {
         const int e = tid + k * kThreads;
-        if (e < R * N) {
-            sB[e] = rB[k];
-            sC[e] = rC[k];
-            sBp[e] = hp ? rBp[k] : 0.f;
-            sbb[e] = rbb[k];
-            scb[e] = rcb[k];
+        const bool ok = e < R * N;  // whole SG-lane groups (R N is a multiple of SG)
+        const float vb = ok ? rB[k] : 0.f, vc = ok ? rC[k] : 0.f, vp = ok ? rBp[k] : 0.f;
+        const float qb = group_sum<SG>(vb * vb), qc = group_sum<SG>(vc * vc), qp = group_sum<SG>(vp * vp);
+        if (ok && e % SG == 0) {
+            const int r = e / N, seg = (e % N) / SG;
+            spart[r * 4 + seg] = qb;
+            spart[(R + r) * 4 + seg] = qc;
+            spart[(2 * R + r) * 4 + seg] = qp;
         }
     }
     // x elements past the first 2 * kThreads (R P > 512: large heads only)
@@ -326,23 +329,13 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
         swc[tid] = rwc;
     }
     if (tid < HALF) {
-        float sv, cv;
-        sincosf(d * rth, &sv, &cv);
-        scs[tid] = cv;
-        ssn[tid] = sv;
+        // the hardware sine and cosine take revolutions; reduce to [0, 1) first
+        const float rev = __builtin_amdgcn_fractf(d * rth * 0.15915494309189535f);
+        scs[tid] = __builtin_amdgcn_cosf(rev);
+        ssn[tid] = __builtin_amdgcn_sinf(rev);
     }
     __syncthreads();
-
-    // ---- BCNorm: one wave per row (B rows, C rows, B_prev rows)
     const int wave = tid / 64, lane = tid % 64;
-    for (int k = wave; k < 3 * R; k += kThreads / 64) {
-        const float *row = (k < R ? sB : (k < 2 * R ? sC : sBp)) + (k % R) * N;
-        float ss = 0.f;
-        for (int n = lane; n < N; n += 64) ss += row[n] * row[n];
-        ss = wave_sum(ss);
-        if (lane == 0) srs[k] = 1.0f / sqrtf(ss / (float)N + a.eps);
-    }
-    __syncthreads();
 
     const float dsk = a.D ? a.D[hi] : 0.f;
     // with the output norm, what is staged: each rank row of y (or of Y, before the
@@ -353,13 +346,23 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     const float beta = a.has_prev ? (1.0f - lm) * d * alpha : 0.f;
     const float gamma = lm * d;
 
-    // ---- per-column coefficients, once per workgroup, in place in LDS:
-    // sB <- gamma * B_t, sBp <- beta * B_{t-1}, sC <- C_t (all normalised + bias)
-    for (int e = tid; e < R * N; e += kThreads) {
-        const int r = e / N, n = e % N;
-        sB[e] = gamma * (sB[e] * srs[r] * swb[n] + sbb[e]);
-        sC[e] = sC[e] * srs[R + r] * swc[n] + scb[e];
-        sBp[e] = beta * (sBp[e] * srs[2 * R + r] * swb[n] + sbb[e]);
+    // ---- per-column coefficients, once per workgroup, from the registers:
+    // sB = gamma * B_t, sBp = beta * B_{t-1}, sC = C_t (all normalised + bias)
+    auto rs_of = [&](int j, int r) {  // 1/rms of row r of B (j = 0), C (1), B_prev (2)
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < N / SG; ++i) ss += spart[(j * R + r) * 4 + i];
+        return 1.0f / sqrtf(ss / (float)N + a.eps);
+    };
+#pragma unroll
+    for (int k = 0; k < EBC; ++k) {
+        const int e = tid + k * kThreads;
+        if (e < R * N) {
+            const int r = e / N, n = e % N;
+            sB[e] = gamma * (rB[k] * rs_of(0, r) * swb[n] + rbb[k]);
+            sC[e] = rC[k] * rs_of(1, r) * swc[n] + rcb[k];
+            sBp[e] = hp ? beta * (rBp[k] * rs_of(2, r) * swb[n] + rbb[k]) : 0.f;
+        }
     }
     __syncthreads();
 
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
 
 template <bool BF16, bool BS, int N, bool ONORM>
 hipError_t launch_nn(const DecodeArgs &a, hipStream_t s) {
-    const size_t smem = sizeof(float) * (5 * a.R * N + 3 * N + 4 * a.R + (a.fused ? 3 : 2) * a.R * a.P +
+    const size_t smem = sizeof(float) * (3 * a.R * N + 3 * N + 12 * a.R + (a.fused ? 3 : 2) * a.R * a.P +
                                          (a.onorm ? a.R * a.P + a.R : 0));
     dim3 grid((unsigned)(a.b * a.H)), block(kThreads);
     switch (a.R) {
