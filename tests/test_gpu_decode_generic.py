@@ -31,6 +31,9 @@ DECODE_CASES = [
     (2, 2, 1, 16, 256, 2, "f32", False, True),
     (2, 3, 1, 16, 16, 4, "f32", True, False),
     (1, 2, 1, 32, 256, 1, "f32", False, False),
+    # R P > 512: x elements past the first two per thread of the set-up
+    (1, 2, 1, 256, 64, 4, "f32", True, True),
+    (2, 2, 1, 160, 128, 4, "bf16", False, False),
 ]
 
 

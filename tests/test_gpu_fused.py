@@ -114,6 +114,7 @@ DECODE = [
     (2, 2, 1, 32, 256, 2, "f32", False, False),
     (2, 2, 1, 48, 16, 4, "f32", False, True),
     (1, 2, 1, 128, 128, 3, "f32", True, False),
+    (1, 2, 1, 200, 64, 4, "f32", False, True),  # R P > 512
 ]
 
 
