@@ -663,6 +663,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs ba) {
 namespace mf {
 constexpr int N = 128, P = 64, HALF = 64, T = 32;
 constexpr int NS = N + 4, PS = P + 4, TS = T + 4;  // 16-byte aligned rows, shifted 4 banks each
+constexpr int PHS = HALF + 1;  // per-token angle rows: scans walk lanes over tokens, so rows shift one bank
 constexpr int NT = kChainThreads;
 
 __device__ __forceinline__ f4 mfma4(f4 a, f4 b, f4 c) {
@@ -729,7 +730,7 @@ __host__ __device__ constexpr size_t smem_floats() {
            + 2 * (size_t)T * NS      // Bb, Cc
            + 2 * (size_t)T * PS      // Xs, dYs
            + 2 * (size_t)T * TS      // Sc, dP (mask folded in)
-           + 2 * (size_t)T * HALF    // Phi, theta (at most 32 tokens)
+           + 2 * (size_t)T * PHS     // Phi, theta (at most 32 tokens)
            + (size_t)T * (HALF + 1)  // dPh
            + (size_t)T * T           // Mk, dMk (tokens <= 32: two [Cb][Cb] <= 32*32 halves)
            + (size_t)T * T
@@ -740,7 +741,8 @@ __host__ __device__ constexpr size_t smem_floats() {
            + 2 * (size_t)T           // 1/rms rows
            + 2 * (size_t)HALF        // carry, rcar
            + NT + 4
-           + 4 * (size_t)NT;         // per-lane bias sums [R][NT]
+           + 4 * (size_t)NT          // per-lane bias sums [R][NT]
+           + 4 * (size_t)T;          // BCNorm: sums of squares of half rows [2][T][2]
 }
 }  // namespace mf
 
@@ -767,9 +769,9 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     float *dYs = Xs + T * PS;         // [T][PS]
     float *Sc = dYs + T * PS;         // [T][TS]
     float *dP = Sc + T * TS;          // [T][TS]
-    float *Phi = dP + T * TS;         // [Cb][HALF]
-    float *thv = Phi + T * HALF;      // [Cb][HALF]
-    float *dPh = thv + T * HALF;      // [Cb][HALF + 1]
+    float *Phi = dP + T * TS;         // [Cb][PHS]
+    float *thv = Phi + T * PHS;       // [Cb][PHS]
+    float *dPh = thv + T * PHS;       // [Cb][HALF + 1]
     float *Mk = dPh + T * (HALF + 1); // [Cb][Cb]
     float *dMk = Mk + T * T;          // [Cb][Cb]
     float *offq = dMk + T * T;        // [T][4]
@@ -797,6 +799,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     float *sbias = misc + 4;          // [2][R][N] B / C bias of this head
     float *sgain = sbias + 8 * N;     // [2][N] BCNorm gains (ones when absent)
     float *sbacc = sgain + 2 * N;     // [R][NT] this lane's bias sums over the chunks done so far
+    float *qsq = sbacc + 4 * NT;      // [2][T][2] sums of squares of the half rows of B and C
 #pragma unroll
     for (int r = 0; r < R; ++r) sbacc[r * NT + tid] = 0.f;
 
@@ -820,14 +823,16 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     };
     // loads of a chunk's inputs into registers (they can be in flight during other work)
     auto stage_issue = [&](int64_t c0, int nv, bool withC, StageRegs &sr) {
-        sr.d = 0.f;
-        sr.lm = 0.f;
-        sr.av = 0.f;
-        if (tid <= Cb && tid <= nv && c0 + tid < L) {
-            const int64_t o = (bi * L + c0 + tid) * H + hi;
-            sr.d = a.dt[o];
-            sr.lm = a.lam[o];
-            sr.av = a.A[o];
+        {
+            // token scalars of threads 0..Cb (clamped indices; zeroed past the chunk)
+            const bool okt = tid <= Cb && tid <= nv && c0 + tid < L;
+            int64_t tt = c0 + (tid <= Cb ? tid : Cb);
+            tt = tt < L ? tt : L - 1;
+            const int64_t o = (bi * L + tt) * H + hi;
+            const float d = a.dt[o], lm = a.lam[o], av = a.A[o];
+            sr.d = okt ? d : 0.f;
+            sr.lm = okt ? lm : 0.f;
+            sr.av = okt ? av : 0.f;
         }
         // The loads of a thread step through the chunk with a fixed token stride: row
         // rho = rho0 + (NT / N) kk, i.e. token t0 + (NT / N / R) kk, same rank (R divides NT / N).
@@ -880,17 +885,26 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         }
     };
     // the registers into LDS
-    auto stage_put = [&](int nv, const StageRegs &sr) {
+    auto stage_put = [&](int nv, const StageRegs &sr, bool withC) {
         if (tid <= Cb) {
             dtv[tid] = sr.d;
             lamv[tid] = sr.lm;
             Av[tid] = sr.av;
         }
+        // BCNorm: a wave holds half of one row (N = 128) per kk, so a wave sum of
+        // the squares is that half row's share
 #pragma unroll
         for (int kk = 0; kk < KBC; ++kk) {
             const int e = tid + kk * NT;
             Bb[(e / N) * NS + e % N] = sr.vb[kk];
             Cc[(e / N) * NS + e % N] = sr.vc[kk];
+            const float qb = wave_sum(sr.vb[kk] * sr.vb[kk]);
+            const float qc = withC ? wave_sum(sr.vc[kk] * sr.vc[kk]) : 0.f;
+            if ((tid & 63) == 0) {
+                const int hr = 2 * (e / N) + (e % N) / 64;
+                qsq[hr] = qb;
+                qsq[2 * T + hr] = qc;
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < KXY; ++kk) {
@@ -902,8 +916,9 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         for (int kk = 0; kk < KPH; ++kk) {
             const int e = tid + kk * NT;
             if (e < Cb * HALF) {
-                Phi[e] = sr.vph[kk] * sr.vth[kk] * kInv2Pi;
-                thv[e] = sr.vth[kk];
+                const int eo = (e / HALF) * PHS + e % HALF;
+                Phi[eo] = sr.vph[kk] * sr.vth[kk] * kInv2Pi;
+                thv[eo] = sr.vth[kk];
             }
         }
     };
@@ -926,20 +941,15 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
 #pragma unroll
         for (int m = 0; m < HALF / 16; ++m) {
             const int i = 8 * w + 2 * m + (l >> 5), t = l & 31;
-            float v = (t < nv) ? Phi[t * HALF + i] : 0.f;
+            float v = (t < nv) ? Phi[t * PHS + i] : 0.f;
             v = group_scan<32>(v, l) + carry[i];
-            if (t < nv) Phi[t * HALF + i] = v;
+            if (t < nv) Phi[t * PHS + i] = v;
         }
-        const int nrow = withC ? 2 * T : T;
-        for (int grp = tid / 8; grp < nrow; grp += NT / 8) {
-            const int lane8 = tid % 8;
-            const bool isC = grp >= T;
-            const int rho = isC ? grp - T : grp;
-            const float *row = (isC ? Cc : Bb) + rho * NS;
-            float ss = 0.f;
-            for (int n = lane8; n < N; n += 8) ss += row[n] * row[n];
-            ss = group_sum<8>(ss);
-            if (lane8 == 0) (isC ? rsC : rsB)[rho] = 1.0f / sqrtf(ss / (float)N + a.eps);
+        if (tid < (withC ? 2 * T : T)) {
+            const bool isC = tid >= T;
+            const int rho = isC ? tid - T : tid;
+            const float *q = qsq + (isC ? 2 * T : 0) + 2 * rho;
+            (isC ? rsC : rsB)[rho] = 1.0f / sqrtf((q[0] + q[1]) / (float)N + a.eps);
         }
         __syncthreads();
         const float cse = lcs[nv - 1];
@@ -955,7 +965,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             if (t < nv) {
                 const float *bb = sbias + r * N;
                 float sn, cs;
-                sincos_rev(Phi[t * HALF + i], &sn, &cs);
+                sincos_rev(Phi[t * PHS + i], &sn, &cs);
                 const float B0 = Bb[rho * NS + i] * rsB[rho] * sgain[i] + bb[i];
                 const float B1 = Bb[rho * NS + i + HALF] * rsB[rho] * sgain[i + HALF] + bb[i + HALF];
                 bl = cs * B0 + sn * B1;
@@ -978,7 +988,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     auto stage_chunk = [&](int64_t c0, int nv, bool withC) {
         StageRegs sr;
         stage_issue(c0, nv, withC, sr);
-        stage_put(nv, sr);
+        stage_put(nv, sr, withC);
         stage_finish(c0, nv, withC);
     };
 
@@ -1041,7 +1051,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         const int64_t c0 = (int64_t)k * Cb;
         const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
         float *slot = chk + (int64_t)k * slotf;
-        stage_put(nv, fsr);
+        stage_put(nv, fsr, false);
         if (k + 1 < nch) {
             const int64_t c1 = c0 + Cb;
             stage_issue(c1, (int)((L - c1) < Cb ? (L - c1) : Cb), false, fsr);
@@ -1065,7 +1075,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma4(av, ld_str(&Xs[kk * PS + 16 * pt + lr], PS), acc[pt]);
         }
-        for (int i = tid; i < HALF; i += NT) carry[i] = __builtin_amdgcn_fractf(Phi[(nv - 1) * HALF + i]);
+        for (int i = tid; i < HALF; i += NT) carry[i] = __builtin_amdgcn_fractf(Phi[(nv - 1) * PHS + i]);
         __syncthreads();
     }
     {
@@ -1128,6 +1138,9 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             for (int kb = 0; kb < 4; ++kb)
                 uprev[q][kb] = *reinterpret_cast<const f4 *>(&slotf_[(16 * (nt0 + 4 * q) + lr) * P + 16 * kb + 4 * lg]);
     }
+    // (reverse chunks are staged in place: holding the next chunk's loads across
+    // steps 6 and 7 cost 33-55 spilled registers and ran slower)
+    StageRegs rsr;
     for (int k = nch - 1; k >= 0; --k) {
         const int l = opaque(tid & 63), lr = l & 15, lg = l >> 4;
         const int64_t c0 = (int64_t)k * Cb;
@@ -1154,7 +1167,9 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
             part = wave_sum(part);
             if (l == 0) red[w] = part;
         }
-        stage_chunk(c0, nv, true);
+        stage_issue(c0, nv, true, rsr);
+        stage_put(nv, rsr, true);
+        stage_finish(c0, nv, true);
         const float cse = lcs[nv - 1];
 
         // (1) dC_bar from the carried-state output term: e^{cs_t} sum_p dY[rho][p] S_in[n][p]
@@ -1324,7 +1339,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                                dch * Cc[rho * NS + i];
                 if (t < nv) {
                     float sn, cs;
-                    sincos_rev(Phi[t * HALF + i], &sn, &cs);
+                    sincos_rev(Phi[t * PHS + i], &sn, &cs);
                     const int64_t o = (((bi * L + c0 + t) * H + hi) * R + r) * N;
                     const float gbl = cs * dbl - sn * dbh, gbh = sn * dbl + cs * dbh;
                     const float gcl = cs * dcl - sn * dch, gch = sn * dcl + cs * dch;
@@ -1398,7 +1413,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                 if (v_) {
                     const int64_t tok = bi * L + c0 + t;
                     ba.gth[(tok * H + hi) * HALF + i] = dtv[t] * rc;
-                    dth_acc += thv[t * HALF + i] * rc;
+                    dth_acc += thv[t * PHS + i] * rc;
                 }
                 if (t == 0) rcar[i] += tot;
             }
