@@ -1153,7 +1153,9 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 uin[q][kb] = *reinterpret_cast<const f4 *>(&slot[(16 * (nt0 + 4 * q) + lr) * P + 16 * kb + 4 * lg]);
-        for (int i = tid; i < HALF; i += NT) carry[i] = slot[N * P + i];
+        // the chunk's starting angle carry: loaded with the staging loads below and
+        // stored with them (a load-then-store here had cost its own memory round trip)
+        const float carry_in = slot[N * P + (tid < HALF ? tid : 0)];
         // <S_out, dS>: S_out fragments in registers, dS in LDS (waves 4..7 hold the same fragments)
         {
             float part = 0.f;
@@ -1169,6 +1171,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         }
         stage_issue(c0, nv, true, rsr);
         stage_put(nv, rsr, true);
+        if (tid < HALF) carry[tid] = carry_in;
         stage_finish(c0, nv, true);
         const float cse = lcs[nv - 1];
 
