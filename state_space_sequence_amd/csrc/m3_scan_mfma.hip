@@ -122,6 +122,7 @@ struct alignas(16) Smem {
     alignas(16) float tokn[4];            // dt, lambda of the token after that chunk
     alignas(16) float angtot[4][kHalf];   // per wave: angle total of its rows (revolutions)
     alignas(16) float carry[kHalf];       // cumulative angle before the current chunk, mod 1 revolution
+    alignas(16) float woff[4][kHalf];     // per wave: angle offset of its rows (carry + earlier waves' totals)
     alignas(16) float bias[2][4][kN];     // B / C bias of this head, per rank
     alignas(16) float normw[2][kN];       // BCNorm gains (ones when absent)
     alignas(16) float onw[kP];            // output-norm gain of this head (ones when absent)
@@ -597,28 +598,26 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         }
 
         // ---- rotate into the frame of the workgroup's first token: add the carry
-        // and the totals of the earlier waves' rows. Branch-free (uniform 0/1
-        // weights), so that all the LDS reads are issued before the first wait.
+        // and the totals of the earlier waves' rows. Lane l forms that offset for
+        // channel l once (branch-free, uniform 0/1 weights) into the wave's LDS
+        // row; each lane then adds it to its 16 slots.
         {
             const float f0 = (w > 0) ? 1.f : 0.f, f1 = (w > 1) ? 1.f : 0.f, f2 = (w > 2) ? 1.f : 0.f;
-            f32x4 cy[4], a0[4], a1[4], a2[4];
+            float o = sm.carry[l];
+            o = __builtin_fmaf(f0, sm.angtot[0][l], o);
+            o = __builtin_fmaf(f1, sm.angtot[1][l], o);
+            sm.woff[w][l] = __builtin_fmaf(f2, sm.angtot[2][l], o);
+            // the wave reads other lanes' entries: its LDS accesses complete in order
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i0 = 32 * (q >> 1) + 8 * lg + 4 * (q & 1);
-                cy[q] = *reinterpret_cast<const f32x4 *>(&sm.carry[i0]);
-                a0[q] = *reinterpret_cast<const f32x4 *>(&sm.angtot[0][i0]);
-                a1[q] = *reinterpret_cast<const f32x4 *>(&sm.angtot[1][i0]);
-                a2[q] = *reinterpret_cast<const f32x4 *>(&sm.angtot[2][i0]);
+                const f32x4 of = *reinterpret_cast<const f32x4 *>(&sm.woff[w][i0]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ph[4 * q + k] += of[k];
             }
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    float v = ph[4 * q + k] + cy[q][k];
-                    v = __builtin_fmaf(f0, a0[q][k], v);
-                    v = __builtin_fmaf(f1, a1[q][k], v);
-                    ph[4 * q + k] = __builtin_fmaf(f2, a2[q][k], v);
-                }
         }
         if (w == 0)
             newcarry = __builtin_amdgcn_fractf(sm.carry[l] + sm.angtot[0][l] + sm.angtot[1][l] + sm.angtot[2][l] +
