@@ -224,7 +224,7 @@ __device__ __forceinline__ ChunkBase chunk_base(const ScanArgs &a, int64_t bi, i
 struct ChunkRegs {
     bf16x8 rb[4], rc[4], xf[2];
     bf16x4 zf[4];  // fused projections: Z' of the row's token at the lane's output columns
-    f32x4 th[4];
+    f32x4 th[4];  // theta of the lane's angle slots: all 4 blocks for R = 1, its own 4 / R blocks otherwise
 };
 
 // nv: tokens of the chunk; avail: tokens from the chunk's first one to the end
@@ -256,11 +256,15 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
         }
     }
     if constexpr (PART == 1) return;
+    // angle slot block b (4 channels) of lane group lg starts at channel
+    // 32 (b >> 1) + 8 lg + 4 (b & 1), i.e. float4 8 (b >> 1) + 2 lg + (b & 1). The R
+    // rank lanes of a token share its angles: rank r owns blocks (4 / R) r ..
     const f32x4 *pt = reinterpret_cast<const f32x4 *>(cb.th + oth);
-    cr.th[0] = pt[2 * ln.lg];
-    cr.th[1] = pt[2 * ln.lg + 1];
-    cr.th[2] = pt[8 + 2 * ln.lg];
-    cr.th[3] = pt[8 + 2 * ln.lg + 1];
+#pragma unroll
+    for (int q = 0; q < 4 / R; ++q) {
+        const int b = (4 / R) * ln.r_row + q;
+        cr.th[q] = pt[8 * (b >> 1) + 2 * ln.lg + (b & 1)];
+    }
     const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + offx);
     cr.xf[0] = px[ln.lg];
     cr.xf[1] = px[4 + ln.lg];
@@ -489,8 +493,9 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         for (int k = 0; k < 4; ++k) {
             rb[k] = cr.rb[k];
             rc[k] = cr.rc[k];
-            th[k] = cr.th[k];
         }
+#pragma unroll
+        for (int k = 0; k < 4 / R; ++k) th[k] = cr.th[k];
         xf[0] = cr.xf[0];
         xf[1] = cr.xf[1];
         bf16x4 zf[4];
@@ -561,27 +566,25 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 
         // ---- angles: prefix over the tokens of this wave's rows (16-lane DPP rows)
         // slot k (0..15) is channel i = 8lg + k (k < 8) or 32 + 8lg + (k - 8)
-        // (in revolutions: dt theta / 2 pi)
+        // (in revolutions: dt theta / 2 pi). A lane computes the 4 / R slot blocks
+        // its rank owns (load_chunk); the token's other rank lanes hold the rest.
+        constexpr int NB = 4 / R;  // owned blocks of 4 slots
         const float drev = drow * kInv2Pi;
-        float ph[16];
+        float ph[4 * NB];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            ph[4 * k + 0] = drev * th[k][0];
-            ph[4 * k + 1] = drev * th[k][1];
-            ph[4 * k + 2] = drev * th[k][2];
-            ph[4 * k + 3] = drev * th[k][3];
-        }
+        for (int q = 0; q < NB; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ph[4 * q + j] = drev * th[q][j];
 #pragma unroll
         for (int sh = R; sh < 16; sh <<= 1)
 #pragma unroll
-            for (int k = 0; k < 16; ++k) ph[k] += dpp_row_shr(ph[k], sh);
-        if (lr == 15) {
+            for (int k = 0; k < 4 * NB; ++k) ph[k] += dpp_row_shr(ph[k], sh);
+        if (lr >= 16 - R) {  // the wave's last token: its rank lanes hold every block
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                *reinterpret_cast<f32x4 *>(&sm.angtot[w][32 * h2 + 8 * lg]) =
-                    f32x4{ph[8 * h2 + 0], ph[8 * h2 + 1], ph[8 * h2 + 2], ph[8 * h2 + 3]};
-                *reinterpret_cast<f32x4 *>(&sm.angtot[w][32 * h2 + 8 * lg + 4]) =
-                    f32x4{ph[8 * h2 + 4], ph[8 * h2 + 5], ph[8 * h2 + 6], ph[8 * h2 + 7]};
+            for (int q = 0; q < NB; ++q) {
+                const int b = NB * r_row + q;
+                *reinterpret_cast<f32x4 *>(&sm.angtot[w][32 * (b >> 1) + 8 * lg + 4 * (b & 1)]) =
+                    f32x4{ph[4 * q + 0], ph[4 * q + 1], ph[4 * q + 2], ph[4 * q + 3]};
             }
         }
         __syncthreads();  // B1
@@ -612,9 +615,9 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int i0 = 32 * (q >> 1) + 8 * lg + 4 * (q & 1);
-                const f32x4 of = *reinterpret_cast<const f32x4 *>(&sm.woff[w][i0]);
+            for (int q = 0; q < NB; ++q) {
+                const int b = NB * r_row + q;
+                const f32x4 of = *reinterpret_cast<const f32x4 *>(&sm.woff[w][32 * (b >> 1) + 8 * lg + 4 * (b & 1)]);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) ph[4 * q + k] += of[k];
             }
@@ -622,6 +625,29 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         if (w == 0)
             newcarry = __builtin_amdgcn_fractf(sm.carry[l] + sm.angtot[0][l] + sm.angtot[1][l] + sm.angtot[2][l] +
                                                sm.angtot[3][l]);
+        // sine and cosine of the owned slots; slot block b comes from the token's
+        // rank lane b / NB (a DPP quad permute within the token's R lanes)
+        float osn[4 * NB], ocn[4 * NB];
+#pragma unroll
+        for (int k = 0; k < 4 * NB; ++k) sincos_rev(ph[k], osn[k], ocn[k]);
+        auto slot_sc = [&](int sl, float &sn, float &cn) {  // sl: compile-time slot 0..15
+            if constexpr (R == 1) {
+                sn = osn[sl];
+                cn = ocn[sl];
+            } else {
+                const int b = sl >> 2, ro = b / NB, k = 4 * (b % NB) + (sl & 3);
+                // every lane of a group of R takes lane (group base + ro)
+                if constexpr (R == 4) {
+                    if (ro == 0) { sn = dpp_mov<0x00>(osn[k]); cn = dpp_mov<0x00>(ocn[k]); }
+                    else if (ro == 1) { sn = dpp_mov<0x55>(osn[k]); cn = dpp_mov<0x55>(ocn[k]); }
+                    else if (ro == 2) { sn = dpp_mov<0xAA>(osn[k]); cn = dpp_mov<0xAA>(ocn[k]); }
+                    else { sn = dpp_mov<0xFF>(osn[k]); cn = dpp_mov<0xFF>(ocn[k]); }
+                } else {  // R == 2: quad_perm [ro, ro, 2 + ro, 2 + ro]
+                    if (ro == 0) { sn = dpp_mov<0xA0>(osn[k]); cn = dpp_mov<0xA0>(ocn[k]); }
+                    else { sn = dpp_mov<0xF5>(osn[k]); cn = dpp_mov<0xF5>(ocn[k]); }
+                }
+            }
+        };
         bf16x8 bfr[4], cfr[4];
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2) {
@@ -647,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 for (int jj = 0; jj < 4; ++jj) {
                     const int j = 4 * jh + jj;
                     float sn, cn;
-                    sincos_rev(ph[8 * ks2 + j], sn, cn);
+                    slot_sc(8 * ks2 + j, sn, cn);
                     const float bl = (float)rb[ks2][j] * (HAS_W ? abl[jj] : rsb) + blo[jj];
                     const float bh = (float)rb[ks2 + 2][j] * (HAS_W ? abh[jj] : rsb) + bhi[jj];
                     // rows past the end of the sequence need no zeroing: their
