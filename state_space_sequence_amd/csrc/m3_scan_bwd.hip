@@ -1593,8 +1593,17 @@ __global__ __launch_bounds__(kThreads) void bwd_theta_kernel(BwdArgs ba, float *
     const int64_t total = a.b * a.L * G * half;
     for (int64_t e = blockIdx.x * (int64_t)kThreads + threadIdx.x; e < total; e += (int64_t)gridDim.x * kThreads) {
         const int64_t i = e % half, g = (e / half) % G, bt = e / (half * G);
+        const float *src = ba.gth + (bt * H + g * hpg) * half + i;
         float s = 0.f;
-        for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) s += ba.gth[(bt * H + h) * half + i];
+        int64_t h = 0;
+        for (; h + 8 <= hpg; h += 8) {  // eight heads of loads in flight, summed in order
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = src[(h + k) * half];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) s += v[k];
+        }
+        for (; h < hpg; ++h) s += src[h * half];
         dtheta[e] = s;
     }
 }
