@@ -465,6 +465,11 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
     }
 
     for (int64_t c = pos.c_begin; c < pos.c_end; ++c) {
+        // Wave priorities by phase: the two workgroups of a CU share each SIMD and
+        // are rarely in the same phase. Favouring the rotation (2) and the score,
+        // mask and output stage (3) over the rest (0) lets the wave that the next
+        // barrier waits on issue first: 0.428 -> 0.368 ms for SISO b8 L4096.
+        __builtin_amdgcn_s_setprio(0);
         const int64_t c0 = c * C;
         const int nv = (int)((L - c0) < C ? (L - c0) : C);
         const ChunkBase cb = chunk_base<R, FUSED>(a, bi, hi, g, c0);
@@ -588,6 +593,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             }
         }
         __syncthreads();  // B1
+        __builtin_amdgcn_s_setprio(2);
 
         // ---- X^T through the matrix core: T = X-fragment x selection, exact for
         // bf16 operands; the output lane holds rows 16w + 4lg..+3 of column lr.
@@ -726,6 +732,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             if (more) load_chunk<MODE, R, FUSED, 1>(chunk_base<R, FUSED>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
         }
 
+        __builtin_amdgcn_s_setprio(3);
         if constexpr (MODE != kPass1) {
             // ---- S^T blocks (s-block sb <= w) for this wave's t-block
             f32x4 sT[4];
@@ -871,6 +878,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 }
             }
             __syncthreads();  // B3: St and Bb reads done
+            __builtin_amdgcn_s_setprio(0);
         }
 
         if (more) load_chunk<MODE, R, FUSED, (R > 1 ? 2 : 0)>(chunk_base<R, FUSED>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
