@@ -204,8 +204,8 @@ def cpu_baseline(shape, chains_target):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-extra", action="store_true", help="only the headline prefill")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-chains", type=int, default=128)
@@ -308,7 +308,7 @@ def main():
             pl = m3.plan(shp)
             w2 = m3.workspace_bytes(shp)
             wsp = torch.empty(w2, dtype=torch.uint8, device=dev) if w2 else None
-            wl, pr = time_prefill(m3, torch, dd, sm_, 10, 3, yy, hh, wsp)
+            wl, pr = time_prefill(m3, torch, dd, sm_, 50, 20, yy, hh, wsp)
             ms = sum(pr) / len(pr)
             bb = prefill_bytes(sm_)
             fd, fc = prefill_flops(sm_)
@@ -358,10 +358,10 @@ def main():
             ydec = torch.empty_like(de["x"])
             base = (de["x"], de["Braw"], de["Craw"], de["dt"], de["A"], de["lam"], de["theta"],
                     de["B_bias"], de["C_bias"])
-            for k in range(8):
+            for k in range(40):
                 m3.decode_step(*base, states[k % 4], x_prev=de["x_prev"], Braw_prev=de["Braw_prev"], y=ydec)
             torch.cuda.synchronize()
-            reps = 40
+            reps = 200
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
             evs[0].record()
             for k in range(reps):
@@ -390,16 +390,16 @@ def main():
         hf2 = torch.empty((sf.batch, sf.nheads, sf.headdim, sf.dstate), dtype=torch.float32, device=dev)
         fargs = (df["x_in"], df["z_in"], df["W_X"], df["W_Z"], df["W_O"], df["Braw"], df["Craw"], df["dt"],
                  df["A"], df["lam"], df["theta"], df["B_bias"], df["C_bias"])
-        for _ in range(3):
+        for _ in range(10):
             m3.scan_fused_fwd(*fargs, chunk=sf.chunk, eps=sf.eps, o=of, h_final=hf2)
         torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(31)]
         evs[0].record()
-        for k in range(10):
+        for k in range(30):
             m3.scan_fused_fwd(*fargs, chunk=sf.chunk, eps=sf.eps, o=of, h_final=hf2)
             evs[k + 1].record()
         torch.cuda.synchronize()
-        ms = sum(evs[k].elapsed_time(evs[k + 1]) for k in range(10)) / 10
+        ms = sum(evs[k].elapsed_time(evs[k + 1]) for k in range(30)) / 30
         bb = fused_prefill_bytes(sf)
         ent = {"tokens_per_s": round(sf.batch * sf.seqlen / (ms * 1e-3), 1), "ms": round(ms, 4),
                "hbm_frac": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bb}
@@ -451,10 +451,10 @@ def main():
                                 sb.chunk, m3.M3_BF16, sb.eps)
             wsb = m3.scan_bwd_workspace_bytes(shp)
             wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
-            for _ in range(2):
+            for _ in range(5):
                 m3.scan_bwd(*bargs, eps=sb.eps, grads=grads, workspace=wsp)
             torch.cuda.synchronize()
-            reps = 5
+            reps = 15
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
             evs[0].record()
             for k in range(reps):
