@@ -177,6 +177,23 @@ def test_decode_bf16_state_matches_oracle(case):
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("name", ["decode_siso_n128", "decode_mimo4_n128", "decode_siso_n64", "decode_mimo4_n64"])
+def test_decode_bf16_state_full_workloads(name):
+    """The four decode workloads at full size (b128 H64 P64), state stored in bf16,
+    in the launch configuration the benchmark times."""
+    shape = WORKLOADS[name]
+    say("decode bf16 state workload", name)
+    inp = make_decode_inputs(shape, seed=3)
+    inp["h"] = round_bf16(inp["h"])
+    y, h = gpu_decode(inp, shape, bf16_state=True)
+    yr, hr = oracle.decode(inp, shape)
+    say("err y %.2e h %.2e" % (relerr(y, yr), relerr(h, hr)))
+    assert relerr(h, hr) < TOL_BF16_STATE
+    assert relerr(y, yr) < TOL_BF16
+    assert np.array_equal(round_bf16(h.astype(np.float32)), h.astype(np.float32))
+
+
+@pytest.mark.gpu
 def test_decode_bf16_state_several_steps():
     """Eight chained steps with a bf16 state against the oracle stepped the same
     way (its state rounded to bf16 between steps, by the test)."""
