@@ -215,8 +215,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on exactly one GPU (the kernels shard over batch and heads, "
-              "but no multi-GPU path is built); got --gpus %d" % args.gpus, file=sys.stderr)
+        print("bench.py: measures one GPU only (the work shards over batch and heads, but the library "
+              "has no multi-GPU path); got --gpus %d" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
