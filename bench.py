@@ -191,9 +191,11 @@ def cpu_baseline(shape, chains_target):
         "unit": "tokens/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": "%d of %d (batch, head) chains, full L=%d, fp64 C oracle with OpenMP over chains; "
-                  "%.2f s measured, scaled by %d/%d" % (chains, shape.batch * shape.nheads, shape.seqlen, dt,
-                                                         shape.batch * shape.nheads, chains),
+        "sample": ("the whole workload: all %d (batch, head) chains, L=%d, fp64 C oracle with OpenMP over "
+                   "chains; %.2f s measured" % (chains, shape.seqlen, dt)) if frac >= 1 else
+                  ("%d of %d (batch, head) chains, full L=%d, fp64 C oracle with OpenMP over chains; "
+                   "%.2f s measured, scaled by %d/%d" % (chains, shape.batch * shape.nheads, shape.seqlen, dt,
+                                                          shape.batch * shape.nheads, chains)),
         "cpu_model": cpu_model(),
         "value_1thread": shape.batch * shape.seqlen / full_time1,
         "sample_1thread": "%d chains on one thread, %.2f s measured, scaled by %d/%d"
