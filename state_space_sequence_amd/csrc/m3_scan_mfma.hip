@@ -229,8 +229,7 @@ struct ChunkRegs {
 
 // nv: tokens of the chunk; avail: tokens from the chunk's first one to the end
 // of the sequence (capped at C + 1).
-// PART 1: raw B and C rows; PART 2: theta, x (and z); 0: both.
-template <int MODE, int R, bool FUSED, int PART = 0>
+template <int MODE, int R, bool FUSED>
 __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, int nv, int avail, int64_t G,
                                            int64_t H, ChunkRegs &cr) {
     // Every load is unconditional, from a clamped index; the consumer zeroes what
@@ -246,16 +245,13 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
     int oth = tr * (int)G * kHalf;
     int offx = FUSED ? tr * (int)H * kP : (tr * (int)H * R + ln.r_row) * kP;
     asm volatile("" : "+v"(offBC), "+v"(oth), "+v"(offx));
-    if constexpr (PART != 2) {
-        const bf16x8 *pb = reinterpret_cast<const bf16x8 *>(cb.B + offBC);
-        const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + offBC);
+    const bf16x8 *pb = reinterpret_cast<const bf16x8 *>(cb.B + offBC);
+    const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + offBC);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            cr.rb[ks] = pb[4 * ks];
-            if constexpr (MODE != kPass1) cr.rc[ks] = pc[4 * ks];
-        }
+    for (int ks = 0; ks < 4; ++ks) {
+        cr.rb[ks] = pb[4 * ks];
+        if constexpr (MODE != kPass1) cr.rc[ks] = pc[4 * ks];
     }
-    if constexpr (PART == 1) return;
     // angle slot block b (4 channels) of lane group lg starts at channel
     // 32 (b >> 1) + 8 lg + 4 (b & 1), i.e. float4 8 (b >> 1) + 2 lg + (b & 1). The R
     // rank lanes of a token share its angles: rank r owns blocks (4 / R) r ..
@@ -722,15 +718,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 
         // ---- the next chunk's inputs. A burst of every wave's loads right after B2
         // filled the CU's queue of outstanding misses and blocked the issuing waves
-        // for a memory latency. Measured best: one burst before the state update
-        // for R = 1; for R > 1 the raw B, C rows here and the rest there.
+        // for a memory latency. Measured best (with the phase priorities): one burst
+        // before the state update, for every R.
         const int64_t c1 = c0 + C;
         const bool more = c + 1 < pos.c_end;
         const int nv1 = (int)((L - c1) < C ? (L - c1) : C);
         const int avail1 = (int)((L - c1) < C + 1 ? (L - c1) : C + 1);
-        if constexpr (R > 1) {
-            if (more) load_chunk<MODE, R, FUSED, 1>(chunk_base<R, FUSED>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
-        }
 
         __builtin_amdgcn_s_setprio(3);
         if constexpr (MODE != kPass1) {
@@ -881,7 +874,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             __builtin_amdgcn_s_setprio(0);
         }
 
-        if (more) load_chunk<MODE, R, FUSED, (R > 1 ? 2 : 0)>(chunk_base<R, FUSED>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
+        if (more) load_chunk<MODE, R, FUSED>(chunk_base<R, FUSED>(a, bi, hi, g, c1), ln, nv1, avail1, G, H, cr);
         scal = load_scalars<R>(a, sbase, bi, c + 2 < pos.c_end ? c + 2 : pos.c_end - 1, ln);
 
         // ---- state update: acc[q][pb] = exp(cs_end) acc + Bt-rows x Xt
