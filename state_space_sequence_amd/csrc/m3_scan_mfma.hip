@@ -1046,13 +1046,35 @@ hipError_t launch_r(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
 bool mfma_kernel_available() { return true; }
 
 int mfma_auto_segments(int64_t chains, int64_t nchunks) {
-    // one resident wave of workgroups is 2 per CU; split only when the chains
-    // alone leave most of them idle, and keep segments at least 8 chunks long
+    // One resident wave of workgroups is 2 per CU. Split only when the chains
+    // alone leave most of them idle, and keep segments at least 8 chunks long.
+    // Start from the most segments that fit one wave; take more (up to two
+    // waves) only when they fill the waves at least 3 points better, since each
+    // segment adds a first pass over its chunks. Measured: 192 chains, 2 -> 5
+    // segments, 10-17% faster; 48 chains, 10 -> 21, 2% faster; 64, 96 and 128
+    // chains (already >= 94% full with one wave) 4-5% slower with twice the
+    // segments.
     const int64_t slots = 2 * kCUs;
     if (chains * 4 >= slots * 3) return 1;
-    int64_t nseg = slots / (chains > 0 ? chains : 1);
-    if (nseg > nchunks / 8) nseg = nchunks / 8;
-    return nseg < 1 ? 1 : (int)nseg;
+    const int64_t c = chains > 0 ? chains : 1;
+    const int64_t cap = nchunks / 8 > 1 ? nchunks / 8 : 1;
+    int64_t best = slots / c;
+    if (best > cap) best = cap;
+    if (best < 1) best = 1;
+    auto fill = [&](int64_t n) {
+        const int64_t wg = c * n, waves = (wg + slots - 1) / slots;
+        return (double)wg / (double)(waves * slots);
+    };
+    double fb = fill(best);
+    const int64_t n1 = best;
+    for (int64_t n = n1 + 1; n <= 2 * n1 + 1 && n <= cap; ++n) {
+        const double f = fill(n);
+        if (f > fb + 0.03) {
+            best = n;
+            fb = f;
+        }
+    }
+    return (int)best;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
