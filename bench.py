@@ -342,6 +342,21 @@ def main():
                 torch.cuda.synchronize()
                 ent["decode_256_steps_us_per_step"] = round(1e3 * e0.elapsed_time(e1) / 256, 3)
                 log("  then 256 decode steps:", ent["decode_256_steps_us_per_step"], "us/step")
+                # the same 256 steps captured once in a HIP graph and replayed: the
+                # step is launch-bound at this size (48 workgroups, 3.2 MB)
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    for _ in range(256):
+                        m3.decode_step(*dargs, x_prev=xp, Braw_prev=bp, y=ydec)
+                graph.replay()
+                torch.cuda.synchronize()
+                e0.record()
+                graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                ent["decode_256_steps_graph_us_per_step"] = round(1e3 * e0.elapsed_time(e1) / 256, 3)
+                log("  the same from one graph:", ent["decode_256_steps_graph_us_per_step"], "us/step")
+                del graph
                 del de, h
             extra[nm] = ent
             del dd, yy, hh, wsp

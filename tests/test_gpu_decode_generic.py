@@ -220,3 +220,49 @@ def test_decode_bf16_state_several_steps():
         assert relerr(yg, yr) < TOL_BF16 and relerr(hg, hr) < 4 * TOL_BF16_STATE
         # the GPU keeps its own chained state; the oracle's is rounded the same way
         h_ref = round_bf16(hr.astype(np.float32)).astype(np.float64)
+
+
+@pytest.mark.gpu
+def test_decode_steps_replayed_from_a_graph():
+    """Four decode steps captured once in a HIP graph and replayed three times,
+    with eager steps on a copy of the state between the replays: every replay
+    gives the eager result bit for bit (the same kernel on the same inputs)."""
+    import torch
+    from state_space_sequence_amd import m3
+    shape = Shape(2, 1, 24, 1, 64, 128, 4, 1, "bf16")
+    inp = make_decode_inputs(shape, seed=21)
+    d = m3.to_device(inp, shape.io)
+    base = (d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"], d["B_bias"], d["C_bias"])
+    kw = dict(eps=shape.eps, x_prev=d["x_prev"], Braw_prev=d["Braw_prev"])
+    h_graph, h_eager = d["h"].clone(), d["h"].clone()
+    y_graph, y_eager = torch.empty_like(d["x"]), torch.empty_like(d["x"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the capture, on a scratch state
+        h_tmp = d["h"].clone()
+        m3.decode_step(*base, h_tmp, y=y_graph, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(4):
+            m3.decode_step(*base, h_graph, y=y_graph, **kw)
+    torch.cuda.synchronize()
+    h_graph.copy_(d["h"])  # capture launches nothing: start both from the same state
+    for rep in range(3):
+        say("graph replay", rep)
+        graph.replay()
+        for _ in range(4):
+            m3.decode_step(*base, h_eager, y=y_eager, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(h_graph, h_eager)
+        assert torch.equal(y_graph, y_eager)
+        # eager work between replays
+        h_eager.mul_(1.0)
+    # the chained result also matches the oracle stepped four times per replay
+    hr = inp["h"].astype(np.float64)
+    for _ in range(12):
+        step = dict(inp)
+        step["h"] = hr.astype(np.float32)
+        _, hr = oracle.decode(step, shape)
+    assert relerr(h_graph.cpu().numpy(), hr) < TOL_F32
