@@ -214,6 +214,9 @@ def main():
     ap.add_argument("--cpu-chains", type=int, default=512)
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for counter collection: one 512 MiB copy, then 2 prefill steps")
+    ap.add_argument("--pmc-decode", action="store_true",
+                    help="short run for counter collection: one 512 MiB copy, then 2 decode steps of the "
+                         "SISO and MIMO-4 N128 workloads (fp32 state)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -231,6 +234,28 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     log("device:", props.name, getattr(props, "gcnArchName", ""), "CUs:", props.multi_processor_count)
+
+    if args.pmc_decode:
+        src = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reference copy: reads and writes exactly 512 MiB
+        torch.cuda.synchronize()
+        del src, dst
+        alg = {}
+        for nm in ("decode_siso_n128", "decode_mimo4_n128"):
+            sd = WORKLOADS[nm]
+            de = m3.to_device(make_decode_inputs(sd, seed=3), sd.io)
+            ydec = torch.empty_like(de["x"])
+            for _ in range(2):
+                m3.decode_step(de["x"], de["Braw"], de["Craw"], de["dt"], de["A"], de["lam"], de["theta"],
+                               de["B_bias"], de["C_bias"], de["h"], x_prev=de["x_prev"],
+                               Braw_prev=de["Braw_prev"], y=ydec)
+            torch.cuda.synchronize()
+            alg[nm] = decode_bytes(sd, 4)
+            del de
+        print(json.dumps({"pmc_decode": True, "copy_bytes": 512 * 1024 * 1024, "decode_bytes_alg": alg}))
+        return
 
     name = "siso_prefill_1p5b"
     s = WORKLOADS[name]
