@@ -80,6 +80,10 @@ GENERIC_CASES = [
     (1, 5, 2, 1, 16, 16, 1, 64, "f32", False, True, False, False),       # shorter than a chunk
     (1, 192, 2, 1, 64, 128, 1, 64, "f32", True, True, False, True),      # 1.5B-like head shape
     (2, 130, 2, 1, 64, 128, 1, 64, "bf16", False, False, False, True),   # bf16 io, fp32 math
+    # at the fp32 kernel's limits (N, P <= 128, N P <= 8192, chunk R <= 64)
+    (1, 90, 2, 1, 128, 64, 1, 64, "f32", True, True, False, True),       # P = 128
+    (1, 70, 2, 1, 64, 128, 2, 32, "f32", False, True, True, False),      # N = 128, R = 2
+    (1, 40, 1, 1, 128, 16, 4, 16, "bf16", True, False, False, True),     # P = 128, R = 4
 ]
 
 
