@@ -78,18 +78,19 @@ def test_backward_is_deterministic(N, P):
         assert np.array_equal(g1[k], g2[k]), k
 
 
-def test_backward_siso_prefill_1p5b_sampled():
-    """The full b8 L4096 H64 workload through the backward; the oracle recomputes the
-    per-chain gradients (dx, dt, A, lam, h0) of one sampled (batch, head) chain."""
+@pytest.mark.parametrize("name,b,h", [("siso_prefill_1p5b", 5, 41), ("mimo4_prefill_1p5b", 2, 17)])
+def test_backward_prefill_1p5b_sampled(name, b, h):
+    """The full b8 L4096 H64 workload (SISO, and MIMO rank 4) through the backward; the
+    oracle recomputes the per-chain gradients (dx, dt, A, lam, h0) of one sampled
+    (batch, head) chain."""
     from state_space_sequence_amd.inputs import WORKLOADS, slice_chain
-    shape = WORKLOADS["siso_prefill_1p5b"]
+    shape = WORKLOADS[name]
     say("backward workload", shape)
     inp = make_scan_inputs(shape, seed=55)
     dy, _ = upstream(shape, 56, False, "bf16")
     got = gpu_scan_bwd(inp, shape, dy, None)
     for k, v in got.items():
         assert np.isfinite(v).all(), k
-    b, h = 5, 41
     sub, s1 = slice_chain(inp, shape, b, h)
     sub["h0"] = np.zeros((1, 1, shape.headdim, shape.dstate), dtype=np.float32)
     ref = oracle.scan_grads(sub, s1, np.ascontiguousarray(dy[b:b + 1, :, h:h + 1]))
