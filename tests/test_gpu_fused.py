@@ -172,11 +172,15 @@ def test_fused_mimo4_prefill_long_sampled():
     assert p.nsegments > 1
 
 
-def test_fused_decode_mimo4_n128_sampled():
-    """Full decode workload; the oracle recomputes a few (batch, head) pairs."""
+@pytest.mark.parametrize("bf16_state", [False, True])
+def test_fused_decode_mimo4_n128_sampled(bf16_state):
+    """Full decode workload, state in fp32 or bf16; the oracle recomputes a few
+    (batch, head) pairs."""
     shape = WORKLOADS["decode_mimo4_n128"]
     inp = make_fused_decode_inputs(shape, seed=7)
-    o, h = gpu_decode_fused(inp, shape)
+    if bf16_state:
+        inp["h"] = round_bf16(inp["h"])
+    o, h = gpu_decode_fused(inp, shape, bf16_state=bf16_state)
     for (b, hh) in [(0, 0), (77, 31), (127, 63)]:
         sub = {}
         for k, v in inp.items():
@@ -193,4 +197,4 @@ def test_fused_decode_mimo4_n128_sampled():
         orf, hr = oracle.decode_fused(sub, shape.replace(batch=1, nheads=1))
         eo, eh = relerr(o[b:b + 1, hh:hh + 1], orf), relerr(h[b:b + 1, hh:hh + 1], hr)
         say("  (%d,%d): err o %.2e h %.2e" % (b, hh, eo, eh))
-        assert eo < TOL_BF16 and eh < TOL_BF16
+        assert eo < TOL_BF16 and eh < (TOL_BF16_STATE if bf16_state else TOL_BF16)
