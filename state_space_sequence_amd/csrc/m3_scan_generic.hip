@@ -20,6 +20,11 @@
 //    exp(cs_t) C_bar_t^T S, S <- exp(cs_end) S + sum_s exp(cs_end - cs_s) w_s B_bar_s X_s^T,
 //    with cs the chunk-local cumulative log decay.
 //  * MIMO rows are the flattened (token, rank) pairs; the mask depends on tokens.
+//  * angles are carried in revolutions (turns): the running total is reduced
+//    mod 1 at every chunk boundary (a whole turn changes no rotation), and each
+//    chunk's prefix starts from that reduced carry, so an angle never grows
+//    beyond a chunk's worth of increments and keeps its fp32 resolution over
+//    any sequence length; sine and cosine take it through sincospif;
 //  * output epilogue: the skip D[h] x_t (the D term of y = C h + D x) and the
 //    grouped output RMSNorm of every (token, rank) row over its P channels; with
 //    the norm the chunk's rows are staged in LDS until their mean square is known.
@@ -30,6 +35,7 @@ namespace m3i {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr float kInv2Pi = 0.15915494309189535f;
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a) {
@@ -53,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a) {
     float *wgt = lcs + C;            // [C] folded weight w
     float *gam = wgt + C;            // [C] gamma
     float *dtv = gam + C;            // [C] dt
-    float *carry = dtv + C;          // [HALF] cumulative angle before this chunk
+    float *carry = dtv + C;          // [HALF] cumulative angle before this chunk, revolutions mod 1
     float *rsB = carry + HALF;       // [T] 1/rms of B rows
     float *rsC = rsB + T;            // [T]
     float *misc = rsC + T;           // [4]: exp(cs_end)
@@ -122,12 +128,13 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a) {
             }
             misc[0] = expf(run);
         }
-        // ---- cumulative angles per channel (serial over the chunk's tokens)
+        // ---- cumulative angles per channel (serial over the chunk's tokens), in
+        // revolutions from the reduced carry
         for (int i = tid; i < HALF; i += kThreads) {
             float ph = carry[i];
             for (int t = 0; t < nv; ++t) {
                 const int64_t tok = bi * L + c0 + t;
-                ph += a.dt[tok * a.H + hi] * a.theta[(tok * a.G + g) * HALF + i];
+                ph += a.dt[tok * a.H + hi] * a.theta[(tok * a.G + g) * HALF + i] * kInv2Pi;
                 Phi[t * HALF + i] = ph;
             }
         }
@@ -163,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a) {
                 const float C0 = ld_io<BF16>(a.Craw, row + i) * rsC[rho] * wcl + cb[i];
                 const float C1 = ld_io<BF16>(a.Craw, row + i + HALF) * rsC[rho] * wch + cb[i + HALF];
                 float sn, cs;
-                sincosf(Phi[t * HALF + i], &sn, &cs);
+                sincospif(2.0f * Phi[t * HALF + i], &sn, &cs);
                 // R(-Phi): (u, v) -> (cos u + sin v, -sin u + cos v)
                 bl = cs * B0 + sn * B1;
                 bhv = -sn * B0 + cs * B1;
@@ -181,9 +188,13 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a) {
             Xs[e] = (t < nv) ? ld_io<BF16>(a.x, (((bi * L + c0 + t) * a.H + hi) * R + r) * P + p) : 0.f;
         }
         __syncthreads();
-        // carry the angle to the end of this chunk (Phi no longer needed after the sync below)
+        // carry the angle to the end of this chunk, reduced mod 1 revolution (Phi
+        // no longer needed after the sync below)
         float newcarry = 0.f;
-        if (tid < HALF) newcarry = (nv > 0) ? Phi[(nv - 1) * HALF + tid] : carry[tid];
+        if (tid < HALF) {
+            const float e = (nv > 0) ? Phi[(nv - 1) * HALF + tid] : carry[tid];
+            newcarry = e - floorf(e);
+        }
         __syncthreads();
         if (tid < HALF) carry[tid] = newcarry;
         // ---- masked scores P[rho][sigma]
@@ -253,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(ScanArgs a) {
         for (int e = tid; e < HALF * P; e += kThreads) {
             const int i = e / P, p = e % P;
             float sn, cs;
-            sincosf(carry[i], &sn, &cs);
+            sincospif(2.0f * carry[i], &sn, &cs);
             const float u = S[i * P + p], v = S[(i + HALF) * P + p];
             a.h_final[(bh * P + p) * N + i] = cs * u - sn * v;
             a.h_final[(bh * P + p) * N + i + HALF] = sn * u + cs * v;
