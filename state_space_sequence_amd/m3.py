@@ -1,9 +1,12 @@
 """Thin Python binding of libm3 (include/m3.h): argument marshalling only.
 
 Every step of the mixer runs in the library's HIP kernels; this module checks
-that tensors are CUDA (HIP) tensors of the right dtype and contiguity, fills the
-C structs and passes raw pointers plus the current stream. If the library is not
-built, importing this module raises: there is no fallback.
+every tensor against the shape and dtype the call implies (the C ABI sees raw
+pointers only, so a short or mistyped buffer would be read or written past its
+end on the GPU), then that tensors are contiguous GPU tensors on one device,
+fills the C structs and passes raw pointers plus the current stream. All checks
+raise before the library is called. If the library is not built, importing this
+module raises: there is no fallback.
 """
 from __future__ import annotations
 
@@ -55,6 +58,14 @@ class Plan(ctypes.Structure):
                 ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class DeviceFacts(ctypes.Structure):
+    _fields_ = [("compute_units", ctypes.c_int32), ("clock_khz", ctypes.c_int32),
+                ("memory_clock_khz", ctypes.c_int32), ("memory_bus_bits", ctypes.c_int32),
+                ("wall_clock_khz", ctypes.c_int32), ("l2_bytes", ctypes.c_int64),
+                ("lds_bytes_per_block", ctypes.c_int64), ("wave_size", ctypes.c_int32),
+                ("arch", ctypes.c_char * 64)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libm3.so is not built (%s); run __graft_entry__.build() or "
@@ -77,6 +88,13 @@ def _load():
     lib.m3_status_str.restype = ctypes.c_char_p
     lib.m3_status_str.argtypes = [ctypes.c_int]
     lib.m3_version.restype = ctypes.c_int
+    lib.m3_probe_copy.restype = ctypes.c_int
+    lib.m3_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    lib.m3_probe_mfma_bf16.restype = ctypes.c_int
+    lib.m3_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                       ctypes.c_void_p]
+    lib.m3_probe_device_facts.restype = ctypes.c_int
+    lib.m3_probe_device_facts.argtypes = [ctypes.c_int, ctypes.POINTER(DeviceFacts)]
     return lib
 
 
@@ -104,6 +122,77 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return t.data_ptr()
+
+
+def _expect(name, t, shape, dtype, device=None):
+    """Raise unless t is None or a tensor of exactly this shape and dtype (dtype may
+    be a tuple of allowed dtypes) and, when given, on the device of that index."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s: expected a torch.Tensor, got %s" % (name, type(t).__name__))
+    if t.dtype is not dtype and not (isinstance(dtype, tuple) and t.dtype in dtype):
+        raise TypeError("%s: dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.shape != shape:
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if device is not None and t.get_device() != device:
+        raise ValueError("%s: on device %d, expected %d (the device of the inputs)" % (name, t.get_device(), device))
+
+
+def _expect_all(specs, device):
+    """specs: (name, tensor, shape tuple, dtype); device: get_device() of the inputs."""
+    for name, t, shape, dtype in specs:
+        if t is not None:
+            _expect(name, t, shape, dtype, device)
+
+
+def _need(name, t):
+    if t is None:
+        raise ValueError("%s is required" % name)
+
+
+def _scan_specs(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, B_normw, C_normw, h0, x_prev, Braw_prev,
+                *, b, L, H, G, R, P, N, io, xr=True):
+    """(name, tensor, shape, dtype) of the prefill inputs; xr: x and x_prev carry the
+    rank axis (False for the fused projections' X')."""
+    f32 = torch.float32
+    xs = (b, L, H, R, P) if xr else (b, L, H, P)
+    xps = (b, H, R, P) if xr else (b, H, P)
+    return [("x", x, xs, io), ("Braw", Braw, (b, L, G, R, N), io), ("Craw", Craw, (b, L, G, R, N), io),
+            ("dt", dt, (b, L, H), f32), ("A", A, (b, L, H), f32), ("lam", lam, (b, L, H), f32),
+            ("theta", theta, (b, L, G, N // 2), f32), ("B_bias", B_bias, (H, R, N), f32),
+            ("C_bias", C_bias, (H, R, N), f32), ("B_normw", B_normw, (N,), f32),
+            ("C_normw", C_normw, (N,), f32), ("h0", h0, (b, H, P, N), f32),
+            ("x_prev", x_prev, xps, io), ("Braw_prev", Braw_prev, (b, G, R, N), io)]
+
+
+def _epilogue_specs(D, out_normw, H, P):
+    return [("D", D, (H,), torch.float32), ("out_normw", out_normw, (H, P), torch.float32)]
+
+
+def _weight_specs(W_X, W_Z, W_O, H, P, R):
+    f32 = torch.float32
+    return [("W_X", W_X, (H, P, R), f32), ("W_Z", W_Z, (H, P, R), f32), ("W_O", W_O, (H, P, R), f32)]
+
+
+def _decode_specs(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, B_normw, C_normw, x_prev, Braw_prev, h,
+                  *, b, H, G, R, P, N, io, xr=True):
+    f32 = torch.float32
+    xs = (b, H, R, P) if xr else (b, H, P)
+    return [("x", x, xs, io), ("Braw", Braw, (b, G, R, N), io), ("Craw", Craw, (b, G, R, N), io),
+            ("dt", dt, (b, H), f32), ("A", A, (b, H), f32), ("lam", lam, (b, H), f32),
+            ("theta", theta, (b, G, N // 2), f32), ("B_bias", B_bias, (H, R, N), f32),
+            ("C_bias", C_bias, (H, R, N), f32), ("B_normw", B_normw, (N,), f32),
+            ("C_normw", C_normw, (N,), f32), ("x_prev", x_prev, xs, io),
+            ("Braw_prev", Braw_prev, (b, G, R, N), io), ("h", h, (b, H, P, N), (f32, torch.bfloat16))]
+
+
+def _dims5(name, t, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s: expected a torch.Tensor" % name)
+    if t.dim() != ndim:
+        raise ValueError("%s: expected %d dimensions, got shape %s" % (name, ndim, tuple(t.shape)))
+    return tuple(t.shape)
 
 
 def _io_dtype(t):
@@ -160,13 +249,22 @@ def scan_fwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *, chunk=64, eps=
     """Chunked-scan prefill (m3_scan_fwd). Shapes: x [b,L,H,R,P], Braw/Craw [b,L,G,R,N],
     dt/A/lam [b,L,H], theta [b,L,G,N/2], biases [H,R,N]; optional skip D [H] and output
     norm (out_norm=True, gain out_normw [H,P]). Returns (y, h_final)."""
+    b, L, H, R, P = _dims5("x", x, 5)
+    _, _, G, _, N = _dims5("Braw", Braw, 5)
+    io = x.dtype
+    _io_dtype(x)
+    _expect_all(_scan_specs(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, B_normw, C_normw, h0, x_prev,
+                            Braw_prev, b=b, L=L, H=H, G=G, R=R, P=P, N=N, io=io)
+                + _epilogue_specs(D, out_normw, H, P)
+                + [("y", y, (b, L, H, R, P), io), ("h_final", h_final, (b, H, P, N), torch.float32),
+                   ("workspace", workspace, (None if workspace is None else workspace.numel(),), torch.uint8)],
+                x.get_device())
     shape = scan_shape(x, Braw, chunk, eps, force_generic=force_generic, nsegments=nsegments,
                        out_norm=out_norm)
     if y is None:
         y = torch.empty_like(x)
     if h_final is None and want_state:
-        b, _, H, _, P = x.shape
-        h_final = torch.empty((b, H, P, Braw.shape[4]), dtype=torch.float32, device=x.device)
+        h_final = torch.empty((b, H, P, N), dtype=torch.float32, device=x.device)
     ws = workspace_bytes(shape)
     if ws and workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=x.device)
@@ -187,10 +285,19 @@ def scan_fused_fwd(x_in, z_in, W_X, W_Z, W_O, Braw, Craw, dt, A, lam, theta, B_b
     x_in, z_in [b,L,H,P] (X', Z'), W_X/W_Z/W_O [H,P,R], x_prev_in [b,H,P] or None;
     skip D [H], output norm out_norm None / "pre" / "post" with gain out_normw [H,P].
     Returns (o [b,L,H,P], h_final)."""
-    b, L, H, P = x_in.shape
-    R = W_X.shape[2]
-    G, N = Braw.shape[2], Braw.shape[4]
-    shape = make_shape(b, L, H, G, P, N, R, chunk, _io_dtype(x_in), eps, _norm_flags(out_norm), nsegments)
+    b, L, H, P = _dims5("x_in", x_in, 4)
+    R = _dims5("W_X", W_X, 3)[2]
+    _, _, G, _, N = _dims5("Braw", Braw, 5)
+    io = x_in.dtype
+    iot = _io_dtype(x_in)
+    _expect_all(_scan_specs(x_in, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, B_normw, C_normw, h0,
+                            x_prev_in, Braw_prev, b=b, L=L, H=H, G=G, R=R, P=P, N=N, io=io, xr=False)
+                + _weight_specs(W_X, W_Z, W_O, H, P, R) + _epilogue_specs(D, out_normw, H, P)
+                + [("z_in", z_in, (b, L, H, P), io), ("o", o, (b, L, H, P), io),
+                   ("h_final", h_final, (b, H, P, N), torch.float32),
+                   ("workspace", workspace, (None if workspace is None else workspace.numel(),), torch.uint8)],
+                x_in.get_device())
+    shape = make_shape(b, L, H, G, P, N, R, chunk, iot, eps, _norm_flags(out_norm), nsegments)
     if o is None:
         o = torch.empty_like(x_in)
     if h_final is None and want_state:
@@ -217,9 +324,16 @@ def scan_bwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, dy, *, eps=1e-5, 
     """Prefill backward (m3_scan_bwd): gradients of <dy, y> + <dh_final, h_final> with
     respect to the forward inputs (same tensors as scan_fwd). Returns a dict of fp32
     tensors named like the inputs (x, Braw, ..., h0, x_prev, Braw_prev when present)."""
-    b, L, H, R, P = x.shape
-    G, N = Braw.shape[2], Braw.shape[4]
-    shape = make_shape(b, L, H, G, P, N, R, max(1, 64 // R), _io_dtype(x), eps)
+    b, L, H, R, P = _dims5("x", x, 5)
+    _, _, G, _, N = _dims5("Braw", Braw, 5)
+    iot = _io_dtype(x)
+    _expect_all(_scan_specs(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, B_normw, C_normw, h0, x_prev,
+                            Braw_prev, b=b, L=L, H=H, G=G, R=R, P=P, N=N, io=x.dtype)
+                + [("dy", dy, (b, L, H, R, P), x.dtype), ("dh_final", dh_final, (b, H, P, N), torch.float32),
+                   ("workspace", workspace, (None if workspace is None else workspace.numel(),), torch.uint8)],
+                x.get_device())
+    _need("dy", dy)
+    shape = make_shape(b, L, H, G, P, N, R, max(1, 64 // R), iot, eps)
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
     if grads is None:
@@ -237,6 +351,15 @@ def scan_bwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, dy, *, eps=1e-5, 
         if x_prev is not None:
             grads["x_prev"] = torch.empty(x_prev.shape, **f32)
             grads["Braw_prev"] = torch.empty(Braw_prev.shape, **f32)
+    # every gradient buffer is fp32 and shaped like the input it belongs to
+    gshape = {"x": x.shape, "Braw": Braw.shape, "Craw": Craw.shape, "dt": dt.shape, "A": A.shape,
+              "lam": lam.shape, "theta": theta.shape, "B_bias": B_bias.shape, "C_bias": C_bias.shape,
+              "B_normw": (N,), "C_normw": (N,), "h0": (b, H, P, N), "x_prev": (b, H, R, P),
+              "Braw_prev": (b, G, R, N)}
+    for k, t in grads.items():
+        if k not in gshape:
+            raise ValueError("grads: unknown entry %r" % k)
+        _expect("grads[%r]" % k, t, tuple(gshape[k]), torch.float32, x.get_device())
     ws = scan_bwd_workspace_bytes(shape)
     if workspace is None and ws:
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
@@ -260,10 +383,15 @@ def decode_step(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, h, *, eps=1e-5
     """One decode step (m3_decode_step). x [b,H,R,P], Braw/Craw [b,G,R,N], dt/A/lam [b,H],
     theta [b,G,N/2], h [b,H,P,N] updated in place: fp32, or bf16 (then the step runs with
     M3_FLAG_BF16_STATE); skip D and output norm as in scan_fwd. Returns y [b,H,R,P]."""
-    b, H, R, P = x.shape
-    G, N = Braw.shape[1], Braw.shape[3]
+    b, H, R, P = _dims5("x", x, 4)
+    _, G, _, N = _dims5("Braw", Braw, 4)
+    iot = _io_dtype(x)
+    _need("h", h)
+    _expect_all(_decode_specs(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, B_normw, C_normw, x_prev,
+                              Braw_prev, h, b=b, H=H, G=G, R=R, P=P, N=N, io=x.dtype)
+                + _epilogue_specs(D, out_normw, H, P) + [("y", y, (b, H, R, P), x.dtype)], x.get_device())
     flags = (M3_FLAG_BF16_STATE if h.dtype == torch.bfloat16 else 0) | _norm_flags(out_norm)
-    shape = make_shape(b, 1, H, G, P, N, R, 1, _io_dtype(x), eps, flags)
+    shape = make_shape(b, 1, H, G, P, N, R, 1, iot, eps, flags)
     if y is None:
         y = torch.empty_like(x)
     io = DecodeIO(_ptr(x), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
@@ -279,11 +407,17 @@ def decode_fused_step(x_in, z_in, W_X, W_Z, W_O, Braw, Craw, dt, A, lam, theta, 
                       D=None, out_norm=None, out_normw=None, stream=None):
     """One decode step with the fused projections. x_in, z_in [b,H,P], W_* [H,P,R],
     h [b,H,P,N] (fp32 or bf16) updated in place. Returns o [b,H,P]."""
-    b, H, P = x_in.shape
-    R = W_X.shape[2]
-    G, N = Braw.shape[1], Braw.shape[3]
+    b, H, P = _dims5("x_in", x_in, 3)
+    R = _dims5("W_X", W_X, 3)[2]
+    _, G, _, N = _dims5("Braw", Braw, 4)
+    iot = _io_dtype(x_in)
+    _need("h", h)
+    _expect_all(_decode_specs(x_in, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, B_normw, C_normw,
+                              x_prev_in, Braw_prev, h, b=b, H=H, G=G, R=R, P=P, N=N, io=x_in.dtype, xr=False)
+                + _weight_specs(W_X, W_Z, W_O, H, P, R) + _epilogue_specs(D, out_normw, H, P)
+                + [("z_in", z_in, (b, H, P), x_in.dtype), ("o", o, (b, H, P), x_in.dtype)], x_in.get_device())
     flags = (M3_FLAG_BF16_STATE if h.dtype == torch.bfloat16 else 0) | _norm_flags(out_norm)
-    shape = make_shape(b, 1, H, G, P, N, R, 1, _io_dtype(x_in), eps, flags)
+    shape = make_shape(b, 1, H, G, P, N, R, 1, iot, eps, flags)
     if o is None:
         o = torch.empty_like(x_in)
     io = DecodeIO(_ptr(x_in), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
@@ -309,3 +443,40 @@ def to_device(inp: dict, io: str, device="cuda"):
             t = t.to(torch.bfloat16)
         out[k] = t.contiguous()
     return out
+
+
+# ------------------------------------------------------ calibration probes ---
+def probe_copy(src, dst, blocks=0, stream=None):
+    """m3_probe_copy: dst <- src (same number of bytes, uint8 or any dtype, contiguous)."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("probe_copy: src and dst sizes differ")
+    _check(lib.m3_probe_copy(_ptr(src), _ptr(dst), nb, int(blocks), _stream(stream)))
+
+
+def probe_mfma_bf16(blocks, iters, seed=1.0, out=None, clock=None, stream=None):
+    """m3_probe_mfma_bf16: returns (out float[blocks], clock int64[2*blocks]) on the GPU;
+    flops = blocks * 4 * iters * 2 * 16384."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        out = torch.empty(blocks, dtype=torch.float32, device=dev)
+    if clock is None:
+        clock = torch.empty(2 * blocks, dtype=torch.int64, device=dev)
+    _expect("out", out, (blocks,), torch.float32)
+    _expect("clock", clock, (2 * blocks,), torch.int64)
+    _check(lib.m3_probe_mfma_bf16(_ptr(out), _ptr(clock), int(blocks), int(iters), float(seed), _stream(stream)))
+    return out, clock
+
+
+def probe_mfma_flops(blocks, iters) -> int:
+    return blocks * 4 * iters * 2 * 16 * 16 * 32 * 2
+
+
+def device_facts(dev=0) -> dict:
+    f = DeviceFacts()
+    _check(lib.m3_probe_device_facts(int(dev), ctypes.byref(f)))
+    return {"compute_units": f.compute_units, "clock_mhz": f.clock_khz / 1e3,
+            "memory_clock_mhz": f.memory_clock_khz / 1e3, "memory_bus_bits": f.memory_bus_bits,
+            "wall_clock_mhz": f.wall_clock_khz / 1e3, "l2_bytes": f.l2_bytes,
+            "lds_bytes_per_block": f.lds_bytes_per_block, "wave_size": f.wave_size,
+            "arch": f.arch.decode(errors="replace")}
