@@ -118,6 +118,79 @@ def time_prefill(m3, torch, d, s, steps, warmup, y, hf, ws):
     return wall, per
 
 
+def settle_clocks(m3, torch, d, s, y, hf, ws, min_s=0.2):
+    """Untimed prefill launches until at least min_s seconds of GPU work have run,
+    so the timed region starts with the clocks already at their working level
+    (20 launches after 5 had varied by up to 20% between runs as clocks settled)."""
+    args = scan_args(d, s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(20):
+            m3.scan_fwd(*args, chunk=s.chunk, eps=s.eps, y=y, h_final=hf, workspace=ws)
+        n += 20
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= min_s:
+            break
+    return {"settle_ms": round(1e3 * (time.perf_counter() - t0), 1), "settle_launches": n}
+
+
+def measured_ceilings(m3, torch, dev, facts):
+    """The HBM and matrix-core ceilings one kernel reaches on this device: the
+    library's stream copy over 512 MiB (twice the last-level cache) and its dense
+    bf16 matrix-core loop, with the shader clock that loop ran at."""
+    nbytes = 512 * 1024 * 1024
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        m3.probe_copy(src, dst)
+    torch.cuda.synchronize()
+    reps = 10
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for k in range(reps):
+        m3.probe_copy(src, dst)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    tcopy = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(reps))[reps // 2]
+    copy_gbs = 2 * nbytes / (tcopy * 1e-3) / 1e9
+    del src, dst
+    blocks, iters = 8 * facts["compute_units"], 8192
+    out, clk = m3.probe_mfma_bf16(blocks, iters)
+    for _ in range(2):
+        m3.probe_mfma_bf16(blocks, iters, out=out, clock=clk)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev[0].record()
+    for k in range(5):
+        m3.probe_mfma_bf16(blocks, iters, out=out, clock=clk)
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    tm = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(5))[2]
+    tflops = m3.probe_mfma_flops(blocks, iters) / (tm * 1e-3) / 1e12
+    c = clk.cpu().double().reshape(-1, 2)
+    mhz = float((c[:, 0] / c[:, 1]).median()) * facts["wall_clock_mhz"] if facts["wall_clock_mhz"] else None
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "hbm_copy_frac_of_spec": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "hbm_copy_bytes": "512 MiB read + 512 MiB written per launch (m3_probe_copy)",
+            "mfma_bf16_TFLOPs": round(tflops, 1), "mfma_frac_of_spec": round(tflops / BF16_DENSE_TFLOPS, 4),
+            "mfma_loop": "%d workgroups x 4 waves x %d x 2 v_mfma_f32_16x16x32_bf16 (m3_probe_mfma_bf16)"
+                         % (blocks, iters),
+            "shader_clock_mhz_in_mfma_loop": None if mhz is None else round(mhz, 1)}
+
+
+def smi_clocks():
+    """Current clocks as rocm-smi reports them (a child process; None if unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                           text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    lines = [ln.strip() for ln in r.stdout.splitlines() if "clk" in ln.lower() and "(" in ln]
+    return lines[:8] or None
+
+
 def src_digest() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -233,7 +306,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
-    log("device:", props.name, getattr(props, "gcnArchName", ""), "CUs:", props.multi_processor_count)
+    facts = m3.device_facts(0)
+    log("device:", props.name, facts)
 
     if args.pmc_decode:
         src = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -247,13 +321,16 @@ def main():
             sd = WORKLOADS[nm]
             de = m3.to_device(make_decode_inputs(sd, seed=3), sd.io)
             ydec = torch.empty_like(de["x"])
-            for _ in range(2):
+            # 8 steps over 4 state buffers (1.07 GB): as in the timed decode, no step
+            # finds its state in the 256 MB last-level cache
+            states = [de["h"].clone() for _ in range(4)]
+            for k in range(8):
                 m3.decode_step(de["x"], de["Braw"], de["Craw"], de["dt"], de["A"], de["lam"], de["theta"],
-                               de["B_bias"], de["C_bias"], de["h"], x_prev=de["x_prev"],
+                               de["B_bias"], de["C_bias"], states[k % 4], x_prev=de["x_prev"],
                                Braw_prev=de["Braw_prev"], y=ydec)
             torch.cuda.synchronize()
             alg[nm] = decode_bytes(sd, 4)
-            del de
+            del de, states
         print(json.dumps({"pmc_decode": True, "copy_bytes": 512 * 1024 * 1024, "decode_bytes_alg": alg}))
         return
 
@@ -281,6 +358,8 @@ def main():
                           "prefill_bytes_alg": prefill_bytes(s)}))
         return
 
+    settle = settle_clocks(m3, torch, d, s, y, hf, ws)
+    log("clocks settled: %s" % settle)
     log("timing %s: %d warmup + %d steps (plan: kernel %d, %d segment(s), %d workgroups)"
         % (name, args.warmup, args.steps, plan.kernel, plan.nsegments, plan.workgroups))
     wall, per = time_prefill(m3, torch, d, s, args.steps, args.warmup, y, hf, ws)
@@ -304,24 +383,13 @@ def main():
     del d, y, hf
     torch.cuda.empty_cache()
 
-    extra = {}
-    # achievable HBM bandwidth for a plain device copy (read + write), beside the spec peak
-    src = torch.empty(256 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(10):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * src.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    extra["hbm_copy_probe"] = {"GB_per_s": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
-                               "bytes": "256 MiB read + 256 MiB written per copy"}
-    log("copy probe: %.0f GB/s" % copy_gbs)
-    del src, dst
+    extra = {"timing": dict(settle, protocol="untimed launches until >= 0.2 s of GPU work, then --warmup "
+                                              "untimed and --steps timed launches back to back"),
+             "device": facts, "rocm_smi_clocks": smi_clocks()}
+    ceil = measured_ceilings(m3, torch, dev, facts)
+    extra["ceilings"] = ceil
+    log("ceilings:", ceil)
+    roof["frac_of_measured_copy"] = round(achieved / ceil["hbm_copy_GBps"], 4)
     if not args.no_extra:
         # ---- MIMO rank-4 prefill, same shape
         for nm in ("mimo4_prefill_1p5b", "mimo4_prefill_long"):
@@ -347,42 +415,56 @@ def main():
                    "segments": pl.nsegments, "workgroups": pl.workgroups}
             log(nm, ent)
             if nm == "mimo4_prefill_long":
-                # 256 decode steps continuing from the prefill's final state
-                sd = sm_.replace(seqlen=1)
-                dinp = make_decode_inputs(sd, seed=5)
-                de = m3.to_device(dinp, sd.io)
+                # 256 decode steps continuing from the prefill's final state: step k
+                # takes new token k (its own x, raw B and C, dt, A, lambda, theta) with
+                # the prefill's biases, and token k - 1 (the prefill's last token for
+                # k = 0) as its previous token
+                K = 256
+                cont = make_scan_inputs(sm_.replace(seqlen=K), seed=6)
+                ct = m3.to_device({k: cont[k] for k in ("x", "Braw", "Craw", "dt", "A", "lam", "theta")}, sm_.io)
+                del cont
                 h = hh.clone()
-                xp, bp = dd["x"][:, -1].contiguous(), dd["Braw"][:, -1].contiguous()
-                ydec = torch.empty_like(de["x"])
-                dargs = (de["x"], de["Braw"], de["Craw"], de["dt"], de["A"], de["lam"], de["theta"],
-                         de["B_bias"], de["C_bias"], h)
-                for _ in range(8):
-                    m3.decode_step(*dargs, x_prev=xp, Braw_prev=bp, y=ydec)
+                toks = [{k: ct[k][:, i].contiguous() for k in ct} for i in range(K)]
+                prevs = [(dd["x"][:, -1].contiguous(), dd["Braw"][:, -1].contiguous())]
+                prevs += [(toks[i]["x"], toks[i]["Braw"]) for i in range(K - 1)]
+                ydec = torch.empty_like(toks[0]["x"])
+
+                def step(i):
+                    t = toks[i]
+                    m3.decode_step(t["x"], t["Braw"], t["Craw"], t["dt"], t["A"], t["lam"], t["theta"],
+                                   dd["B_bias"], dd["C_bias"], h, eps=sm_.eps, x_prev=prevs[i][0],
+                                   Braw_prev=prevs[i][1], y=ydec)
+
+                for i in range(8):
+                    step(i)
+                h.copy_(hh)
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                for _ in range(256):
-                    m3.decode_step(*dargs, x_prev=xp, Braw_prev=bp, y=ydec)
+                for i in range(K):
+                    step(i)
                 e1.record()
                 torch.cuda.synchronize()
-                ent["decode_256_steps_us_per_step"] = round(1e3 * e0.elapsed_time(e1) / 256, 3)
+                ent["decode_256_steps_us_per_step"] = round(1e3 * e0.elapsed_time(e1) / K, 3)
                 log("  then 256 decode steps:", ent["decode_256_steps_us_per_step"], "us/step")
                 # the same 256 steps captured once in a HIP graph and replayed: the
                 # step is launch-bound at this size (48 workgroups, 3.2 MB)
                 graph = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(graph):
-                    for _ in range(256):
-                        m3.decode_step(*dargs, x_prev=xp, Braw_prev=bp, y=ydec)
+                    for i in range(K):
+                        step(i)
+                h.copy_(hh)
                 graph.replay()
+                torch.cuda.synchronize()
+                h.copy_(hh)
                 torch.cuda.synchronize()
                 e0.record()
                 graph.replay()
                 e1.record()
                 torch.cuda.synchronize()
-                ent["decode_256_steps_graph_us_per_step"] = round(1e3 * e0.elapsed_time(e1) / 256, 3)
+                ent["decode_256_steps_graph_us_per_step"] = round(1e3 * e0.elapsed_time(e1) / K, 3)
                 log("  the same from one graph:", ent["decode_256_steps_graph_us_per_step"], "us/step")
-                del graph
-                del de, h
+                del graph, toks, prevs, ct, h
             extra[nm] = ent
             del dd, yy, hh, wsp
             torch.cuda.empty_cache()

@@ -32,19 +32,45 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source into libm3.so (always rebuilds)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + ["-I", INCLUDE, "-I", CSRC] + sources() + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+def _clean(text: str) -> str:
     # the host pass does not know the packed-fp32 feature and says so; drop that noise
-    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out, flush=True)
+    return "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every HIP source into libm3.so (always rebuilds). Each source is
+    compiled to an object of its own, in parallel, then the objects are linked."""
+    tag = "%d" % os.getpid()
+    tmp = LIB + ".tmp" + tag
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    base = [hipcc()] + [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra_flags) + ["-I", INCLUDE, "-I", CSRC]
+    procs, objs = [], []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + "." + tag + ".o")
+        cmd = base + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+        objs.append(obj)
+    failed = []
+    for src, pr in procs:
+        out = _clean(pr.communicate()[0])
+        if pr.returncode != 0:
+            failed.append("%s:\n%s" % (src, out))
+        elif verbose and out.strip():
+            print(out, flush=True)
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+        cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp]
+        res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n" + _clean(res.stdout))
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,0 +1,119 @@
+// Calibration probes (include/m3_probe.h): a stream copy for the HBM ceiling, a
+// dense bf16 matrix-core loop for the MFMA ceiling and the shader clock, and the
+// runtime's device facts.
+#include <string.h>
+
+#include "m3_internal.h"
+#include "m3_probe.h"
+
+namespace m3i {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// dst = src in 16-byte lane accesses, four independent accesses in flight per
+// lane, grid-stride over the whole buffer
+__global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                   size_t n) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+        dst[i] = v0;
+        dst[i + stride] = v1;
+        dst[i + 2 * stride] = v2;
+        dst[i + 3 * stride] = v3;
+    }
+    for (; i < n; i += stride) dst[i] = src[i];
+}
+
+// 2 independent 16x16x32 bf16 accumulation chains per wave; enough waves per
+// SIMD cover the matrix core's latency. (With more chains per wave the compiler
+// renamed the accumulators on every trip with register moves between the matrix
+// instructions.)
+__global__ __launch_bounds__(256) void mfma_kernel(float *out, long long *clk, int iters, float seed) {
+    __shared__ float part[4];
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    bf16x8 a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = (__bf16)(seed * (float)((l + 3 * j) % 17 - 8) * (1.f / 1024.f));
+        b[j] = (__bf16)((float)((5 * l + j) % 13 - 6) * (1.f / 1024.f));
+    }
+    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+    asm volatile("" ::: "memory");
+    const long long t0 = clock64(), r0 = wall_clock64();
+    for (int it = 0; it < iters; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
+    }
+    const f32x4 t = c0 + c1;
+    float s = (t[0] + t[1]) + (t[2] + t[3]);
+    asm volatile("" : "+v"(s)::"memory");
+    const long long t1 = clock64(), r1 = wall_clock64();
+    s = wave_sum(s);
+    if (l == 0) part[w] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        out[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+        if (clk) {
+            clk[2 * blockIdx.x] = t1 - t0;
+            clk[2 * blockIdx.x + 1] = r1 - r0;
+        }
+    }
+}
+
+}  // namespace
+}  // namespace m3i
+
+using namespace m3i;
+
+extern "C" {
+
+m3_status m3_probe_copy(const void *src, void *dst, size_t bytes, int blocks, void *stream) {
+    if (blocks < 0 || bytes % 16 != 0) return M3_ERR_INVALID_ARG;
+    if (bytes == 0) return M3_OK;
+    if (!src || !dst) return M3_ERR_INVALID_ARG;
+    if ((((uintptr_t)src) & 15u) || (((uintptr_t)dst) & 15u)) return M3_ERR_MISALIGNED;
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return M3_ERR_INVALID_ARG;
+    if (blocks == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return M3_ERR_HIP;
+        blocks = 8 * cus;
+    }
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                       static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), bytes / 16);
+    return hipGetLastError() == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+m3_status m3_probe_mfma_bf16(float *out, int64_t *clock, int blocks, int iters, float seed, void *stream) {
+    if (!out || blocks < 1 || iters < 1) return M3_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), out,
+                       reinterpret_cast<long long *>(clock), iters, seed);
+    return hipGetLastError() == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+m3_status m3_probe_device_facts(int dev, m3_device_facts *f) {
+    if (!f) return M3_ERR_INVALID_ARG;
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return M3_ERR_HIP;
+    int wall = 0;
+    if (hipDeviceGetAttribute(&wall, hipDeviceAttributeWallClockRate, dev) != hipSuccess) wall = 0;
+    memset(f, 0, sizeof(*f));
+    f->compute_units = p.multiProcessorCount;
+    f->clock_khz = p.clockRate;
+    f->memory_clock_khz = p.memoryClockRate;
+    f->memory_bus_bits = p.memoryBusWidth;
+    f->wall_clock_khz = wall;
+    f->l2_bytes = p.l2CacheSize;
+    f->lds_bytes_per_block = (int64_t)p.sharedMemPerBlock;
+    f->wave_size = p.warpSize;
+    strncpy(f->arch, p.gcnArchName, sizeof(f->arch) - 1);
+    return M3_OK;
+}
+
+}  // extern "C"

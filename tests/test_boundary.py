@@ -4,13 +4,14 @@ plans the expected kernel for each workload."""
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "m3.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 LIB = os.path.join(ROOT, "state_space_sequence_amd", "libm3.so")
 
 
@@ -24,14 +25,17 @@ def m3():
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(m3_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        names |= set(re.findall(r"\b(m3_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function(m3):
     names = declared_functions()
-    assert "m3_scan_fwd" in names and "m3_decode_step" in names
+    assert "m3_scan_fwd" in names and "m3_decode_step" in names and "m3_probe_copy" in names
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), "libm3.so does not export %s" % n
@@ -264,3 +268,27 @@ def test_backward_validated_on_host(m3):
     assert _bwd(m3, _shape(m3, flags=m3.M3_FLAG_OUT_NORM), io, _fake_grads(m3, io)) == -2
     # shapes beyond the LDS tiles
     assert _bwd(m3, _shape(m3, dstate=256, headdim=16), io, _fake_grads(m3, io)) == -2
+
+
+# ------------------------------------------------- calibration probes (host) --
+def test_probe_copy_validates_before_any_hip_call(m3):
+    f = m3.lib.m3_probe_copy
+    assert f(0x100000, 0x200000, 17, 0, None) == m3_status(m3, "INVALID_ARG")      # not a multiple of 16
+    assert f(None, 0x200000, 64, 0, None) == m3_status(m3, "INVALID_ARG")          # null source
+    assert f(0x100000, None, 64, 0, None) == m3_status(m3, "INVALID_ARG")
+    assert f(0x100004, 0x200000, 64, 0, None) == m3_status(m3, "MISALIGNED")
+    assert f(0x100000, 0x100010, 64, 0, None) == m3_status(m3, "INVALID_ARG")      # overlapping
+    assert f(0x100000, 0x200000, 64, -1, None) == m3_status(m3, "INVALID_ARG")
+    assert f(None, None, 0, 0, None) == 0                                           # nothing to copy
+
+
+def test_probe_mfma_and_facts_validate(m3):
+    g = m3.lib.m3_probe_mfma_bf16
+    assert g(None, None, 4, 4, 1.0, None) == m3_status(m3, "INVALID_ARG")
+    assert g(0x100000, None, 0, 4, 1.0, None) == m3_status(m3, "INVALID_ARG")
+    assert g(0x100000, None, 4, 0, 1.0, None) == m3_status(m3, "INVALID_ARG")
+    assert m3.lib.m3_probe_device_facts(0, None) == m3_status(m3, "INVALID_ARG")
+
+
+def m3_status(m3, name):
+    return {"INVALID_ARG": -1, "UNSUPPORTED": -2, "MISALIGNED": -3, "WORKSPACE_TOO_SMALL": -4, "HIP": -5}[name]
