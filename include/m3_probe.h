@@ -26,8 +26,9 @@
 extern "C" {
 #endif
 
-/* Stream copy: dst[i] = src[i] for `bytes` bytes, 16 bytes per lane access,
- * grid-stride, `blocks` workgroups of 256 threads (0 picks 8 per compute unit).
+/* Stream copy: dst[i] = src[i] for `bytes` bytes, in 16 KiB tiles of 256 lanes x
+ * four 16-byte non-temporal accesses; `blocks` workgroups walk the tiles with a
+ * stride of the grid (0: one workgroup per tile, a single pass).
  * src and dst are device pointers, 16-byte aligned, not overlapping; bytes is a
  * multiple of 16. HBM traffic is `bytes` read plus `bytes` written; a size well
  * above the 256 MB last-level cache measures HBM.

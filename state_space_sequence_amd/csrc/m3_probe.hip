@@ -12,20 +12,32 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// dst = src in 16-byte lane accesses, four independent accesses in flight per
-// lane, grid-stride over the whole buffer
-__global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// dst = src over 16 KiB tiles: each lane moves four 16-byte pieces 4 KiB apart,
+// all four loads in flight before the stores, with non-temporal loads and
+// stores (streamed data is not kept in the caches). Tiles are walked with a
+// stride of the grid; a grid of one workgroup per tile is one pass. Measured on
+// 512 MiB: 6.1 TB/s in one pass, against 4.2-4.9 TB/s for grid-stride loops of
+// 8-32 workgroups per compute unit and 5.3 TB/s for torch's copy.
+constexpr int kTile = 1024;  // 16-byte pieces per tile
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
                                                    size_t n) {
-    const size_t stride = (size_t)gridDim.x * 256;
-    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + 3 * stride < n; i += 4 * stride) {
-        const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-        dst[i] = v0;
-        dst[i + stride] = v1;
-        dst[i + 2 * stride] = v2;
-        dst[i + 3 * stride] = v3;
+    const size_t ntiles = (n + kTile - 1) / kTile;
+    for (size_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const size_t base = t * kTile + threadIdx.x;
+        u32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const size_t i = base + 256 * k;
+            if (i < n) v[k] = __builtin_nontemporal_load(src + i);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const size_t i = base + 256 * k;
+            if (i < n) __builtin_nontemporal_store(v[k], dst + i);
+        }
     }
-    for (; i < n; i += stride) dst[i] = src[i];
 }
 
 // 2 independent 16x16x32 bf16 accumulation chains per wave; enough waves per
@@ -78,15 +90,12 @@ m3_status m3_probe_copy(const void *src, void *dst, size_t bytes, int blocks, vo
     if ((((uintptr_t)src) & 15u) || (((uintptr_t)dst) & 15u)) return M3_ERR_MISALIGNED;
     const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
     if (s0 < d0 + bytes && d0 < s0 + bytes) return M3_ERR_INVALID_ARG;
-    if (blocks == 0) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return M3_ERR_HIP;
-        blocks = 8 * cus;
-    }
-    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
-                       static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), bytes / 16);
+    const size_t n = bytes / 16, ntiles = (n + kTile - 1) / kTile;
+    size_t grid = blocks > 0 ? (size_t)blocks : ntiles;
+    if (grid > ntiles) grid = ntiles;
+    if (grid > 0x7fffffffu) grid = 0x7fffffffu;
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                       static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n);
     return hipGetLastError() == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 
