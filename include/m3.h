@@ -207,6 +207,25 @@ typedef struct {
 m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspace,
                       size_t ws_bytes, void *stream);
 
+/* m3_scan_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, kernels and results as m3_scan_fwd, but the segment split's
+ * workspace is a device array inside the library, fixed at
+ * m3_scan_noalloc_max_workspace_bytes() (64 MiB) per GPU, held by each GPU the
+ * library runs on until the process ends; every automatic plan fits (the largest
+ * needs about 34 MB). The call allocates and frees nothing. On its first use on a
+ * device it looks up that device's copy of the array (a host-side query, no
+ * allocation). A plan whose workspace exceeds the maximum (only reachable by
+ * forcing shape->nsegments) returns M3_ERR_WORKSPACE_TOO_SMALL before any HIP call.
+ * Calls on one GPU share its array, which keeps the last call's contents; no
+ * part of it needs to start at zero. Calls that overlap on one GPU (on different
+ * streams, or replayed graphs running concurrently) race on the array: the
+ * caller serialises them. */
+m3_status m3_scan_fwd_noalloc(const m3_shape *shape, const m3_scan_io *io, void *stream);
+
+/* The fixed workspace size of m3_scan_fwd_noalloc, in bytes. */
+size_t m3_scan_noalloc_max_workspace_bytes(void);
+
 /* Bytes of device workspace m3_scan_fwd needs for this shape (0 if none). */
 size_t m3_scan_workspace_bytes(const m3_shape *shape);
 

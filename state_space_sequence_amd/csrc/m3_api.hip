@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "m3_internal.h"
 
 namespace m3i {
@@ -89,6 +91,50 @@ m3_status make_plan(const m3_shape &s, Plan *pl) {
     return M3_OK;
 }
 
+// Device-resident scratch of the allocation-free prefill entry point: the
+// segment split's workspace (segment end states, decays and angles). Each GPU the
+// library runs on holds its own copy until the process ends. Host code never
+// passes the array's name to a kernel: its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device a call's work runs on: the stream's, or the current one for the
+// null stream.
+hipError_t call_device(hipStream_t s, int *dev) {
+    if (s) return hipStreamGetDevice(s, dev);
+    return hipGetDevice(dev);
+}
+
+// Device address of this device's scratch array, looked up on first use.
+hipError_t scratch_address(hipStream_t s, void **out) {
+    int dev = 0;
+    hipError_t e = call_device(s, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 }  // namespace m3i
 
@@ -140,8 +186,10 @@ size_t m3_scan_workspace_bytes(const m3_shape *shape) {
     return p.ws_bytes;
 }
 
-m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspace, size_t ws_bytes,
-                      void *stream) {
+// m3_scan_fwd with the workspace either the caller's or, for noalloc, this
+// device's scratch array (checked against its size before any HIP call).
+static m3_status scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspace, size_t ws_bytes,
+                          void *stream, bool noalloc) {
     m3_status st = check_shape(shape);
     if (st != M3_OK) return st;
     if (!io) return M3_ERR_INVALID_ARG;
@@ -165,9 +213,21 @@ m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspa
     st = make_plan(s, &p);
     if (st != M3_OK) return st;
     if (fused && p.kernel != 1) return M3_ERR_UNSUPPORTED;  // the fp32 kernel does not take the fused form
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    if (noalloc) {
+        // nothing in the scratch array needs clearing: pass 1 writes every segment
+        // record before the combine reads it, and the combine writes every
+        // incoming state before pass 2 reads it
+        if (p.ws_bytes > kScratchBytes) return M3_ERR_WORKSPACE_TOO_SMALL;
+        workspace = nullptr;
+        ws_bytes = 0;
+        if (p.ws_bytes > 0) {
+            if (scratch_address(hs, &workspace) != hipSuccess) return M3_ERR_HIP;
+            ws_bytes = kScratchBytes;
+        }
+    }
     if (p.ws_bytes > 0 && (workspace == nullptr || ws_bytes < p.ws_bytes)) return M3_ERR_WORKSPACE_TOO_SMALL;
 
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     ScanArgs a{};
     a.b = s.batch; a.L = s.seqlen; a.H = s.nheads; a.G = s.ngroups; a.P = s.headdim; a.N = s.dstate;
     a.R = s.rank; a.C = s.chunk; a.eps = s.eps; a.bf16 = (s.io_dtype == M3_BF16);
@@ -203,6 +263,17 @@ m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspa
     }
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
+
+m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspace, size_t ws_bytes,
+                      void *stream) {
+    return scan_fwd(shape, io, workspace, ws_bytes, stream, false);
+}
+
+m3_status m3_scan_fwd_noalloc(const m3_shape *shape, const m3_scan_io *io, void *stream) {
+    return scan_fwd(shape, io, nullptr, 0, stream, true);
+}
+
+size_t m3_scan_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
 
 // Backward limits: those of the fp32 prefill kernel (the backward keeps every
 // tile of a 32-row chunk in LDS), and N, P multiples of 4 (16-byte row reads).

@@ -81,6 +81,10 @@ def _load():
     lib.m3_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
     lib.m3_decode_step.restype = ctypes.c_int
     lib.m3_decode_step.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(DecodeIO), ctypes.c_void_p]
+    lib.m3_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.m3_scan_fwd_noalloc.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ScanIO), ctypes.c_void_p]
+    lib.m3_scan_noalloc_max_workspace_bytes.restype = ctypes.c_size_t
+    lib.m3_scan_noalloc_max_workspace_bytes.argtypes = []
     lib.m3_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.m3_scan_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
     lib.m3_scan_plan.restype = ctypes.c_int
@@ -275,6 +279,36 @@ def scan_fwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *, chunk=64, eps=
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.m3_scan_fwd(ctypes.byref(shape), ctypes.byref(io), _ptr(workspace), wsb, _stream(stream)))
     return y, h_final
+
+
+def scan_fwd_noalloc(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, y, h_final, *, chunk=64, eps=1e-5,
+                     B_normw=None, C_normw=None, h0=None, x_prev=None, Braw_prev=None, nsegments=0,
+                     force_generic=False, D=None, out_norm=False, out_normw=None, stream=None):
+    """m3_scan_fwd_noalloc: scan_fwd for callers that cannot allocate. The caller
+    passes the outputs y [b,L,H,R,P] (io dtype) and h_final [b,H,P,N] fp32 (or None);
+    the segment split's workspace is the library's per-GPU array. Nothing is
+    allocated here either. Returns (y, h_final)."""
+    b, L, H, R, P = _dims5("x", x, 5)
+    _, _, G, _, N = _dims5("Braw", Braw, 5)
+    _io_dtype(x)
+    _need("y", y)
+    _expect_all(_scan_specs(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, B_normw, C_normw, h0, x_prev,
+                            Braw_prev, b=b, L=L, H=H, G=G, R=R, P=P, N=N, io=x.dtype)
+                + _epilogue_specs(D, out_normw, H, P)
+                + [("y", y, (b, L, H, R, P), x.dtype), ("h_final", h_final, (b, H, P, N), torch.float32)],
+                x.get_device())
+    shape = scan_shape(x, Braw, chunk, eps, force_generic=force_generic, nsegments=nsegments,
+                       out_norm=out_norm)
+    io = ScanIO(_ptr(x), _ptr(Braw), _ptr(Craw), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
+                _ptr(B_bias), _ptr(C_bias), _ptr(B_normw), _ptr(C_normw), _ptr(h0),
+                _ptr(x_prev), _ptr(Braw_prev), _ptr(y), _ptr(h_final))
+    io.D, io.out_normw = _ptr(D), _ptr(out_normw)
+    _check(lib.m3_scan_fwd_noalloc(ctypes.byref(shape), ctypes.byref(io), _stream(stream)))
+    return y, h_final
+
+
+def noalloc_max_workspace_bytes() -> int:
+    return int(lib.m3_scan_noalloc_max_workspace_bytes())
 
 
 def scan_fused_fwd(x_in, z_in, W_X, W_Z, W_O, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, *,

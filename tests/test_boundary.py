@@ -292,3 +292,28 @@ def test_probe_mfma_and_facts_validate(m3):
 
 def m3_status(m3, name):
     return {"INVALID_ARG": -1, "UNSUPPORTED": -2, "MISALIGNED": -3, "WORKSPACE_TOO_SMALL": -4, "HIP": -5}[name]
+
+
+def test_noalloc_rejects_workspace_beyond_its_array(m3):
+    # 256 chains forced into 16 segments each need ~135 MB of workspace, beyond
+    # the allocation-free entry point's fixed 64 MiB: refused before any HIP call
+    shape = _shape(m3, batch=4, nheads=64, seqlen=1024, nsegments=16)
+    p = m3.plan(shape)
+    assert p.workspace_bytes > m3.noalloc_max_workspace_bytes() == 64 << 20
+    io = _fake_io(m3)
+    rc = m3.lib.m3_scan_fwd_noalloc(ctypes.byref(shape), ctypes.byref(io), None)
+    assert rc == -4  # M3_ERR_WORKSPACE_TOO_SMALL
+    # argument errors come first, as in m3_scan_fwd
+    assert m3.lib.m3_scan_fwd_noalloc(ctypes.byref(shape), None, None) == -1
+    bad = _fake_io(m3, misalign="x")
+    assert m3.lib.m3_scan_fwd_noalloc(ctypes.byref(shape), ctypes.byref(bad), None) == -3
+
+
+def test_every_automatic_plan_fits_the_noalloc_array(m3):
+    cap = m3.noalloc_max_workspace_bytes()
+    for b in (1, 2, 3, 4, 8):
+        for H in (1, 2, 4, 8, 16, 24, 32, 48, 64, 96, 128, 191, 255, 383):
+            for L in (4096, 32768, 1 << 20):
+                for R, C in ((1, 64), (2, 32), (4, 16)):
+                    p = m3.plan(_shape(m3, batch=b, nheads=H, seqlen=L, rank=R, chunk=C))
+                    assert p.workspace_bytes <= cap, (b, H, L, R, p.workspace_bytes)
