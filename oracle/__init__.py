@@ -33,10 +33,14 @@ def build(force: bool = False) -> str:
 
 
 def _load():
+    """The compiled oracle. M3_ORACLE_LIB names another build of the same source to
+    load instead (the sanitizer test runs the pins against an ASan/UBSan build)."""
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("M3_ORACLE_LIB")
+        if not path:
+            path = build()
+        lib = ctypes.CDLL(path)
         f = lib.m3o_scan
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.c_long] * 7 + [ctypes.c_double] + [ctypes.c_void_p] * 16 + [ctypes.c_int]
