@@ -58,7 +58,18 @@ constexpr int kCUs = 256;  // MI355X compute units: 2 resident workgroups each
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kInv2Pi = 0.15915494309189535f;
 
-enum Mode { kFull = 0, kPass1 = 1, kPass2 = 2 };
+// kFull: one pass over the whole sequence. Segment split (state passing):
+//   kPass1 + combine + kPass2: end states only, then every segment again from its
+//     incoming state (used with the output norm, which is not linear in y);
+//   kLocal + combine + kCorrect: every segment's outputs and end state from a
+//     zero state, then the outputs corrected for the incoming state. The
+//     recurrence is linear in its initial state: a token's output gains
+//     e^{cs_t} C_bar_t^T H_in, with cs_t the decay from the segment start, and
+//     nothing else. The correction pass rotates only C, has no input term and
+//     stops once the decay since the segment start falls below e^kCorrectStop,
+//     where the term is far below the output's rounding.
+enum Mode { kFull = 0, kPass1 = 1, kPass2 = 2, kLocal = 3, kCorrect = 4 };
+constexpr float kCorrectStop = -80.f;
 
 // A value the compiler cannot see through: lane-derived indices computed from it
 // inside the chunk loop are recomputed each iteration instead of being hoisted
@@ -249,7 +260,7 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
     const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + offBC);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        cr.rb[ks] = pb[4 * ks];
+        if constexpr (MODE != kCorrect) cr.rb[ks] = pb[4 * ks];
         if constexpr (MODE != kPass1) cr.rc[ks] = pc[4 * ks];
     }
     // angle slot block b (4 channels) of lane group lg starts at channel
@@ -261,9 +272,11 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
         const int b = (4 / R) * ln.r_row + q;
         cr.th[q] = pt[8 * (b >> 1) + 2 * ln.lg + (b & 1)];
     }
-    const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + offx);
-    cr.xf[0] = px[ln.lg];
-    cr.xf[1] = px[4 + ln.lg];
+    if constexpr (MODE != kCorrect) {
+        const bf16x8 *px = reinterpret_cast<const bf16x8 *>(cb.x + offx);
+        cr.xf[0] = px[ln.lg];
+        cr.xf[1] = px[4 + ln.lg];
+    }
     if constexpr (FUSED && MODE != kPass1) {
         // columns p = 16pb + 4lg..+3 of the output rows this lane holds
         const bf16x4 *pz = reinterpret_cast<const bf16x4 *>(cb.z + offx + 4 * ln.lg);
@@ -356,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
     }
     // skip term D x: added to the diagonal of the masked scores (P[t][t] += D), so
     // the X^T P^T product carries it
-    const float dsk = (MODE != kPass1 && a.D) ? a.D[hi] : 0.f;
+    const float dsk = (MODE != kPass1 && MODE != kCorrect && a.D) ? a.D[hi] : 0.f;
     if constexpr (FUSED) {
         // global W is [H][P][R]: e runs over (p, r) of this head, rank fastest
         for (int e = tid; e < 3 * R * kP; e += kThreads) {
@@ -373,7 +386,11 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) acc[q][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if constexpr (MODE == kFull || MODE == kPass2) {
+    if constexpr (MODE == kCorrect) {
+        // segment 0 has nothing to correct without an initial state or previous token
+        if (pos.seg == 0 && !a.h0 && !a.has_prev) return;
+    }
+    if constexpr (MODE == kFull || MODE == kPass2 || MODE == kCorrect) {
         const float *src = nullptr;
         if (MODE == kFull)
             src = a.h0 ? a.h0 + chain * (kP * kN) : nullptr;
@@ -497,12 +514,16 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         }
 #pragma unroll
         for (int k = 0; k < 4 / R; ++k) th[k] = cr.th[k];
-        xf[0] = cr.xf[0];
-        xf[1] = cr.xf[1];
+        if constexpr (MODE != kCorrect) {
+            xf[0] = cr.xf[0];
+            xf[1] = cr.xf[1];
+        }
         bf16x4 zf[4];
         if constexpr (FUSED) {
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) zf[pb] = cr.zf[pb];
+        }
+        if constexpr (FUSED && MODE != kCorrect) {
             // rank expansion X = W_X (.) X' for this lane's rank (App. C), rounded
             // to bf16 like any other matrix-core operand
 #pragma unroll
@@ -554,8 +575,10 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bf16x2 vb = {rb[ks][2 * j], rb[ks][2 * j + 1]};
-                ssb = __builtin_amdgcn_fdot2_f32_bf16(vb, vb, ssb, false);
+                if constexpr (MODE != kCorrect) {
+                    const bf16x2 vb = {rb[ks][2 * j], rb[ks][2 * j + 1]};
+                    ssb = __builtin_amdgcn_fdot2_f32_bf16(vb, vb, ssb, false);
+                }
                 if constexpr (MODE != kPass1) {
                     const bf16x2 vc = {rc[ks][2 * j], rc[ks][2 * j + 1]};
                     ssc = __builtin_amdgcn_fdot2_f32_bf16(vc, vc, ssc, false);
@@ -595,11 +618,13 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         // bf16 operands; the output lane holds rows 16w + 4lg..+3 of column lr.
         // Written after B1, which every wave passes only once its state update of
         // the previous chunk (a reader of every column of X^T) is done.
+        if constexpr (MODE != kCorrect) {
 #pragma unroll
-        for (int pb = 0; pb < 4; ++pb) {
-            const f32x4 t = mfma(xf[pb >> 1], (pb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f});
-            const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
-            *reinterpret_cast<bf16x4 *>(&sm.Xt[(16 * pb + lr) * kLdR + 16 * w + 4 * lg]) = v;
+            for (int pb = 0; pb < 4; ++pb) {
+                const f32x4 t = mfma(xf[pb >> 1], (pb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f});
+                const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
+                *reinterpret_cast<bf16x4 *>(&sm.Xt[(16 * pb + lr) * kLdR + 16 * w + 4 * lg]) = v;
+            }
         }
 
         // ---- rotate into the frame of the workgroup's first token: add the carry
@@ -676,14 +701,16 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     const int j = 4 * jh + jj;
                     float sn, cn;
                     slot_sc(8 * ks2 + j, sn, cn);
-                    const float bl = (float)rb[ks2][j] * (HAS_W ? abl[jj] : rsb) + blo[jj];
-                    const float bh = (float)rb[ks2 + 2][j] * (HAS_W ? abh[jj] : rsb) + bhi[jj];
-                    // rows past the end of the sequence need no zeroing: their
-                    // weights w, gamma and cst are 0 and their outputs are not stored
-                    const float bbl = cn * bl + sn * bh;
-                    const float bbh = cn * bh - sn * bl;
-                    bfr[ks2][j] = (__bf16)bbl;
-                    bfr[ks2 + 2][j] = (__bf16)bbh;
+                    if constexpr (MODE != kCorrect) {
+                        const float bl = (float)rb[ks2][j] * (HAS_W ? abl[jj] : rsb) + blo[jj];
+                        const float bh = (float)rb[ks2 + 2][j] * (HAS_W ? abh[jj] : rsb) + bhi[jj];
+                        // rows past the end of the sequence need no zeroing: their
+                        // weights w, gamma and cst are 0 and their outputs are not stored
+                        const float bbl = cn * bl + sn * bh;
+                        const float bbh = cn * bh - sn * bl;
+                        bfr[ks2][j] = (__bf16)bbl;
+                        bfr[ks2 + 2][j] = (__bf16)bbh;
+                    }
                     if constexpr (MODE != kPass1) {
                         const float cl = (float)rc[ks2][j] * (HAS_W ? acl[jj] : rsc) + clo[jj];
                         const float ch = (float)rc[ks2 + 2][j] * (HAS_W ? ach[jj] : rsc) + chi[jj];
@@ -695,14 +722,14 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 }
             }
         }
-        if constexpr (MODE != kPass1) {
+        if constexpr (MODE != kPass1 && MODE != kCorrect) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 *reinterpret_cast<bf16x8 *>(&sm.Bb[row * kLdN + 32 * ks + 8 * lg]) = bfr[ks];
         }
         // ---- B_bar^T scaled by cst through the matrix core; the scale belongs to
         // the output rows 16w + 4lg + j
-        {
+        if constexpr (MODE != kCorrect) {
             const f32x4 cs4 = *reinterpret_cast<const f32x4 *>(&sm.cstt[16 * w + 4 * lg]);
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
@@ -727,6 +754,9 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 
         __builtin_amdgcn_s_setprio(3);
         if constexpr (MODE != kPass1) {
+            // the correction pass has no input term: only the carried-state output
+            bf16x8 pfr[2];
+            if constexpr (MODE != kCorrect) {
             // ---- S^T blocks (s-block sb <= w) for this wave's t-block
             f32x4 sT[4];
 #pragma unroll
@@ -773,7 +803,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     sT[sb] = sT[sb] * mdiag + dadd;
                 }
             }
-            bf16x8 pfr[2];
 #pragma unroll
             for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
@@ -781,6 +810,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     pfr[m2][j] = (__bf16)sT[2 * m2][j];
                     pfr[m2][j + 4] = (__bf16)sT[2 * m2 + 1][j];
                 }
+            }
             // ---- Y^T = (St C_bar^T) diag(exp(cs)) + X^T P^T ; lane: column t = row, rows p
             const float eo = sm.eoff[row];
             auto y_block = [&](int pb) -> f32x4 {
@@ -792,6 +822,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     yv = mfma(sv, cfr[ks], yv);
                 }
                 yv *= eo;
+                if constexpr (MODE == kCorrect) return yv;
 #pragma unroll
                 for (int m2 = 0; m2 < 2; ++m2) {
                     if (2 * m2 <= w) {
@@ -823,8 +854,14 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             };
             __bf16 *const orow = FUSED ? cb.y + t_row * (int)H * kP : cb.y + ln.offX;
             auto store_block = [&](int pb, const f32x4 &v) {
-                const bf16x4 o = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                *reinterpret_cast<bf16x4 *>(orow + 16 * pb + 4 * lg) = o;
+                bf16x4 *dst = reinterpret_cast<bf16x4 *>(orow + 16 * pb + 4 * lg);
+                f32x4 t = v;
+                if constexpr (MODE == kCorrect) {  // add to the local pass's output
+                    const bf16x4 old = *dst;
+                    t = f32x4{(float)old[0], (float)old[1], (float)old[2], (float)old[3]} + v;
+                }
+                const bf16x4 o = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
+                *dst = o;
             };
             // the token's rank-0 lane stores the gated output
             const bool writer = valid && (!FUSED || r_row == 0);
@@ -885,7 +922,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb) acc[q][pb] *= dec;
 #pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2) {
+        for (int m2 = 0; m2 < (MODE == kCorrect ? 0 : 2); ++m2) {
             bf16x8 xb[4];
 #pragma unroll
             for (int pb = 0; pb < 4; ++pb)
@@ -911,13 +948,19 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         }
         // carry was last read before B2 of this chunk; the next read is after B1 of the next
         if (w == 0) sm.carry[l] = newcarry;
+        if constexpr (MODE == kCorrect) {
+            // every later output's share of the incoming state is below e^kCorrectStop
+            // (logdecay_total is the same in every wave)
+            if (logdecay_total < kCorrectStop) break;
+        }
     }
     __syncthreads();
 
     // ------------------------------------------------------------- epilogue
+    if constexpr (MODE == kCorrect) return;  // the combine wrote the final state
     const bool last_seg = (MODE == kFull) || (pos.c_end * C >= L);
     float *dst = nullptr;
-    if (MODE == kPass1)
+    if (MODE == kPass1 || MODE == kLocal)
         dst = sp.seg_state + (chain * sp.nseg + pos.seg) * (kP * kN);
     else if (last_seg)
         dst = a.h_final ? a.h_final + chain * (kP * kN) : nullptr;
@@ -943,16 +986,17 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 *reinterpret_cast<f32x4 *>(dst + p * kN + n0) = acc[q][pb];
             }
     }
-    if constexpr (MODE == kPass1) {
+    if constexpr (MODE == kPass1 || MODE == kLocal) {
         if (tid < kHalf) sp.seg_angle[(chain * sp.nseg + pos.seg) * kHalf + tid] = sm.carry[tid];
         if (tid == 0) sp.seg_decay[chain * sp.nseg + pos.seg] = logdecay_total;
     }
 }
 
 // Chain the segment end states: H_in[0] = h0 (+ fold of the previous token);
-// H_in[k+1] = exp(D_k) R(Phi_k) H_in[k] + E_k. Overwrites E_k with H_in[k].
+// H_in[k+1] = exp(D_k) R(Phi_k) H_in[k] + E_k. Overwrites E_k with H_in[k]; with
+// write_final, H_in[nseg] (the state after the last token) goes to h_final.
 template <int R, bool FUSED>
-__global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan sp) {
+__global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan sp, bool write_final) {
     __shared__ float rsp[4];
     const int tid = threadIdx.x;
     const int64_t chain = blockIdx.x;
@@ -1007,6 +1051,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
             hiv[k] = dec * (sn * u + cn * v) + eh;
         }
     }
+    if (write_final && a.h_final) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int p = (tid + kThreads * k) / kHalf;
+            a.h_final[(chain * kP + p) * kN + i] = lo[k];
+            a.h_final[(chain * kP + p) * kN + i + kHalf] = hiv[k];
+        }
+    }
 }
 
 template <int R, bool HAS_W, bool FUSED, bool ONORM>
@@ -1018,11 +1070,26 @@ hipError_t launch_rw(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
         return hipGetLastError();
     }
     const unsigned nblk = (unsigned)(chains * sp.nseg);
-    // pass 1 produces no output, so it takes no output norm
+    if constexpr (!ONORM) {
+        // local outputs and end states, the combine (which also writes the final
+        // state), then the correction of each segment's outputs for its incoming state
+        hipLaunchKernelGGL((scan_mfma_kernel<kLocal, R, HAS_W, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a,
+                           sp);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp, true);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((scan_mfma_kernel<kCorrect, R, HAS_W, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a,
+                           sp);
+        return hipGetLastError();
+    }
+    // the output norm is not linear in y: end states first, then every segment
+    // again from its incoming state. Pass 1 produces no output, so it takes no norm
     hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R, HAS_W, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp);
+    hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp, false);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R, HAS_W, FUSED, ONORM>), dim3(nblk), dim3(kThreads), 0, s, a, sp);

@@ -66,12 +66,17 @@ def test_mfma_agrees_with_fp32_kernel(R, C):
     assert relerr(y1, y0) < TOL_BF16 and relerr(h1, h0) < TOL_BF16
 
 
-@pytest.mark.parametrize("R,C,nseg", [(1, 64, 3), (4, 16, 5), (2, 32, 2)])
-def test_segment_split_matches_single_pass(R, C, nseg):
-    """State passing between segments (two passes + combine) gives the single-pass result."""
+@pytest.mark.parametrize("R,C,nseg,slow,state", [(1, 64, 3, True, True), (4, 16, 5, True, True),
+                                                 (2, 32, 2, True, True), (1, 64, 4, False, False),
+                                                 (4, 16, 6, False, True), (4, 16, 3, True, False)])
+def test_segment_split_matches_single_pass(R, C, nseg, slow, state):
+    """State passing between segments (local pass + combine + correction of each
+    segment's outputs for its incoming state) gives the single-pass result. With
+    fast decay the correction stops after the first chunk or two of a segment;
+    with slow decay it runs through every segment."""
     shape = Shape(2, 700, 2, 1, 64, 128, R, C, "bf16")
     assert plan_of(shape, nsegments=nseg).nsegments == nseg
-    inp = make_scan_inputs(shape, seed=23, slow_decay=True, with_h0=True, with_prev=True)
+    inp = make_scan_inputs(shape, seed=23, slow_decay=slow, with_h0=state, with_prev=state)
     y1, h1 = gpu_scan(inp, shape, nsegments=1)
     ys, hs = gpu_scan(inp, shape, nsegments=nseg)
     yr, hr = oracle.scan(inp, shape)
