@@ -530,7 +530,33 @@ def main():
                "hbm_frac": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bb}
         log(nm + "_fused", ent)
         extra[nm + "_fused"] = ent
-        del df, of, hf2
+        # the same output without the fusion: rank expansion, the core, gate and
+        # rank contraction as three launches (X and y round-trip through HBM)
+        xe = torch.empty((sf.batch, sf.seqlen, sf.nheads, sf.rank, sf.headdim), dtype=df["x_in"].dtype, device=dev)
+        ye = torch.empty_like(xe)
+        core = (df["Braw"], df["Craw"], df["dt"], df["A"], df["lam"], df["theta"], df["B_bias"], df["C_bias"])
+
+        def unfused():
+            m3.expand_ranks(df["x_in"], df["W_X"], x_out=xe)
+            m3.scan_fwd(xe, *core, chunk=sf.chunk, eps=sf.eps, y=ye, h_final=hf2)
+            m3.gate_contract(ye, df["z_in"], df["W_Z"], df["W_O"], o=of)
+
+        for _ in range(10):
+            unfused()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(31)]
+        evs[0].record()
+        for k in range(30):
+            unfused()
+            evs[k + 1].record()
+        torch.cuda.synchronize()
+        ms_u = sum(evs[k].elapsed_time(evs[k + 1]) for k in range(30)) / 30
+        ent_u = {"ms": round(ms_u, 4), "tokens_per_s": round(sf.batch * sf.seqlen / (ms_u * 1e-3), 1),
+                 "fused_speedup": round(ms_u / ent["ms"], 3),
+                 "steps": "m3_expand_ranks + m3_scan_fwd + m3_gate_contract"}
+        log(nm + "_unfused_pipeline", ent_u)
+        extra[nm + "_unfused_pipeline"] = ent_u
+        del df, of, hf2, xe, ye
         torch.cuda.empty_cache()
         for nm, bf16_state in (("decode_mimo4_n128", False), ("decode_mimo4_n128", True)):
             sd = WORKLOADS[nm]
@@ -559,7 +585,33 @@ def main():
             key = nm + "_fused" + ("_bf16state" if bf16_state else "")
             log(key, ent)
             extra[key] = ent
-            del de, states
+            # the same step unfused: expansion, the plain decode step, gate
+            xe = torch.empty((sd.batch, sd.nheads, sd.rank, sd.headdim), dtype=de["x_in"].dtype, device=dev)
+            xpe = torch.empty_like(xe)
+            ye = torch.empty_like(xe)
+            dcore = (de["Braw"], de["Craw"], de["dt"], de["A"], de["lam"], de["theta"], de["B_bias"], de["C_bias"])
+
+            def unfused(st):
+                m3.expand_ranks(de["x_in"], de["W_X"], x_out=xe)
+                m3.expand_ranks(de["x_prev_in"], de["W_X"], x_out=xpe)
+                m3.decode_step(xe, *dcore, st, x_prev=xpe, Braw_prev=de["Braw_prev"], y=ye)
+                m3.gate_contract(ye, de["z_in"], de["W_Z"], de["W_O"], o=od)
+
+            for k in range(8):
+                unfused(states[k % 4])
+            torch.cuda.synchronize()
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            evs[0].record()
+            for k in range(reps):
+                unfused(states[k % 4])
+                evs[k + 1].record()
+            torch.cuda.synchronize()
+            tu = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(reps))[reps // 2]
+            ent_u = {"us_per_step": round(1e3 * tu, 2), "fused_speedup": round(tu / med, 3),
+                     "steps": "2 x m3_expand_ranks + m3_decode_step + m3_gate_contract"}
+            log(key.replace("_fused", "_unfused_pipeline"), ent_u)
+            extra[key.replace("_fused", "_unfused_pipeline")] = ent_u
+            del de, states, xe, xpe, ye
             torch.cuda.empty_cache()
 
         # ---- prefill backward (training): SISO and MIMO rank-4, b8 L4096

@@ -256,6 +256,24 @@ m3_status m3_scan_bwd(const m3_shape *shape, const m3_scan_io *io, const m3_scan
 /* Bytes of device workspace m3_scan_bwd needs for this shape. */
 size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape);
 
+/* The MIMO projections of App. C as stand-alone steps, for callers that run the
+ * core without the fused form (and the unfused baseline of the fused path). Both
+ * use shape->batch, seqlen (1 for a decode token), nheads, headdim P (a multiple
+ * of 8), rank R (<= 4) and io_dtype; rows are the batch * seqlen * nheads (token,
+ * head) pairs. Weights are [H,P,R] fp32. Pointers 16-byte aligned; nothing is
+ * allocated; M3_ERR_UNSUPPORTED for P % 8 != 0, P > 2048 or R > 4, or more than
+ * 65535 heads.
+ *
+ * m3_expand_ranks: the rank expansion X = W_X (.) X' of App. C,
+ *   x_out[b,L,H,R,P][r][p] = W_X[h][p][r] * x_in[b,L,H,P][p]            (io dtype) */
+m3_status m3_expand_ranks(const m3_shape *shape, const void *x_in, const float *W_X, void *x_out, void *stream);
+
+/* m3_gate_contract: App. C's gate and rank contraction after the core,
+ *   o[b,L,H,P][p] = sum_r W_O[h][p][r] * y[b,L,H,R,P][r][p] * SiLU(W_Z[h][p][r] * z_in[b,L,H,P][p])
+ * with SiLU(v) = v / (1 + e^-v); y, z_in, o in the io dtype, accumulated in fp32. */
+m3_status m3_gate_contract(const m3_shape *shape, const void *y, const void *z_in, const float *W_Z,
+                           const float *W_O, void *o, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *m3_status_str(m3_status status);
 

@@ -92,6 +92,10 @@ def _load():
     lib.m3_status_str.restype = ctypes.c_char_p
     lib.m3_status_str.argtypes = [ctypes.c_int]
     lib.m3_version.restype = ctypes.c_int
+    lib.m3_expand_ranks.restype = ctypes.c_int
+    lib.m3_expand_ranks.argtypes = [ctypes.POINTER(Shape)] + [ctypes.c_void_p] * 4
+    lib.m3_gate_contract.restype = ctypes.c_int
+    lib.m3_gate_contract.argtypes = [ctypes.POINTER(Shape)] + [ctypes.c_void_p] * 6
     lib.m3_probe_copy.restype = ctypes.c_int
     lib.m3_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     lib.m3_probe_mfma_bf16.restype = ctypes.c_int
@@ -477,6 +481,46 @@ def to_device(inp: dict, io: str, device="cuda"):
             t = t.to(torch.bfloat16)
         out[k] = t.contiguous()
     return out
+
+
+# -------------------------------------------- unfused projections (App. C) ---
+def expand_ranks(x_in, W_X, x_out=None, stream=None):
+    """m3_expand_ranks: x_in [..., H, P] (io dtype), W_X [H, P, R] fp32 ->
+    x_out [..., H, R, P] with x_out[..., h, r, p] = W_X[h, p, r] * x_in[..., h, p]."""
+    H, P = x_in.shape[-2], x_in.shape[-1]
+    R = _dims5("W_X", W_X, 3)[2]
+    iot = _io_dtype(x_in)
+    lead = tuple(x_in.shape[:-2])
+    _expect_all([("W_X", W_X, (H, P, R), torch.float32),
+                 ("x_out", x_out, lead + (H, R, P), x_in.dtype)], x_in.get_device())
+    if x_out is None:
+        x_out = torch.empty(lead + (H, R, P), dtype=x_in.dtype, device=x_in.device)
+    rows = 1
+    for v in lead:
+        rows *= int(v)
+    shape = make_shape(rows, 1, H, 1, P, 2, R, 1, iot)
+    _check(lib.m3_expand_ranks(ctypes.byref(shape), _ptr(x_in), _ptr(W_X), _ptr(x_out), _stream(stream)))
+    return x_out
+
+
+def gate_contract(y, z_in, W_Z, W_O, o=None, stream=None):
+    """m3_gate_contract: y [..., H, R, P], z_in [..., H, P] (io dtype), W_Z, W_O [H, P, R]
+    fp32 -> o [..., H, P] = sum_r W_O * y * SiLU(W_Z * z_in)."""
+    H, R, P = y.shape[-3], y.shape[-2], y.shape[-1]
+    iot = _io_dtype(y)
+    lead = tuple(y.shape[:-3])
+    _expect_all([("z_in", z_in, lead + (H, P), y.dtype), ("W_Z", W_Z, (H, P, R), torch.float32),
+                 ("W_O", W_O, (H, P, R), torch.float32), ("o", o, lead + (H, P), y.dtype)], y.get_device())
+    _need("z_in", z_in)
+    if o is None:
+        o = torch.empty(lead + (H, P), dtype=y.dtype, device=y.device)
+    rows = 1
+    for v in lead:
+        rows *= int(v)
+    shape = make_shape(rows, 1, H, 1, P, 2, R, 1, iot)
+    _check(lib.m3_gate_contract(ctypes.byref(shape), _ptr(y), _ptr(z_in), _ptr(W_Z), _ptr(W_O), _ptr(o),
+                                _stream(stream)))
+    return o
 
 
 # ------------------------------------------------------ calibration probes ---

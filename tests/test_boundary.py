@@ -317,3 +317,18 @@ def test_every_automatic_plan_fits_the_noalloc_array(m3):
                 for R, C in ((1, 64), (2, 32), (4, 16)):
                     p = m3.plan(_shape(m3, batch=b, nheads=H, seqlen=L, rank=R, chunk=C))
                     assert p.workspace_bytes <= cap, (b, H, L, R, p.workspace_bytes)
+
+
+def test_projection_steps_validate_before_any_hip_call(m3):
+    ok = _shape(m3, batch=2, seqlen=3, nheads=4, headdim=64, rank=4)
+    f = m3.lib.m3_expand_ranks
+    g = m3.lib.m3_gate_contract
+    assert f(ctypes.byref(ok), None, 0x1000, 0x2000, None) == -1                   # missing input
+    assert f(ctypes.byref(ok), 0x1004, 0x1000, 0x2000, None) == -3                 # misaligned
+    assert f(ctypes.byref(_shape(m3, headdim=60)), 0x1000, 0x2000, 0x3000, None) == -2  # P % 8
+    assert f(ctypes.byref(_shape(m3, rank=5)), 0x1000, 0x2000, 0x3000, None) == -2
+    assert g(ctypes.byref(ok), 0x1000, None, 0x2000, 0x3000, 0x4000, None) == -1
+    assert g(ctypes.byref(ok), 0x1000, 0x2000, 0x3000, 0x4008, 0x5000, None) == -3
+    assert g(None, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None) == -1
+    empty = _shape(m3, batch=0)
+    assert f(ctypes.byref(empty), None, None, None, None) == 0
