@@ -566,10 +566,11 @@ def main():
             od = torch.empty_like(de["x_in"])
             base = (de["x_in"], de["z_in"], de["W_X"], de["W_Z"], de["W_O"], de["Braw"], de["Craw"], de["dt"],
                     de["A"], de["lam"], de["theta"], de["B_bias"], de["C_bias"])
-            for k in range(8):
+            # the same protocol as the plain decode: 40 untimed steps, then the median of 200
+            for k in range(40):
                 m3.decode_fused_step(*base, states[k % 4], x_prev_in=de["x_prev_in"], Braw_prev=de["Braw_prev"], o=od)
             torch.cuda.synchronize()
-            reps = 40
+            reps = 200
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
             evs[0].record()
             for k in range(reps):
@@ -597,7 +598,7 @@ def main():
                 m3.decode_step(xe, *dcore, st, x_prev=xpe, Braw_prev=de["Braw_prev"], y=ye)
                 m3.gate_contract(ye, de["z_in"], de["W_Z"], de["W_O"], o=od)
 
-            for k in range(8):
+            for k in range(40):
                 unfused(states[k % 4])
             torch.cuda.synchronize()
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
