@@ -10,21 +10,31 @@
 namespace m3i {
 namespace {
 
+// grid-stride element loops over n floats, with a grid of at most kFillBlocks
+constexpr int64_t kFillBlocks = 65536;
+
+unsigned fill_grid(int64_t n) {
+    const int64_t g = (n + 255) / 256;
+    return (unsigned)(g < kFillBlocks ? g : kFillBlocks);
+}
+
 __global__ void state_copy_kernel(const float *h0, float *hf, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) hf[i] = h0 ? h0[i] : 0.f;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        hf[i] = h0 ? h0[i] : 0.f;
 }
 
 bool aligned16(const void *p) { return p == nullptr || (((uintptr_t)p) & 15u) == 0; }
 
+constexpr int64_t kMaxGrid = 0x7fffffff;  // workgroups of one launch
+
 __global__ void fill_zero_kernel(float *p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0.f;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.f;
 }
 
 hipError_t zero(float *p, int64_t n, hipStream_t s) {
     if (!p || n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(fill_grid(n)), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 
@@ -59,6 +69,11 @@ m3_status check_shape(const m3_shape *s) {
     // (the bf16-state flag is decode only)
     if (s->flags & ~(M3_FLAG_FORCE_GENERIC | M3_FLAG_OUT_NORM | M3_FLAG_NORM_AFTER_GATE)) return M3_ERR_INVALID_ARG;
     if (s->batch > (1LL << 31) || s->nheads > (1LL << 20) || s->seqlen > (1LL << 40)) return M3_ERR_UNSUPPORTED;
+    // every launch takes at most one workgroup per (batch, head) chain and segment,
+    // and the grid is a 32-bit count; tokens and elements stay far below 64-bit overflow
+    if (s->batch * s->nheads > kMaxGrid || (s->seqlen > 0 && s->batch > (1LL << 40) / s->seqlen) ||
+        s->headdim > (1 << 16) || s->dstate > (1 << 16) || s->rank > (1 << 10))
+        return M3_ERR_UNSUPPORTED;
     return M3_OK;
 }
 
@@ -76,6 +91,7 @@ m3_status make_plan(const m3_shape &s, Plan *pl) {
         p.seg_chunks = nseg > 1 ? (nchunks + nseg - 1) / nseg : nchunks;
         if (nseg > 1) p.nseg = (int)((nchunks + p.seg_chunks - 1) / p.seg_chunks);
         p.workgroups = s.batch * s.nheads * p.nseg;
+        if (p.workgroups > kMaxGrid) return M3_ERR_UNSUPPORTED;
         p.ws_bytes = p.nseg > 1 ? mfma_workspace_bytes(s.batch * s.nheads, p.nseg, s.headdim, s.dstate) : 0;
     } else if (generic_applicable(s)) {
         if (s.nsegments > 1) return M3_ERR_UNSUPPORTED;  // the fp32 kernel runs each chain in one pass
@@ -246,7 +262,7 @@ static m3_status scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *wor
     if (s.seqlen == 0) {
         if (io->h_final) {
             const int64_t n = s.batch * s.nheads * s.headdim * s.dstate;
-            hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs, io->h0,
+            hipLaunchKernelGGL(state_copy_kernel, dim3(fill_grid(n)), dim3(256), 0, hs, io->h0,
                                io->h_final, n);
             e = hipGetLastError();
         }
@@ -278,8 +294,10 @@ size_t m3_scan_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
 // Backward limits: those of the fp32 prefill kernel (the backward keeps every
 // tile of a 32-row chunk in LDS), and N, P multiples of 4 (16-byte row reads).
 static bool bwd_shape_ok(const m3_shape &s) {
+    // the group reduction runs one wave per raw B/C row, four to a workgroup
     return s.dstate <= kGenericMaxN && s.headdim <= kGenericMaxP && s.dstate * s.headdim <= kGenericMaxNP &&
-           s.rank <= 4 && s.dstate % 4 == 0 && s.headdim % 4 == 0;
+           s.rank <= 4 && s.dstate % 4 == 0 && s.headdim % 4 == 0 &&
+           s.batch * s.seqlen * s.ngroups * s.rank / 4 < kMaxGrid;
 }
 
 static ScanArgs bwd_args(const m3_shape &s, const m3_scan_io *io) {
@@ -341,7 +359,7 @@ m3_status m3_scan_bwd(const m3_shape *shape, const m3_scan_io *io, const m3_scan
             (e = zero(gr->dBraw_prev, s.batch * s.ngroups * s.rank * s.dstate, hs)) != hipSuccess)
             return M3_ERR_HIP;
         if (gr->dh0 && nst > 0) {
-            hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, hs, gr->dh_final,
+            hipLaunchKernelGGL(state_copy_kernel, dim3(fill_grid(nst)), dim3(256), 0, hs, gr->dh_final,
                                gr->dh0, nst);
             if (hipGetLastError() != hipSuccess) return M3_ERR_HIP;
         }
@@ -370,7 +388,7 @@ m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *st
     if ((io->x_prev == nullptr) != (io->Braw_prev == nullptr)) return M3_ERR_INVALID_ARG;
     const int64_t N = s.dstate;
     if (!(N == 16 || N == 32 || N == 64 || N == 128 || N == 256) || s.headdim > kDecodeMaxP ||
-        s.rank > kDecodeMaxR || s.batch > (1LL << 31))
+        s.rank > kDecodeMaxR || s.batch > (1LL << 31) || s.nheads > (1LL << 20) || s.batch * s.nheads > kMaxGrid)
         return M3_ERR_UNSUPPORTED;
     const bool fused = io->W_X != nullptr;
     if (fused && (!io->W_Z || !io->W_O)) return M3_ERR_INVALID_ARG;

@@ -179,6 +179,7 @@ m3_status proj_check(const m3_shape *s, int64_t *rows) {
     if (s->io_dtype != M3_F32 && s->io_dtype != M3_BF16) return M3_ERR_INVALID_ARG;
     if (s->headdim % kVec != 0 || s->headdim > kVec * kThreads || s->rank > 4) return M3_ERR_UNSUPPORTED;
     if (s->batch > (1LL << 31) || s->seqlen > (1LL << 40) || s->nheads > 65535) return M3_ERR_UNSUPPORTED;
+    if (s->seqlen > 0 && s->batch > (1LL << 40) / s->seqlen) return M3_ERR_UNSUPPORTED;
     *rows = s->batch * s->seqlen;  // tokens; the heads are the grid's y
     return M3_OK;
 }

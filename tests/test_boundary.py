@@ -332,3 +332,24 @@ def test_projection_steps_validate_before_any_hip_call(m3):
     assert g(None, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None) == -1
     empty = _shape(m3, batch=0)
     assert f(ctypes.byref(empty), None, None, None, None) == 0
+
+
+def test_shapes_beyond_one_launch_grid_are_refused(m3):
+    # b * H chains beyond a 32-bit grid: refused on the host, never launched truncated
+    big = _shape(m3, batch=1 << 31, nheads=4)
+    assert m3.lib.m3_scan_fwd(ctypes.byref(big), ctypes.byref(_fake_io(m3)), None, 0, None) == -2
+    assert m3.lib.m3_scan_workspace_bytes(ctypes.byref(big)) == 0
+    io = m3.DecodeIO()
+    for i, (name, _) in enumerate(m3.DecodeIO._fields_):
+        if name in ("x", "Braw", "Craw", "dt", "A", "lam", "theta", "B_bias", "C_bias", "h", "y"):
+            setattr(io, name, 0x100000 + 0x1000 * (i + 1))
+    dec = _shape(m3, batch=1 << 30, nheads=8, seqlen=1, chunk=1)
+    assert m3.lib.m3_decode_step(ctypes.byref(dec), ctypes.byref(io), None) == -2
+    # a forced split whose workgroups overflow the grid
+    split = _shape(m3, batch=1 << 20, nheads=1024, seqlen=64 * 8, nsegments=8)
+    assert m3.lib.m3_scan_fwd(ctypes.byref(split), ctypes.byref(_fake_io(m3)), None, 0, None) == -2
+    # tokens beyond 2^40
+    toks = _shape(m3, batch=1 << 20, seqlen=1 << 21)
+    assert m3.lib.m3_scan_fwd(ctypes.byref(toks), ctypes.byref(_fake_io(m3)), None, 0, None) == -2
+    assert m3.lib.m3_expand_ranks(ctypes.byref(_shape(m3, batch=1 << 20, seqlen=1 << 21, rank=4)), 0x1000, 0x2000,
+                                  0x3000, None) == -2
