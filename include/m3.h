@@ -203,20 +203,25 @@ typedef struct {
  * Chunked algorithm of §3.3 (quadratic masked form inside a chunk, §3.1.3 eq. 7
  * mask; linear state passing between chunks) on B and C rotated by the
  * cumulative angle (§3.2.2, Proposition 4). Returns M3_OK or a negative status.
- * workspace may be NULL when m3_scan_workspace_bytes returns 0. */
+ * workspace may be NULL when m3_scan_workspace_bytes returns 0. The bf16
+ * matrix-core path always takes one: B and C after BCNorm and its gain, computed
+ * once per (token, group, rank) row rather than once per head (2 * b*L*G*R * N/2
+ * f16 pairs, 4 * b*L*G*R*N bytes), then, when the sequence is split, the segment
+ * records. Its contents need not be initialised and are not kept. */
 m3_status m3_scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *workspace,
                       size_t ws_bytes, void *stream);
 
 /* m3_scan_fwd for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
- * arguments, kernels and results as m3_scan_fwd, but the segment split's
- * workspace is a device array inside the library, fixed at
- * m3_scan_noalloc_max_workspace_bytes() (64 MiB) per GPU, held by each GPU the
- * library runs on until the process ends; every automatic plan fits (the largest
- * needs about 34 MB). The call allocates and frees nothing. On its first use on a
- * device it looks up that device's copy of the array (a host-side query, no
- * allocation). A plan whose workspace exceeds the maximum (only reachable by
- * forcing shape->nsegments) returns M3_ERR_WORKSPACE_TOO_SMALL before any HIP call.
+ * arguments, kernels and results as m3_scan_fwd, but the workspace is a device
+ * array inside the library, fixed at m3_scan_noalloc_max_workspace_bytes()
+ * (256 MiB) per GPU, held by each GPU the library runs on until the process
+ * ends. Every automatic plan with at most 2^18 raw B rows (b*L*G*R) fits: the
+ * normalised rows take 128 MiB there and the segment records at most ~36 MB.
+ * The call allocates and frees nothing. On its first use on a device it looks up
+ * that device's copy of the array (a host-side query, no allocation). A plan
+ * whose workspace exceeds the maximum returns M3_ERR_WORKSPACE_TOO_SMALL before
+ * any HIP call; the caller then splits the batch.
  * Calls on one GPU share its array, which keeps the last call's contents; no
  * part of it needs to start at zero. Calls that overlap on one GPU (on different
  * streams, or replayed graphs running concurrently) race on the array: the

@@ -47,7 +47,9 @@ struct Plan {
 };
 
 bool mfma_applicable(const m3_shape &s) {
+    // (a chunk's per-lane element offsets are 32-bit: at most 2^18 heads)
     return s.io_dtype == M3_BF16 && s.dstate == 128 && s.headdim == 64 && s.chunk * s.rank == 64 &&
+           s.nheads <= (1 << 18) &&
            (s.rank == 1 || s.rank == 2 || s.rank == 4) &&
            !(s.flags & M3_FLAG_FORCE_GENERIC) && mfma_kernel_available();
 }
@@ -92,7 +94,9 @@ m3_status make_plan(const m3_shape &s, Plan *pl) {
         if (nseg > 1) p.nseg = (int)((nchunks + p.seg_chunks - 1) / p.seg_chunks);
         p.workgroups = s.batch * s.nheads * p.nseg;
         if (p.workgroups > kMaxGrid) return M3_ERR_UNSUPPORTED;
-        p.ws_bytes = p.nseg > 1 ? mfma_workspace_bytes(s.batch * s.nheads, p.nseg, s.headdim, s.dstate) : 0;
+        const int64_t rows = s.batch * s.seqlen * s.ngroups * s.rank;  // raw B (C) rows
+        if (rows > (1LL << 44)) return M3_ERR_UNSUPPORTED;
+        p.ws_bytes = mfma_workspace_bytes(rows, s.batch * s.nheads, p.nseg, s.headdim, s.dstate);
     } else if (generic_applicable(s)) {
         if (s.nsegments > 1) return M3_ERR_UNSUPPORTED;  // the fp32 kernel runs each chain in one pass
         p.kernel = 0;
@@ -108,11 +112,12 @@ m3_status make_plan(const m3_shape &s, Plan *pl) {
 }
 
 // Device-resident scratch of the allocation-free prefill entry point: the
-// segment split's workspace (segment end states, decays and angles). Each GPU the
-// library runs on holds its own copy until the process ends. Host code never
-// passes the array's name to a kernel: its device address comes from
-// hipGetSymbolAddress, once per device, with that device current.
-constexpr size_t kScratchBytes = size_t(64) << 20;
+// matrix-core path's workspace (normalised B and C rows, and the segment split's
+// end states, decays and angles). Each GPU the library runs on holds its own copy
+// until the process ends. Host code never passes the array's name to a kernel:
+// its device address comes from hipGetSymbolAddress, once per device, with that
+// device current.
+constexpr size_t kScratchBytes = size_t(256) << 20;
 constexpr int kMaxDevices = 64;
 __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
@@ -231,7 +236,8 @@ static m3_status scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *wor
     if (fused && p.kernel != 1) return M3_ERR_UNSUPPORTED;  // the fp32 kernel does not take the fused form
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     if (noalloc) {
-        // nothing in the scratch array needs clearing: pass 1 writes every segment
+        // nothing in the scratch array needs clearing: the BCNorm pass writes every
+        // normalised row before the scan reads it, pass 1 writes every segment
         // record before the combine reads it, and the combine writes every
         // incoming state before pass 2 reads it
         if (p.ws_bytes > kScratchBytes) return M3_ERR_WORKSPACE_TOO_SMALL;
@@ -274,7 +280,8 @@ static m3_status scan_fwd(const m3_shape *shape, const m3_scan_io *io, void *wor
         SplitPlan sp{};
         sp.nseg = p.nseg;
         sp.seg_chunks = p.seg_chunks;
-        if (p.nseg > 1) mfma_workspace_carve(workspace, s.batch * s.nheads, p.nseg, s.headdim, s.dstate, &sp);
+        mfma_workspace_carve(workspace, s.batch * s.seqlen * s.ngroups * s.rank, s.batch * s.nheads, p.nseg,
+                             s.headdim, s.dstate, &a, &sp);
         e = launch_scan_mfma(a, sp, hs);
     }
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;

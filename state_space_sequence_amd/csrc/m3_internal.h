@@ -29,6 +29,9 @@ struct ScanArgs {
     // output epilogue: skip D[h] x, grouped output RMSNorm (gain [H,P] or NULL)
     const float *D, *out_normw;
     bool onorm, norm_after_gate;
+    // matrix-core path: B and C after BCNorm and its gain (scaled by a power of two,
+    // see the prefill), one row of N/2 f16 pairs (n, n + N/2) per (token, group, rank)
+    unsigned *Bq, *Cq;
 };
 
 struct DecodeArgs {
@@ -79,8 +82,10 @@ hipError_t launch_scan_mfma(const ScanArgs &a, const SplitPlan &sp, hipStream_t 
 // matrix-core prefill planning (m3_scan_mfma.hip)
 bool mfma_kernel_available();
 int mfma_auto_segments(int64_t chains, int64_t nchunks);
-size_t mfma_workspace_bytes(int64_t chains, int nseg, int64_t P, int64_t N);
-void mfma_workspace_carve(void *ws, int64_t chains, int nseg, int64_t P, int64_t N, SplitPlan *sp);
+// rows: raw B (or C) rows, b * L * G * R; chains: b * H
+size_t mfma_workspace_bytes(int64_t rows, int64_t chains, int nseg, int64_t P, int64_t N);
+void mfma_workspace_carve(void *ws, int64_t rows, int64_t chains, int nseg, int64_t P, int64_t N, ScanArgs *a,
+                          SplitPlan *sp);
 
 // limits of the individual kernels (checked by the C ABI before launching)
 constexpr int kGenericMaxN = 128;

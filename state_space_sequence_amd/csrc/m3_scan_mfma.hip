@@ -47,6 +47,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kN = 128, kP = 64, kRows = 64, kHalf = 64;
 // LDS row strides (elements): 16 bytes of padding per row puts the 8 rows that
@@ -117,6 +119,51 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// Rotation of f16 pairs v = (lo, hi) by their angles, in fp32 (v_dot2_f32_f16):
+// lo' = cos lo + sin hi = dot(v, (cos, sin)), hi' = cos hi - sin lo =
+// dot(v, (-sin, cos)); cs = (cos, sin) and sc = (-sin, cos) of each pair's angle.
+// Written out because the compiler's form of the builtin accumulates into its
+// destination and needs a zeroing move per product. A vector instruction that
+// reads a dot product's result needs 3 wait states after it, which the compiler
+// inserts only for dot instructions it emitted itself: each block ends with
+// s_nop 2, and its outputs are early-clobber (written while inputs are still read).
+__device__ __forceinline__ void rot_pairs2(h2 v0, h2 v1, h2 cs0, h2 sc0, h2 cs1, h2 sc1, float &l0, float &h0,
+                                           float &l1, float &h1) {
+    asm("v_dot2_f32_f16 %0, %4, %6, 0\n\t"
+        "v_dot2_f32_f16 %1, %4, %7, 0\n\t"
+        "v_dot2_f32_f16 %2, %5, %8, 0\n\t"
+        "v_dot2_f32_f16 %3, %5, %9, 0\n\t"
+        "s_nop 2"
+        : "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
+        : "v"(v0), "v"(v1), "v"(cs0), "v"(sc0), "v"(cs1), "v"(sc1));
+}
+// two rows (B and C) sharing the angles of two slots
+__device__ __forceinline__ void rot_pairs4(h2 b0, h2 b1, h2 c0, h2 c1, h2 cs0, h2 sc0, h2 cs1, h2 sc1, float *ob,
+                                           float *oc) {
+    asm("v_dot2_f32_f16 %0, %8, %12, 0\n\t"
+        "v_dot2_f32_f16 %1, %8, %13, 0\n\t"
+        "v_dot2_f32_f16 %2, %9, %14, 0\n\t"
+        "v_dot2_f32_f16 %3, %9, %15, 0\n\t"
+        "v_dot2_f32_f16 %4, %10, %12, 0\n\t"
+        "v_dot2_f32_f16 %5, %10, %13, 0\n\t"
+        "v_dot2_f32_f16 %6, %11, %14, 0\n\t"
+        "v_dot2_f32_f16 %7, %11, %15, 0\n\t"
+        "s_nop 2"
+        : "=&v"(ob[0]), "=&v"(ob[1]), "=&v"(ob[2]), "=&v"(ob[3]), "=&v"(oc[0]), "=&v"(oc[1]), "=&v"(oc[2]),
+          "=&v"(oc[3])
+        : "v"(b0), "v"(b1), "v"(c0), "v"(c1), "v"(cs0), "v"(sc0), "v"(cs1), "v"(sc1));
+}
+
+// Smallest e with m <= 2^e for finite m > 0 (-126 for m == 0), clamped to
+// [-126, 100]; exact, from the bits.
+__device__ __forceinline__ int exp_ceil(float m) {
+    if (!(m > 0.f)) return -126;
+    const unsigned u = __float_as_uint(m);
+    int e = (int)((u >> 23) & 0xff) - 127;
+    if (u & 0x7fffff) ++e;
+    return e < -126 ? -126 : (e > 100 ? 100 : e);
+}
+
 struct alignas(16) Smem {
     alignas(16) __bf16 Bb[kRows * kLdN];  // B_bar [row][n]
     alignas(16) __bf16 Bt[kN * kLdR];     // B_bar * cst, [n][row]
@@ -134,8 +181,8 @@ struct alignas(16) Smem {
     alignas(16) float angtot[4][kHalf];   // per wave: angle total of its rows (revolutions)
     alignas(16) float carry[kHalf];       // cumulative angle before the current chunk, mod 1 revolution
     alignas(16) float woff[4][kHalf];     // per wave: angle offset of its rows (carry + earlier waves' totals)
-    alignas(16) float bias[2][4][kN];     // B / C bias of this head, per rank
-    alignas(16) float normw[2][kN];       // BCNorm gains (ones when absent)
+    alignas(16) unsigned bq[2][4][kHalf];  // B / C bias of this head per rank, f16 pairs (n, n + 64), scaled
+    alignas(16) float mx[4][4];           // prologue: per-wave maxima of |gain| and |bias|
     alignas(16) float onw[kP];            // output-norm gain of this head (ones when absent)
 };
 
@@ -206,7 +253,8 @@ __device__ __forceinline__ Lane make_lane(int l, int w, int64_t H) {
 // projections x is X' and z is Z' (one row of P per token, no rank axis) and the
 // output goes to o, also one row per token.
 struct ChunkBase {
-    const __bf16 *B, *Cr, *x, *z;
+    const unsigned *qB, *qC;  // normalised B, C rows (f16 pairs)
+    const __bf16 *x, *z;
     const float *th;
     const float *dt, *A, *lam;
     __bf16 *y;
@@ -216,8 +264,8 @@ template <int R, bool FUSED>
 __device__ __forceinline__ ChunkBase chunk_base(const ScanArgs &a, int64_t bi, int64_t hi, int64_t g, int64_t c0) {
     ChunkBase cb;
     const int64_t t0 = bi * a.L + c0;  // first token of the chunk
-    cb.B = static_cast<const __bf16 *>(a.Braw) + (t0 * a.G + g) * R * kN;
-    cb.Cr = static_cast<const __bf16 *>(a.Craw) + (t0 * a.G + g) * R * kN;
+    cb.qB = a.Bq + (t0 * a.G + g) * R * kHalf;
+    cb.qC = a.Cq + (t0 * a.G + g) * R * kHalf;
     cb.th = a.theta + (t0 * a.G + g) * kHalf;
     constexpr int XR = FUSED ? 1 : R;  // x rows per token
     cb.x = static_cast<const __bf16 *>(a.x) + (t0 * a.H + hi) * XR * kP;
@@ -229,11 +277,13 @@ __device__ __forceinline__ ChunkBase chunk_base(const ScanArgs &a, int64_t bi, i
     return cb;
 }
 
-// Global inputs of one chunk for one lane: its row of raw B, C, theta and X (MFMA
-// fragment layout) and, in lanes 0..C-1, the token scalars. Loaded one chunk ahead
-// so the loads are in flight while the previous chunk is computed.
+// Global inputs of one chunk for one lane: its row's normalised B and C pairs
+// (pairs 8lg..8lg+7 and 32+8lg..32+8lg+7), theta and X (MFMA fragment layout).
+// Loaded one chunk ahead so the loads are in flight while the previous chunk is
+// computed.
 struct ChunkRegs {
-    bf16x8 rb[4], rc[4], xf[2];
+    u32x4 qb[4], qc[4];
+    bf16x8 xf[2];
     bf16x4 zf[4];  // fused projections: Z' of the row's token at the lane's output columns
     f32x4 th[4];  // theta of the lane's angle slots: all 4 blocks for R = 1, its own 4 / R blocks otherwise
 };
@@ -252,16 +302,17 @@ __device__ __forceinline__ void load_chunk(const ChunkBase &cb, const Lane &ln, 
     // weights, gamma, state weight and angle increment are all zero, and whose
     // outputs are not stored
     const int tr = ln.t_row < nv ? ln.t_row : nv - 1;
-    int offBC = (tr * (int)G * R + ln.r_row) * kN + 8 * ln.lg;
+    int offBC = (tr * (int)G * R + ln.r_row) * kHalf + 8 * ln.lg;
     int oth = tr * (int)G * kHalf;
     int offx = FUSED ? tr * (int)H * kP : (tr * (int)H * R + ln.r_row) * kP;
     asm volatile("" : "+v"(offBC), "+v"(oth), "+v"(offx));
-    const bf16x8 *pb = reinterpret_cast<const bf16x8 *>(cb.B + offBC);
-    const bf16x8 *pc = reinterpret_cast<const bf16x8 *>(cb.Cr + offBC);
+    const u32x4 *pb = reinterpret_cast<const u32x4 *>(cb.qB + offBC);
+    const u32x4 *pc = reinterpret_cast<const u32x4 *>(cb.qC + offBC);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        if constexpr (MODE != kCorrect) cr.rb[ks] = pb[4 * ks];
-        if constexpr (MODE != kPass1) cr.rc[ks] = pc[4 * ks];
+    for (int k = 0; k < 4; ++k) {
+        const int o = (k >> 1) * 8 + (k & 1);  // pairs 8lg + 4k (k < 2), 32 + 8lg + 4(k - 2)
+        if constexpr (MODE != kCorrect) cr.qb[k] = pb[o];
+        if constexpr (MODE != kPass1) cr.qc[k] = pc[o];
     }
     // angle slot block b (4 channels) of lane group lg starts at channel
     // 32 (b >> 1) + 8 lg + 4 (b & 1), i.e. float4 8 (b >> 1) + 2 lg + (b & 1). The R
@@ -340,7 +391,7 @@ __device__ __forceinline__ float prev_x(const ScanArgs &a, int64_t bi, int64_t h
     }
 }
 
-template <int MODE, int R, bool HAS_W, bool FUSED, bool ONORM>
+template <int MODE, int R, bool FUSED, bool ONORM>
 __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, SplitPlan sp) {
     constexpr int C = kRows / R;  // tokens per chunk
     __shared__ typename std::conditional<FUSED, SmemFused, Smem>::type sm;
@@ -355,13 +406,61 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
     const int l = tid & 63, lr = l & 15, lg = l >> 4;
 
     // ---------------------------------------------------------------- prologue
-    for (int e = tid; e < 2 * R * kN; e += kThreads) {
-        const int which = e / (R * kN), rem = e % (R * kN);
-        sm.bias[which][rem / kN][rem % kN] = (which == 0 ? a.B_bias : a.C_bias)[(hi * R) * kN + rem];
-    }
-    for (int e = tid; e < 2 * kN; e += kThreads) {
-        const float *src = (e < kN) ? a.B_normw : a.C_normw;
-        sm.normw[e / kN][e % kN] = src ? src[e % kN] : 1.f;
+    // Scales of the f16 rotation inputs. The normalised rows hold u g 2^-eg, with
+    // |u| <= sqrt(N) after BCNorm and max |g| <= 2^eg, so they stay below sqrt(N).
+    // This head adds its bias scaled by 2^-k, with k >= eg the least exponent that
+    // keeps |bias| 2^-k <= 2^14: the f16 sums stay finite for any gains and biases.
+    // The rotated B_bar and C_bar are then 2^-kB and 2^-kC times the true ones; the
+    // per-row tables of the chunk loop carry the inverse powers of two (exact).
+    h2 rrB, rrC;  // 2^(eg - k) per matrix: the factor of the normalised rows
+    float sB, sC, sBC;
+    {
+        float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+        if (tid < kN) {
+            m0 = a.B_normw ? fabsf(a.B_normw[tid]) : 1.f;
+            m1 = a.C_normw ? fabsf(a.C_normw[tid]) : 1.f;
+        }
+        for (int e = tid; e < R * kN; e += kThreads) {
+            m2 = fmaxf(m2, fabsf(a.B_bias[hi * R * kN + e]));
+            m3 = fmaxf(m3, fabsf(a.C_bias[hi * R * kN + e]));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            m0 = fmaxf(m0, __shfl_xor(m0, o));
+            m1 = fmaxf(m1, __shfl_xor(m1, o));
+            m2 = fmaxf(m2, __shfl_xor(m2, o));
+            m3 = fmaxf(m3, __shfl_xor(m3, o));
+        }
+        if (l == 0) {
+            sm.mx[w][0] = m0;
+            sm.mx[w][1] = m1;
+            sm.mx[w][2] = m2;
+            sm.mx[w][3] = m3;
+        }
+        __syncthreads();
+        f32x4 m = *reinterpret_cast<const f32x4 *>(&sm.mx[0][0]);
+#pragma unroll
+        for (int k = 1; k < 4; ++k) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(&sm.mx[k][0]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = fmaxf(m[j], v[j]);
+        }
+        const int egB = max(0, exp_ceil(m[0])), egC = max(0, exp_ceil(m[1]));
+        const int kB = __builtin_amdgcn_readfirstlane(max(egB, exp_ceil(m[2]) - 14));
+        const int kC = __builtin_amdgcn_readfirstlane(max(egC, exp_ceil(m[3]) - 14));
+        const _Float16 fB = (_Float16)ldexpf(1.f, egB - kB), fC = (_Float16)ldexpf(1.f, egC - kC);
+        rrB = h2{fB, fB};
+        rrC = h2{fC, fC};
+        sB = ldexpf(1.f, kB);
+        sC = ldexpf(1.f, kC);
+        sBC = ldexpf(1.f, kB + kC);
+        for (int e = tid; e < 2 * R * kHalf; e += kThreads) {
+            const int which = e / (R * kHalf), r = (e / kHalf) % R, i = e % kHalf;
+            const float *bsrc = (which == 0 ? a.B_bias : a.C_bias) + (hi * R + r) * kN;
+            const int k = which == 0 ? kB : kC;
+            const h2 v = {(_Float16)ldexpf(bsrc[i], -k), (_Float16)ldexpf(bsrc[i + kHalf], -k)};
+            sm.bq[which][r][i] = __builtin_bit_cast(unsigned, v);
+        }
     }
     if (tid < kHalf) sm.carry[tid] = 0.f;
     if constexpr (ONORM) {
@@ -505,12 +604,13 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         const float d = tin ? d0 : 0.f, av = tin ? a0_ : 0.f, lm = tin ? l0 : 0.f;
         const float dn = tnx ? (lastt ? dnl : dsh) : 0.f, lmn = tnx ? (lastt ? lmnl : lsh) : 0.f;
         const float drow = valid ? drw : 0.f;
-        bf16x8 rb[4], rc[4], xf[2];
+        u32x4 qb[4], qc[4];
+        bf16x8 xf[2];
         f32x4 th[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            rb[k] = cr.rb[k];
-            rc[k] = cr.rc[k];
+            qb[k] = cr.qb[k];
+            qc[k] = cr.qc[k];
         }
 #pragma unroll
         for (int k = 0; k < 4 / R; ++k) th[k] = cr.th[k];
@@ -543,16 +643,19 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         const float gm = lm * d;
         const float wt = gm + (1.f - lmn) * dn;
         const float cs_end = lane_value(cs, 63);
-        // per-row tables; the previous chunk's reads of them ended before its last barrier
+        // per-row tables; the previous chunk's reads of them ended before its last barrier.
+        // The mask weights carry 2^(kB + kC), the state-input weights 2^kB and the
+        // carried-state output scale 2^kC: the inverse scales of B_bar and C_bar.
         {
             const float l2c = cs * kLog2e;
+            const float wtm = wt * sBC;
             if (w == 0) {
                 sm.l2cs[l] = l2c;
-                sm.wgt[l] = wt;
-                sm.gam[l] = gm;
-                sm.eoff[l] = __expf(cs);
+                sm.wgt[l] = wtm;
+                sm.gam[l] = gm * sBC;
+                sm.eoff[l] = __expf(cs) * sC;
             } else if (w == 1) {
-                sm.cstt[l] = __expf(cs_end - cs) * wt;
+                sm.cstt[l] = __expf(cs_end - cs) * wt * sB;
                 // factor of row t against the last row of the block before its own
                 const float ref = (l < 32) ? lane_value(l2c, 15) : ((l < 48) ? lane_value(l2c, 31) : lane_value(l2c, 47));
                 sm.ftab[l] = __builtin_amdgcn_exp2f(fminf(l2c - ref, 0.f));
@@ -563,30 +666,11 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     const int wb = (w == 2) ? 1 + k : 3;
                     if (w == 2 || k == 0) {
                         const float ref = lane_value(l2c, 16 * wb - 1);
-                        sm.tw[wb - 1][l] = (l < 16 * wb) ? __builtin_amdgcn_exp2f(fminf(ref - l2c, 0.f)) * wt : 0.f;
+                        sm.tw[wb - 1][l] = (l < 16 * wb) ? __builtin_amdgcn_exp2f(fminf(ref - l2c, 0.f)) * wtm : 0.f;
                     }
                 }
             }
         }
-
-        // ---- BCNorm factors of this row (sum over the 4 lanes that hold it)
-        float ssb = 0.f, ssc = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (MODE != kCorrect) {
-                    const bf16x2 vb = {rb[ks][2 * j], rb[ks][2 * j + 1]};
-                    ssb = __builtin_amdgcn_fdot2_f32_bf16(vb, vb, ssb, false);
-                }
-                if constexpr (MODE != kPass1) {
-                    const bf16x2 vc = {rc[ks][2 * j], rc[ks][2 * j + 1]};
-                    ssc = __builtin_amdgcn_fdot2_f32_bf16(vc, vc, ssc, false);
-                }
-            }
-        const float rsb = __builtin_amdgcn_rsqf(sum_over_rows(ssb) * (1.f / kN) + a.eps);
-        float rsc = 0.f;
-        if constexpr (MODE != kPass1) rsc = __builtin_amdgcn_rsqf(sum_over_rows(ssc) * (1.f / kN) + a.eps);
 
         // ---- angles: prefix over the tokens of this wave's rows (16-lane DPP rows)
         // slot k (0..15) is channel i = 8lg + k (k < 8) or 32 + 8lg + (k - 8)
@@ -652,73 +736,87 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         if (w == 0)
             newcarry = __builtin_amdgcn_fractf(sm.carry[l] + sm.angtot[0][l] + sm.angtot[1][l] + sm.angtot[2][l] +
                                                sm.angtot[3][l]);
-        // sine and cosine of the owned slots; slot block b comes from the token's
-        // rank lane b / NB (a DPP quad permute within the token's R lanes)
-        float osn[4 * NB], ocn[4 * NB];
+        // sine and cosine of the owned slots, packed as f16 (cos, sin) and (-sin, cos);
+        // slot block b comes from the token's rank lane b / NB (a DPP quad permute
+        // within the token's R lanes)
+        unsigned csp[4 * NB], scp[4 * NB];
 #pragma unroll
-        for (int k = 0; k < 4 * NB; ++k) sincos_rev(ph[k], osn[k], ocn[k]);
-        auto slot_sc = [&](int sl, float &sn, float &cn) {  // sl: compile-time slot 0..15
+        for (int k = 0; k < 4 * NB; ++k) {
+            float sn, cn;
+            sincos_rev(ph[k], sn, cn);
+            csp[k] = __builtin_bit_cast(unsigned, h2{(_Float16)cn, (_Float16)sn});
+            scp[k] = __builtin_bit_cast(unsigned, h2{(_Float16)(-sn), (_Float16)cn});
+        }
+        auto slot_pair = [&](const unsigned *src, int sl) -> h2 {  // sl: compile-time slot 0..15
             if constexpr (R == 1) {
-                sn = osn[sl];
-                cn = ocn[sl];
+                return __builtin_bit_cast(h2, src[sl]);
             } else {
                 const int b = sl >> 2, ro = b / NB, k = 4 * (b % NB) + (sl & 3);
+                const float v = __uint_as_float(src[k]);
+                float t;
                 // every lane of a group of R takes lane (group base + ro)
                 if constexpr (R == 4) {
-                    if (ro == 0) { sn = dpp_mov<0x00>(osn[k]); cn = dpp_mov<0x00>(ocn[k]); }
-                    else if (ro == 1) { sn = dpp_mov<0x55>(osn[k]); cn = dpp_mov<0x55>(ocn[k]); }
-                    else if (ro == 2) { sn = dpp_mov<0xAA>(osn[k]); cn = dpp_mov<0xAA>(ocn[k]); }
-                    else { sn = dpp_mov<0xFF>(osn[k]); cn = dpp_mov<0xFF>(ocn[k]); }
+                    if (ro == 0) t = dpp_mov<0x00>(v);
+                    else if (ro == 1) t = dpp_mov<0x55>(v);
+                    else if (ro == 2) t = dpp_mov<0xAA>(v);
+                    else t = dpp_mov<0xFF>(v);
                 } else {  // R == 2: quad_perm [ro, ro, 2 + ro, 2 + ro]
-                    if (ro == 0) { sn = dpp_mov<0xA0>(osn[k]); cn = dpp_mov<0xA0>(ocn[k]); }
-                    else { sn = dpp_mov<0xF5>(osn[k]); cn = dpp_mov<0xF5>(ocn[k]); }
+                    t = ro == 0 ? dpp_mov<0xA0>(v) : dpp_mov<0xF5>(v);
                 }
+                return __builtin_bit_cast(h2, __float_as_uint(t));
             }
         };
+        // B~ = normalised row times 2^(eg - k) plus the scaled bias (one packed f16
+        // multiply-add per channel pair), then rotated in fp32 and rounded to bf16.
+        // Rows past the end of the sequence need no zeroing: their weights w, gamma
+        // and cst are 0 and their outputs are not stored.
         bf16x8 bfr[4], cfr[4];
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2) {
+            const int i0 = 32 * ks2 + 8 * lg;  // first of this lane's 8 pairs
+            u32x4 bb[2], bc[2];
 #pragma unroll
-            for (int jh = 0; jh < 2; ++jh) {
-                const int i0 = 32 * ks2 + 8 * lg + 4 * jh;  // first of 4 channels
-                const f32x4 blo = *reinterpret_cast<const f32x4 *>(&sm.bias[0][r_row][i0]);
-                const f32x4 bhi = *reinterpret_cast<const f32x4 *>(&sm.bias[0][r_row][i0 + 64]);
-                f32x4 clo = {0.f, 0.f, 0.f, 0.f}, chi = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (MODE != kPass1) {
-                    clo = *reinterpret_cast<const f32x4 *>(&sm.bias[1][r_row][i0]);
-                    chi = *reinterpret_cast<const f32x4 *>(&sm.bias[1][r_row][i0 + 64]);
-                }
-                // BCNorm scale per channel: 1/rms, times the gain when there is one
-                f32x4 abl, abh, acl, ach;
-                if constexpr (HAS_W) {
-                    abl = rsb * *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0]);
-                    abh = rsb * *reinterpret_cast<const f32x4 *>(&sm.normw[0][i0 + 64]);
-                    acl = rsc * *reinterpret_cast<const f32x4 *>(&sm.normw[1][i0]);
-                    ach = rsc * *reinterpret_cast<const f32x4 *>(&sm.normw[1][i0 + 64]);
-                }
+            for (int hh = 0; hh < 2; ++hh) {
+                if constexpr (MODE != kCorrect) bb[hh] = *reinterpret_cast<const u32x4 *>(&sm.bq[0][r_row][i0 + 4 * hh]);
+                if constexpr (MODE != kPass1) bc[hh] = *reinterpret_cast<const u32x4 *>(&sm.bq[1][r_row][i0 + 4 * hh]);
+            }
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int j = 4 * jh + jj;
-                    float sn, cn;
-                    slot_sc(8 * ks2 + j, sn, cn);
+            for (int j = 0; j < 8; j += 2) {
+                const h2 cs0 = slot_pair(csp, 8 * ks2 + j), sc0 = slot_pair(scp, 8 * ks2 + j);
+                const h2 cs1 = slot_pair(csp, 8 * ks2 + j + 1), sc1 = slot_pair(scp, 8 * ks2 + j + 1);
+                // (vector elements go through scalars: a bit cast of an element
+                // lvalue was compiled as a cast of the vector's first element)
+                h2 vb[2], vc[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int jj = j + e;
                     if constexpr (MODE != kCorrect) {
-                        const float bl = (float)rb[ks2][j] * (HAS_W ? abl[jj] : rsb) + blo[jj];
-                        const float bh = (float)rb[ks2 + 2][j] * (HAS_W ? abh[jj] : rsb) + bhi[jj];
-                        // rows past the end of the sequence need no zeroing: their
-                        // weights w, gamma and cst are 0 and their outputs are not stored
-                        const float bbl = cn * bl + sn * bh;
-                        const float bbh = cn * bh - sn * bl;
-                        bfr[ks2][j] = (__bf16)bbl;
-                        bfr[ks2 + 2][j] = (__bf16)bbh;
+                        const unsigned qv = qb[2 * ks2 + (jj >> 2)][jj & 3], bv = bb[jj >> 2][jj & 3];
+                        vb[e] = __builtin_bit_cast(h2, qv) * rrB + __builtin_bit_cast(h2, bv);
                     }
                     if constexpr (MODE != kPass1) {
-                        const float cl = (float)rc[ks2][j] * (HAS_W ? acl[jj] : rsc) + clo[jj];
-                        const float ch = (float)rc[ks2 + 2][j] * (HAS_W ? ach[jj] : rsc) + chi[jj];
-                        const float ccl = cn * cl + sn * ch;
-                        const float cch = cn * ch - sn * cl;
-                        cfr[ks2][j] = (__bf16)ccl;
-                        cfr[ks2 + 2][j] = (__bf16)cch;
+                        const unsigned qv = qc[2 * ks2 + (jj >> 2)][jj & 3], bv = bc[jj >> 2][jj & 3];
+                        vc[e] = __builtin_bit_cast(h2, qv) * rrC + __builtin_bit_cast(h2, bv);
                     }
+                }
+                float ob[4], oc[4];
+                if constexpr (MODE != kCorrect && MODE != kPass1)
+                    rot_pairs4(vb[0], vb[1], vc[0], vc[1], cs0, sc0, cs1, sc1, ob, oc);
+                else if constexpr (MODE == kPass1)
+                    rot_pairs2(vb[0], vb[1], cs0, sc0, cs1, sc1, ob[0], ob[1], ob[2], ob[3]);
+                else
+                    rot_pairs2(vc[0], vc[1], cs0, sc0, cs1, sc1, oc[0], oc[1], oc[2], oc[3]);
+                if constexpr (MODE != kCorrect) {
+                    bfr[ks2][j] = (__bf16)ob[0];
+                    bfr[ks2 + 2][j] = (__bf16)ob[1];
+                    bfr[ks2][j + 1] = (__bf16)ob[2];
+                    bfr[ks2 + 2][j + 1] = (__bf16)ob[3];
+                }
+                if constexpr (MODE != kPass1) {
+                    cfr[ks2][j] = (__bf16)oc[0];
+                    cfr[ks2 + 2][j] = (__bf16)oc[1];
+                    cfr[ks2][j + 1] = (__bf16)oc[2];
+                    cfr[ks2 + 2][j + 1] = (__bf16)oc[3];
                 }
             }
         }
@@ -1061,11 +1159,59 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
     }
 }
 
-template <int R, bool HAS_W, bool FUSED, bool ONORM>
+// BCNorm of every raw B and C row (Mamba-3 paper §3.4, "BCNorm"), once per
+// (token, group, rank) row instead of once per head that reads it:
+// u = x / sqrt(mean(x^2) + eps) times the gain, scaled by 2^-eg with
+// max |g| <= 2^eg, stored as f16 pairs (n, n + N/2) -- the rotation's operand
+// layout. 16 lanes per row, lane k taking pairs 4k..4k+3; blockIdx.y is 0 for B
+// and 1 for C. Every row of both outputs is written.
+__global__ __launch_bounds__(256) void bcnorm_pairs_kernel(const __bf16 *Bm, const __bf16 *Cm, const float *gB,
+                                                           const float *gC, float eps, int64_t rows, unsigned *qB,
+                                                           unsigned *qC) {
+    const bool isC = blockIdx.y != 0;
+    const __bf16 *src = isC ? Cm : Bm;
+    const float *gn = isC ? gC : gB;
+    unsigned *dst = isC ? qC : qB;
+    const int k = threadIdx.x & 15;
+    f32x4 gl = {1.f, 1.f, 1.f, 1.f}, gh = {1.f, 1.f, 1.f, 1.f};
+    if (gn) {
+        gl = *reinterpret_cast<const f32x4 *>(gn + 4 * k);
+        gh = *reinterpret_cast<const f32x4 *>(gn + kHalf + 4 * k);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(gl[j]), fabsf(gh[j])));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+    const float sc = ldexpf(1.f, -max(0, exp_ceil(m)));
+    gl *= sc;
+    gh *= sc;
+    for (int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); r < rows; r += (int64_t)gridDim.x * 16) {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(src + r * kN + 4 * k);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(src + r * kN + kHalf + 4 * k);
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float a = (float)lo[j], b = (float)hi[j];
+            ss = __builtin_fmaf(a, a, __builtin_fmaf(b, b, ss));
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 16);
+        const float rs = __builtin_amdgcn_rsqf(ss * (1.f / kN) + eps);
+        u32x4 out;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            out[j] = __builtin_bit_cast(
+                unsigned, h2{(_Float16)((float)lo[j] * rs * gl[j]), (_Float16)((float)hi[j] * rs * gh[j])});
+        *reinterpret_cast<u32x4 *>(dst + r * kHalf + 4 * k) = out;
+    }
+}
+
+template <int R, bool FUSED, bool ONORM>
 hipError_t launch_rw(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
     const int64_t chains = a.b * a.H;
     if (sp.nseg <= 1) {
-        hipLaunchKernelGGL((scan_mfma_kernel<kFull, R, HAS_W, FUSED, ONORM>), dim3((unsigned)chains), dim3(kThreads), 0,
+        hipLaunchKernelGGL((scan_mfma_kernel<kFull, R, FUSED, ONORM>), dim3((unsigned)chains), dim3(kThreads), 0,
                            s, a, sp);
         return hipGetLastError();
     }
@@ -1073,34 +1219,32 @@ hipError_t launch_rw(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
     if constexpr (!ONORM) {
         // local outputs and end states, the combine (which also writes the final
         // state), then the correction of each segment's outputs for its incoming state
-        hipLaunchKernelGGL((scan_mfma_kernel<kLocal, R, HAS_W, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a,
+        hipLaunchKernelGGL((scan_mfma_kernel<kLocal, R, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a,
                            sp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp, true);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((scan_mfma_kernel<kCorrect, R, HAS_W, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a,
+        hipLaunchKernelGGL((scan_mfma_kernel<kCorrect, R, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a,
                            sp);
         return hipGetLastError();
     }
     // the output norm is not linear in y: end states first, then every segment
     // again from its incoming state. Pass 1 produces no output, so it takes no norm
-    hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R, HAS_W, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
+    hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp, false);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R, HAS_W, FUSED, ONORM>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
+    hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R, FUSED, ONORM>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
     return hipGetLastError();
 }
 
 template <int R, bool FUSED>
 hipError_t launch_rf(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
-    const bool hw = a.B_normw || a.C_normw;
-    if (a.onorm) return hw ? launch_rw<R, true, FUSED, true>(a, sp, s) : launch_rw<R, false, FUSED, true>(a, sp, s);
-    return hw ? launch_rw<R, true, FUSED, false>(a, sp, s) : launch_rw<R, false, FUSED, false>(a, sp, s);
+    return a.onorm ? launch_rw<R, FUSED, true>(a, sp, s) : launch_rw<R, FUSED, false>(a, sp, s);
 }
 
 template <int R>
@@ -1146,22 +1290,42 @@ int mfma_auto_segments(int64_t chains, int64_t nchunks) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t mfma_workspace_bytes(int64_t chains, int nseg, int64_t P, int64_t N) {
-    return align256(sizeof(float) * chains * nseg * P * N) + align256(sizeof(float) * chains * nseg) +
-           align256(sizeof(float) * chains * nseg * (N / 2));
+// Workspace: the normalised B and C rows, then (with a split) the segment records.
+size_t mfma_workspace_bytes(int64_t rows, int64_t chains, int nseg, int64_t P, int64_t N) {
+    size_t b = 2 * align256(sizeof(unsigned) * rows * (N / 2));
+    if (nseg > 1)
+        b += align256(sizeof(float) * chains * nseg * P * N) + align256(sizeof(float) * chains * nseg) +
+             align256(sizeof(float) * chains * nseg * (N / 2));
+    return b;
 }
 
-void mfma_workspace_carve(void *ws, int64_t chains, int nseg, int64_t P, int64_t N, SplitPlan *sp) {
+void mfma_workspace_carve(void *ws, int64_t rows, int64_t chains, int nseg, int64_t P, int64_t N, ScanArgs *a,
+                          SplitPlan *sp) {
     char *p = static_cast<char *>(ws);
-    sp->seg_state = reinterpret_cast<float *>(p);
-    p += align256(sizeof(float) * chains * nseg * P * N);
-    sp->seg_decay = reinterpret_cast<float *>(p);
-    p += align256(sizeof(float) * chains * nseg);
-    sp->seg_angle = reinterpret_cast<float *>(p);
+    a->Bq = reinterpret_cast<unsigned *>(p);
+    p += align256(sizeof(unsigned) * rows * (N / 2));
+    a->Cq = reinterpret_cast<unsigned *>(p);
+    p += align256(sizeof(unsigned) * rows * (N / 2));
+    if (nseg > 1) {
+        sp->seg_state = reinterpret_cast<float *>(p);
+        p += align256(sizeof(float) * chains * nseg * P * N);
+        sp->seg_decay = reinterpret_cast<float *>(p);
+        p += align256(sizeof(float) * chains * nseg);
+        sp->seg_angle = reinterpret_cast<float *>(p);
+    }
 }
 
 hipError_t launch_scan_mfma(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
     if (a.b * a.H == 0) return hipSuccess;
+    const int64_t rows = a.b * a.L * a.G * a.R;
+    if (rows > 0) {
+        const int64_t nb = (rows + 15) / 16;
+        hipLaunchKernelGGL(bcnorm_pairs_kernel, dim3((unsigned)(nb < 16384 ? nb : 16384), 2), dim3(256), 0, s,
+                           static_cast<const __bf16 *>(a.Braw), static_cast<const __bf16 *>(a.Craw), a.B_normw,
+                           a.C_normw, a.eps, rows, a.Bq, a.Cq);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     switch (a.R) {
         case 1: return launch_r<1>(a, sp, s);
         case 2: return launch_r<2>(a, sp, s);

@@ -290,7 +290,7 @@ def scan_fwd_noalloc(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, y, h_fina
                      force_generic=False, D=None, out_norm=False, out_normw=None, stream=None):
     """m3_scan_fwd_noalloc: scan_fwd for callers that cannot allocate. The caller
     passes the outputs y [b,L,H,R,P] (io dtype) and h_final [b,H,P,N] fp32 (or None);
-    the segment split's workspace is the library's per-GPU array. Nothing is
+    the workspace (normalised B and C rows, segment records) is the library's per-GPU array. Nothing is
     allocated here either. Returns (y, h_final)."""
     b, L, H, R, P = _dims5("x", x, 5)
     _, _, G, _, N = _dims5("Braw", Braw, 5)

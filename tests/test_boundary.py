@@ -295,11 +295,11 @@ def m3_status(m3, name):
 
 
 def test_noalloc_rejects_workspace_beyond_its_array(m3):
-    # 256 chains forced into 16 segments each need ~135 MB of workspace, beyond
-    # the allocation-free entry point's fixed 64 MiB: refused before any HIP call
-    shape = _shape(m3, batch=4, nheads=64, seqlen=1024, nsegments=16)
+    # 4 x 262144 tokens need 512 MiB of normalised B and C rows alone, beyond the
+    # allocation-free entry point's fixed 256 MiB: refused before any HIP call
+    shape = _shape(m3, batch=4, nheads=64, seqlen=1 << 18)
     p = m3.plan(shape)
-    assert p.workspace_bytes > m3.noalloc_max_workspace_bytes() == 64 << 20
+    assert p.workspace_bytes > m3.noalloc_max_workspace_bytes() == 256 << 20
     io = _fake_io(m3)
     rc = m3.lib.m3_scan_fwd_noalloc(ctypes.byref(shape), ctypes.byref(io), None)
     assert rc == -4  # M3_ERR_WORKSPACE_TOO_SMALL
@@ -309,12 +309,27 @@ def test_noalloc_rejects_workspace_beyond_its_array(m3):
     assert m3.lib.m3_scan_fwd_noalloc(ctypes.byref(shape), ctypes.byref(bad), None) == -3
 
 
-def test_every_automatic_plan_fits_the_noalloc_array(m3):
+def test_matrix_core_workspace_layout(m3):
+    # the normalised B and C rows (N/2 f16 pairs each) come first, then the segment records
+    for b, L, H, R, C in ((8, 4096, 64, 1, 64), (8, 4096, 64, 4, 16), (2, 32768, 24, 4, 16), (1, 5, 2, 2, 32)):
+        p = m3.plan(_shape(m3, batch=b, nheads=H, seqlen=L, rank=R, chunk=C))
+        rows = b * L * R
+        q = 2 * ((rows * 64 * 4 + 255) // 256 * 256)
+        seg = 0
+        if p.nsegments > 1:
+            ch = b * H * p.nsegments
+            seg = sum((n * 4 + 255) // 256 * 256 for n in (ch * 64 * 128, ch, ch * 64))
+        assert p.workspace_bytes == q + seg, (b, L, H, R, p.nsegments)
+
+
+def test_every_automatic_plan_up_to_2pow18_rows_fits_the_noalloc_array(m3):
     cap = m3.noalloc_max_workspace_bytes()
     for b in (1, 2, 3, 4, 8):
         for H in (1, 2, 4, 8, 16, 24, 32, 48, 64, 96, 128, 191, 255, 383):
-            for L in (4096, 32768, 1 << 20):
+            for L in (1024, 4096, 32768, 1 << 17):
                 for R, C in ((1, 64), (2, 32), (4, 16)):
+                    if b * L * R > 1 << 18:
+                        continue
                     p = m3.plan(_shape(m3, batch=b, nheads=H, seqlen=L, rank=R, chunk=C))
                     assert p.workspace_bytes <= cap, (b, H, L, R, p.workspace_bytes)
 
