@@ -121,18 +121,20 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
 
 // Rotation of f16 pairs v = (lo, hi) by their angles, in fp32 (v_dot2_f32_f16):
 // lo' = cos lo + sin hi = dot(v, (cos, sin)), hi' = cos hi - sin lo =
-// dot(v, (-sin, cos)); cs = (cos, sin) and sc = (-sin, cos) of each pair's angle.
+// dot(v, (-sin, cos)); cs = (cos, sin) and sc = (sin, cos) of each pair's angle,
+// the second product negating the low half of sc through the encoding's neg_lo.
 // Written out because the compiler's form of the builtin accumulates into its
-// destination and needs a zeroing move per product. A vector instruction that
-// reads a dot product's result needs 3 wait states after it, which the compiler
-// inserts only for dot instructions it emitted itself: each block ends with
-// s_nop 2, and its outputs are early-clobber (written while inputs are still read).
+// destination and needs a zeroing move per product, and does not fold the
+// negation. A vector instruction that reads a dot product's result needs 3 wait
+// states after it, which the compiler inserts only for dot instructions it
+// emitted itself: each block ends with s_nop 2, and its outputs are early-clobber
+// (written while inputs are still read).
 __device__ __forceinline__ void rot_pairs2(h2 v0, h2 v1, h2 cs0, h2 sc0, h2 cs1, h2 sc1, float &l0, float &h0,
                                            float &l1, float &h1) {
     asm("v_dot2_f32_f16 %0, %4, %6, 0\n\t"
-        "v_dot2_f32_f16 %1, %4, %7, 0\n\t"
+        "v_dot2_f32_f16 %1, %4, %7, 0 neg_lo:[0,1,0]\n\t"
         "v_dot2_f32_f16 %2, %5, %8, 0\n\t"
-        "v_dot2_f32_f16 %3, %5, %9, 0\n\t"
+        "v_dot2_f32_f16 %3, %5, %9, 0 neg_lo:[0,1,0]\n\t"
         "s_nop 2"
         : "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
         : "v"(v0), "v"(v1), "v"(cs0), "v"(sc0), "v"(cs1), "v"(sc1));
@@ -141,13 +143,13 @@ __device__ __forceinline__ void rot_pairs2(h2 v0, h2 v1, h2 cs0, h2 sc0, h2 cs1,
 __device__ __forceinline__ void rot_pairs4(h2 b0, h2 b1, h2 c0, h2 c1, h2 cs0, h2 sc0, h2 cs1, h2 sc1, float *ob,
                                            float *oc) {
     asm("v_dot2_f32_f16 %0, %8, %12, 0\n\t"
-        "v_dot2_f32_f16 %1, %8, %13, 0\n\t"
+        "v_dot2_f32_f16 %1, %8, %13, 0 neg_lo:[0,1,0]\n\t"
         "v_dot2_f32_f16 %2, %9, %14, 0\n\t"
-        "v_dot2_f32_f16 %3, %9, %15, 0\n\t"
+        "v_dot2_f32_f16 %3, %9, %15, 0 neg_lo:[0,1,0]\n\t"
         "v_dot2_f32_f16 %4, %10, %12, 0\n\t"
-        "v_dot2_f32_f16 %5, %10, %13, 0\n\t"
+        "v_dot2_f32_f16 %5, %10, %13, 0 neg_lo:[0,1,0]\n\t"
         "v_dot2_f32_f16 %6, %11, %14, 0\n\t"
-        "v_dot2_f32_f16 %7, %11, %15, 0\n\t"
+        "v_dot2_f32_f16 %7, %11, %15, 0 neg_lo:[0,1,0]\n\t"
         "s_nop 2"
         : "=&v"(ob[0]), "=&v"(ob[1]), "=&v"(ob[2]), "=&v"(ob[3]), "=&v"(oc[0]), "=&v"(oc[1]), "=&v"(oc[2]),
           "=&v"(oc[3])
@@ -736,7 +738,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         if (w == 0)
             newcarry = __builtin_amdgcn_fractf(sm.carry[l] + sm.angtot[0][l] + sm.angtot[1][l] + sm.angtot[2][l] +
                                                sm.angtot[3][l]);
-        // sine and cosine of the owned slots, packed as f16 (cos, sin) and (-sin, cos);
+        // sine and cosine of the owned slots, packed as f16 (cos, sin) and (sin, cos);
         // slot block b comes from the token's rank lane b / NB (a DPP quad permute
         // within the token's R lanes)
         unsigned csp[4 * NB], scp[4 * NB];
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             float sn, cn;
             sincos_rev(ph[k], sn, cn);
             csp[k] = __builtin_bit_cast(unsigned, h2{(_Float16)cn, (_Float16)sn});
-            scp[k] = __builtin_bit_cast(unsigned, h2{(_Float16)(-sn), (_Float16)cn});
+            scp[k] = __builtin_bit_cast(unsigned, h2{(_Float16)sn, (_Float16)cn});
         }
         auto slot_pair = [&](const unsigned *src, int sl) -> h2 {  // sl: compile-time slot 0..15
             if constexpr (R == 1) {
