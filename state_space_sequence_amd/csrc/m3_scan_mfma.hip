@@ -681,14 +681,20 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
         constexpr int NB = 4 / R;  // owned blocks of 4 slots
         const float drev = drow * kInv2Pi;
         float ph[4 * NB];
+        {
+            // (no contraction: fused into the first step's product, each add with a
+            // neighbour's value took a zeroed register and a separate DPP move
+            // instead of one DPP add)
+#pragma clang fp contract(off)
 #pragma unroll
-        for (int q = 0; q < NB; ++q)
+            for (int q = 0; q < NB; ++q)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ph[4 * q + j] = drev * th[q][j];
+                for (int j = 0; j < 4; ++j) ph[4 * q + j] = drev * th[q][j];
 #pragma unroll
-        for (int sh = R; sh < 16; sh <<= 1)
+            for (int sh = R; sh < 16; sh <<= 1)
 #pragma unroll
-            for (int k = 0; k < 4 * NB; ++k) ph[k] += dpp_row_shr(ph[k], sh);
+                for (int k = 0; k < 4 * NB; ++k) ph[k] += dpp_row_shr(ph[k], sh);
+        }
         if (lr >= 16 - R) {  // the wave's last token: its rank lanes hold every block
 #pragma unroll
             for (int q = 0; q < NB; ++q) {
