@@ -85,6 +85,30 @@ def test_segment_split_matches_single_pass(R, C, nseg, slow, state):
     assert relerr(ys, y1) < 1e-2 and relerr(hs, h1) < 1e-2
 
 
+@pytest.mark.parametrize("R,C", [(1, 64), (4, 16)])
+def test_mfma_large_gains_and_biases(R, C):
+    """BCNorm gains and biases far from 1. The matrix-core path holds the
+    normalised B and C in f16 for the rotation, scaled per head by powers of two
+    (the gain exponent, raised further where a bias needs it) that the per-row
+    tables undo exactly. Head 0 has B biases ~1e7 (scale beyond the gain's), head
+    1 C biases ~1e5; B gains ~400, C gains ~1e-3. Each head is checked against
+    the oracle on its own scale."""
+    shape = Shape(2, 150, 3, 1, 64, 128, R, C, "bf16")
+    inp = make_scan_inputs(shape, seed=26, with_normw=True, slow_decay=True)
+    inp["B_normw"] = (inp["B_normw"] * 400.0).astype(np.float32)
+    inp["C_normw"] = (inp["C_normw"] * 1e-3).astype(np.float32)
+    inp["B_bias"][0] *= 1e8
+    inp["C_bias"][1] *= 1e6
+    y, h = gpu_scan(inp, shape)
+    yr, hr = oracle.scan(inp, shape)
+    assert np.isfinite(y).all() and np.isfinite(h).all()
+    for hh in range(shape.nheads):
+        ey = relerr(y[:, :, hh], yr[:, :, hh])
+        eh = relerr(h[:, hh], hr[:, hh])
+        say("R=%d head %d: |y| %.2e err y %.2e h %.2e" % (R, hh, np.abs(yr[:, :, hh]).max(), ey, eh))
+        assert ey < TOL_BF16 and eh < TOL_BF16
+
+
 def test_mfma_deterministic():
     shape = Shape(2, 256, 4, 1, 64, 128, 1, 64, "bf16")
     inp = make_scan_inputs(shape, seed=24)
