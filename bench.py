@@ -373,7 +373,8 @@ def main():
     traffic = traffic_from_counters(balg)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "scan_mfma_kernel<full, R=1>", "avg_launch_ms": round(kern_ms, 5),
+            "kernel": "bcnorm_pairs_kernel + scan_mfma_kernel<full, R=1> (one m3_scan_fwd call)",
+            "avg_launch_ms": round(kern_ms, 5),
             "alg_bytes_per_launch": balg,
             "mfma_frac_dense": round(fl_dense / (kern_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4),
             "mfma_frac_causal": round(fl_causal / (kern_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4),
