@@ -84,6 +84,17 @@ typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
 #define M3_FLAG_NORM_AFTER_GATE 8u /* with M3_FLAG_OUT_NORM and the fused gate (W_X set):
                                     norm O' (after the gate and the rank contraction)
                                     instead of Y. M3_ERR_INVALID_ARG without both. */
+#define M3_FLAG_BWD_LOW_MEMORY 16u /* m3_scan_bwd only, N = 128, P = 64, R in {1, 2, 4}: the
+                                      windowed schedule. The forward sweep keeps a state
+                                      checkpoint every k chunks; then, last window first,
+                                      each window of k chunks has its states recomputed
+                                      from its checkpoint, its reverse sweep run and its
+                                      per-head dB, dC, d theta sums reduced before the next
+                                      window reuses the buffers. k minimises the workspace
+                                      (about sqrt of the chunk count). Same results, bit
+                                      for bit, for about one more forward sweep of time;
+                                      m3_scan_bwd_workspace_bytes gives the smaller size
+                                      for a shape with this flag. */
 
 typedef struct {
     int64_t batch;     /* b >= 0 */

@@ -69,7 +69,8 @@ m3_status check_shape(const m3_shape *s) {
     if (!(s->eps >= 0.f) || !isfinite(s->eps)) return M3_ERR_INVALID_ARG;
     if (s->nsegments < 0) return M3_ERR_INVALID_ARG;
     // (the bf16-state flag is decode only)
-    if (s->flags & ~(M3_FLAG_FORCE_GENERIC | M3_FLAG_OUT_NORM | M3_FLAG_NORM_AFTER_GATE)) return M3_ERR_INVALID_ARG;
+    if (s->flags & ~(M3_FLAG_FORCE_GENERIC | M3_FLAG_OUT_NORM | M3_FLAG_NORM_AFTER_GATE | M3_FLAG_BWD_LOW_MEMORY))
+        return M3_ERR_INVALID_ARG;
     if (s->batch > (1LL << 31) || s->nheads > (1LL << 20) || s->seqlen > (1LL << 40)) return M3_ERR_UNSUPPORTED;
     // every launch takes at most one workgroup per (batch, head) chain and segment,
     // and the grid is a 32-bit count; tokens and elements stay far below 64-bit overflow
@@ -80,6 +81,7 @@ m3_status check_shape(const m3_shape *s) {
 }
 
 m3_status make_plan(const m3_shape &s, Plan *pl) {
+    if (s.flags & M3_FLAG_BWD_LOW_MEMORY) return M3_ERR_INVALID_ARG;  // a backward flag
     Plan p{};
     const int64_t nchunks = (s.seqlen + s.chunk - 1) / s.chunk;
     if (mfma_applicable(s)) {
@@ -322,7 +324,11 @@ static ScanArgs bwd_args(const m3_shape &s, const m3_scan_io *io) {
 
 size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape) {
     if (check_shape(shape) != M3_OK || !bwd_shape_ok(*shape)) return 0;
-    return scan_bwd_workspace_bytes(bwd_args(*shape, nullptr), nullptr);
+    const ScanArgs a = bwd_args(*shape, nullptr);
+    const bool lowmem = (shape->flags & M3_FLAG_BWD_LOW_MEMORY) != 0;
+    if (shape->flags & ~(M3_FLAG_FORCE_GENERIC | M3_FLAG_BWD_LOW_MEMORY)) return 0;
+    if (lowmem && !scan_bwd_lowmem_ok(a)) return 0;
+    return scan_bwd_workspace_bytes(a, lowmem);
 }
 
 m3_status m3_scan_bwd(const m3_shape *shape, const m3_scan_io *io, const m3_scan_grads *gr, void *workspace,
@@ -331,7 +337,9 @@ m3_status m3_scan_bwd(const m3_shape *shape, const m3_scan_io *io, const m3_scan
     if (st != M3_OK) return st;
     if (!io || !gr) return M3_ERR_INVALID_ARG;
     const m3_shape &s = *shape;
-    if (s.flags & ~M3_FLAG_FORCE_GENERIC) return (s.flags & M3_FLAG_OUT_NORM) ? M3_ERR_UNSUPPORTED : M3_ERR_INVALID_ARG;
+    if (s.flags & ~(M3_FLAG_FORCE_GENERIC | M3_FLAG_BWD_LOW_MEMORY))
+        return (s.flags & M3_FLAG_OUT_NORM) ? M3_ERR_UNSUPPORTED : M3_ERR_INVALID_ARG;
+    const bool lowmem = (s.flags & M3_FLAG_BWD_LOW_MEMORY) != 0;
     if (io->W_X || io->W_Z || io->W_O || io->z || io->o || io->D || io->out_normw) return M3_ERR_UNSUPPORTED;
     if ((io->x_prev == nullptr) != (io->Braw_prev == nullptr)) return M3_ERR_INVALID_ARG;
     if (!bwd_shape_ok(s)) return M3_ERR_UNSUPPORTED;
@@ -372,14 +380,15 @@ m3_status m3_scan_bwd(const m3_shape *shape, const m3_scan_io *io, const m3_scan
         }
         return M3_OK;
     }
-    const size_t need = scan_bwd_workspace_bytes(a, nullptr);
+    if (lowmem && !scan_bwd_lowmem_ok(a)) return M3_ERR_UNSUPPORTED;
+    const size_t need = scan_bwd_workspace_bytes(a, lowmem);
     if (workspace == nullptr || ws_bytes < need) return M3_ERR_WORKSPACE_TOO_SMALL;
     BwdIO bio{};
     bio.dy = gr->dy; bio.dh_final = gr->dh_final; bio.dx = gr->dx; bio.dBraw = gr->dBraw; bio.dCraw = gr->dCraw;
     bio.ddt = gr->ddt; bio.dA = gr->dA; bio.dlam = gr->dlam; bio.dtheta = gr->dtheta; bio.dB_bias = gr->dB_bias;
     bio.dC_bias = gr->dC_bias; bio.dB_normw = gr->dB_normw; bio.dC_normw = gr->dC_normw; bio.dh0 = gr->dh0;
     bio.dx_prev = gr->dx_prev; bio.dBraw_prev = gr->dBraw_prev;
-    e = launch_scan_bwd(a, bio, workspace, hs);
+    e = launch_scan_bwd(a, bio, workspace, lowmem, hs);
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 

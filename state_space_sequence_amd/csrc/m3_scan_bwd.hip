@@ -114,6 +114,18 @@ struct BwdArgs {
     float *gBp;   // [b,H,R,N]   previous token's dB (per head)
     float *fold;  // [b,H]       gradient of the fold factor (1 - lam_0) dt_0
     float *bpart; // [b,H][2][R][2][N] matrix-core chain kernel: per-chain bias sums (row tile, rank, B / C)
+    // Rows of gB, gC and gth: token t of batch b is row b * Lb + t - tbase (Lb = L, tbase = 0
+    // in one pass; the window's tokens under the low-memory schedule).
+    int64_t Lb, tbase;
+    // Low-memory schedule (matrix-core chain kernel only; wchunks = 0: one pass). chk then
+    // holds a checkpoint every wchunks chunks plus the final state ([b*H][nwin+1][slot]).
+    // A launch with win < 0 runs the forward sweep only; a launch with win = w recomputes
+    // the states of window w's chunks into chkw ([b*H][wchunks+1][slot]) from its
+    // checkpoint and runs the reverse sweep over them, carrying dS, the angle-gradient
+    // carry and the bias sums to the next window (win - 1) through rst.
+    int wchunks, win;
+    float *chkw;
+    float *rst;   // [b*H][N*P + N/2 + 4*512]
 };
 
 // NF, PF: N and P fixed at compile time (0: taken from the arguments)
@@ -760,6 +772,15 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     const int64_t L = a.L, H = a.H, G = a.G;
     const int nch = (int)((L + Cb - 1) / Cb);
     const int64_t slotf = (int64_t)N * P + HALF;
+    // chunks this launch sweeps: all of them in one pass, else window ba.win (the
+    // forward-only launch, win < 0, sweeps all and keeps every wchunks-th state)
+    const bool windowed = ba.wchunks > 0;
+    const int nwin = windowed ? (nch + ba.wchunks - 1) / ba.wchunks : 1;
+    const bool fwd_only = windowed && ba.win < 0;
+    const int kc0 = (windowed && !fwd_only) ? ba.win * ba.wchunks : 0;
+    const int kc1 = (windowed && !fwd_only) ? (kc0 + ba.wchunks < nch ? kc0 + ba.wchunks : nch) : nch;
+    const bool last_win = !windowed || fwd_only || ba.win == nwin - 1;
+    const bool first_win = !windowed || ba.win == 0;
 
     extern __shared__ float sm[];
     float *dSl = sm;                  // [N][PS]
@@ -803,7 +824,19 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
 #pragma unroll
     for (int r = 0; r < R; ++r) sbacc[r * NT + tid] = 0.f;
 
-    float *chk = ba.chk + bh * (int64_t)(nch + 1) * slotf;
+    // where the forward sweep stores the state before chunk k (k = kc1: after the last
+    // chunk), and where the reverse sweep reads it; nullptr: not stored
+    float *const chk = ba.chk + bh * (int64_t)((windowed ? nwin : nch) + 1) * slotf;
+    float *const chkw = windowed ? ba.chkw + bh * (int64_t)(ba.wchunks + 1) * slotf : nullptr;
+    auto fwd_slot = [&](int k) -> float * {
+        if (!windowed) return chk + (int64_t)k * slotf;
+        if (fwd_only) return (k == nch) ? chk + (int64_t)nwin * slotf
+                                        : ((k % ba.wchunks == 0) ? chk + (int64_t)(k / ba.wchunks) * slotf : nullptr);
+        return chkw + (int64_t)(k - kc0) * slotf;
+    };
+    auto rev_slot = [&](int k) -> const float * {
+        return windowed ? chkw + (int64_t)(k - kc0) * slotf : chk + (int64_t)k * slotf;
+    };
     for (int e = tid; e < 2 * R * N; e += NT) {
         const int which = e / (R * N), rem = e % (R * N);
         sbias[e] = (which == 0 ? a.B_bias : a.C_bias)[hi * R * N + rem];
@@ -1019,21 +1052,28 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         __syncthreads();
     };
 
-    // ---- initial state into LDS, then into the accumulators (rows 16w + 4lg + jj, column 16pt + lr)
-    for (int e = tid; e < N * P; e += NT) {
-        const int p = e / N, n = e % N;  // coalesced over h0's n
-        dSl[n * PS + p] = a.h0 ? a.h0[(bh * P + p) * N + n] : 0.f;
-    }
-    for (int i = tid; i < HALF; i += NT) carry[i] = 0.f;
+    // ---- initial state into LDS, then into the accumulators (rows 16w + 4lg + jj, column 16pt + lr):
+    // h0 with the previous token's fold, or a window's checkpoint
     const float fold_f = (a.has_prev && L > 0) ? (1.0f - a.lam[bi * L * H + hi]) * a.dt[bi * L * H + hi] : 0.f;
-    if (a.has_prev && L > 0) {
-        __syncthreads();
-        prev_rows();
+    if (windowed && !fwd_only) {
+        const float *s0 = chk + (int64_t)ba.win * slotf;
+        for (int e = tid; e < N * P; e += NT) dSl[(e / P) * PS + e % P] = s0[e];
+        for (int i = tid; i < HALF; i += NT) carry[i] = s0[N * P + i];
+    } else {
         for (int e = tid; e < N * P; e += NT) {
-            const int n = e / P, p = e % P;
-            float acc = 0.f;
-            for (int r = 0; r < R; ++r) acc += pB[r * NS + n] * pX[r * PS + p];
-            dSl[n * PS + p] += fold_f * acc;
+            const int p = e / N, n = e % N;  // coalesced over h0's n
+            dSl[n * PS + p] = a.h0 ? a.h0[(bh * P + p) * N + n] : 0.f;
+        }
+        for (int i = tid; i < HALF; i += NT) carry[i] = 0.f;
+        if (a.has_prev && L > 0) {
+            __syncthreads();
+            prev_rows();
+            for (int e = tid; e < N * P; e += NT) {
+                const int n = e / P, p = e % P;
+                float acc = 0.f;
+                for (int r = 0; r < R; ++r) acc += pB[r * NS + n] * pX[r * PS + p];
+                dSl[n * PS + p] += fold_f * acc;
+            }
         }
     }
     __syncthreads();
@@ -1045,22 +1085,27 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
 
     // ---- forward sweep (each chunk's inputs are loaded during the previous chunk)
     StageRegs fsr;
-    if (nch > 0) stage_issue(0, (int)(L < Cb ? L : Cb), false, fsr);
-    for (int k = 0; k < nch; ++k) {
+    if (kc0 < kc1) {
+        const int64_t cf = (int64_t)kc0 * Cb;
+        stage_issue(cf, (int)((L - cf) < Cb ? (L - cf) : Cb), false, fsr);
+    }
+    for (int k = kc0; k < kc1; ++k) {
         const int l = opaque(tid & 63), lr = l & 15, lg = l >> 4;
         const int64_t c0 = (int64_t)k * Cb;
         const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
-        float *slot = chk + (int64_t)k * slotf;
+        float *slot = fwd_slot(k);
         stage_put(nv, fsr, false);
-        if (k + 1 < nch) {
+        if (k + 1 < kc1) {
             const int64_t c1 = c0 + Cb;
             stage_issue(c1, (int)((L - c1) < Cb ? (L - c1) : Cb), false, fsr);
         }
+        if (slot) {
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
+            for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) slot[(16 * w + 4 * lg + jj) * P + 16 * pt + lr] = acc[pt][jj];
-        for (int i = tid; i < HALF; i += NT) slot[N * P + i] = carry[i];
+                for (int jj = 0; jj < 4; ++jj) slot[(16 * w + 4 * lg + jj) * P + 16 * pt + lr] = acc[pt][jj];
+            for (int i = tid; i < HALF; i += NT) slot[N * P + i] = carry[i];
+        }
         stage_finish(c0, nv, false);
         // S <- e^{cs_end} S + sum_sigma (E B_bar)^T x: A[n][sigma] = E_s B_bar[sigma][n], B[sigma][p] = x
         const float dec = expf(lcs[nv - 1]);
@@ -1079,19 +1124,29 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         __syncthreads();
     }
     {
-        float *slot = chk + (int64_t)nch * slotf;
+        float *slot = fwd_slot(kc1);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 slot[(16 * w + 4 * lg + jj) * P + 16 * pt + lr] = acc[pt][jj];
-                dSl[(16 * w + 4 * lg + jj) * PS + 16 * pt + lr] = acc[pt][jj];  // S_final
+                dSl[(16 * w + 4 * lg + jj) * PS + 16 * pt + lr] = acc[pt][jj];  // S_final (last window)
             }
         for (int i = tid; i < HALF; i += NT) slot[N * P + i] = carry[i];
     }
     __syncthreads();
+    if (fwd_only) return;
+    constexpr int64_t rstf = (int64_t)N * P + HALF + 4 * NT;  // dS, angle-gradient carry, bias sums
+    if (!last_win) {
+        // a later window's reverse sweep left dS, the angle-gradient carry and the bias sums
+        const float *rs = ba.rst + bh * rstf;
+        for (int e = tid; e < N * P; e += NT) dSl[(e / P) * PS + e % P] = rs[e];
+        for (int i = tid; i < HALF; i += NT) rcar[i] = rs[N * P + i];
+#pragma unroll
+        for (int r = 0; r < R; ++r) sbacc[r * NT + tid] = rs[N * P + HALF + r * NT + tid];
+    }
     // ---- d Phi_end[i] = sum_p (-dh_lo h_hi + dh_hi h_lo), h = R(Phi_end) S_final
-    for (int i = tid; i < HALF; i += NT) {
+    for (int i = tid; last_win && i < HALF; i += NT) {
         float rg = 0.f;
         if (ba.dh_final) {
             float sn, cs;
@@ -1106,7 +1161,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     }
     __syncthreads();
     // dS = R(-Phi_end) dh_final
-    for (int e = tid; e < HALF * P; e += NT) {
+    for (int e = tid; last_win && e < HALF * P; e += NT) {
         const int p = e / HALF, i = e % HALF;
         float dlo = 0.f, dhi = 0.f;
         if (ba.dh_final) {
@@ -1131,7 +1186,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     // columns p = 16 kb + 4 lg + j. The first is S_final; after that, the previous chunk's S_in.
     f4 uprev[2][4];
     {
-        const float *slotf_ = chk + (int64_t)nch * slotf;
+        const float *slotf_ = rev_slot(kc1);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -1141,11 +1196,11 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
     // (reverse chunks are staged in place: holding the next chunk's loads across
     // steps 6 and 7 cost 33-55 spilled registers and ran slower)
     StageRegs rsr;
-    for (int k = nch - 1; k >= 0; --k) {
+    for (int k = kc1 - 1; k >= kc0; --k) {
         const int l = opaque(tid & 63), lr = l & 15, lg = l >> 4;
         const int64_t c0 = (int64_t)k * Cb;
         const int nv = (int)((L - c0) < Cb ? (L - c0) : Cb);
-        const float *slot = chk + (int64_t)k * slotf;
+        const float *slot = rev_slot(k);
         // S_in fragments of (1), in flight during the staging
         f4 uin[2][4];
 #pragma unroll
@@ -1343,7 +1398,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                 if (t < nv) {
                     float sn, cs;
                     sincos_rev(Phi[t * PHS + i], &sn, &cs);
-                    const int64_t o = (((bi * L + c0 + t) * H + hi) * R + r) * N;
+                    const int64_t o = (((bi * ba.Lb + c0 + t - ba.tbase) * H + hi) * R + r) * N;
                     const float gbl = cs * dbl - sn * dbh, gbh = sn * dbl + cs * dbh;
                     const float gcl = cs * dcl - sn * dch, gch = sn * dcl + cs * dch;
                     ba.gB[o + i] = gbl;
@@ -1414,8 +1469,8 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
                 const float tot = group_sum<32>(d);
                 const float rc = rcar[i] + tot - incl + d;  // sum over tokens >= t
                 if (v_) {
-                    const int64_t tok = bi * L + c0 + t;
-                    ba.gth[(tok * H + hi) * HALF + i] = dtv[t] * rc;
+                    const int64_t tokp = bi * ba.Lb + c0 + t - ba.tbase;
+                    ba.gth[(tokp * H + hi) * HALF + i] = dtv[t] * rc;
                     dth_acc += thv[t * PHS + i] * rc;
                 }
                 if (t == 0) rcar[i] += tot;
@@ -1458,6 +1513,15 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
         }
     }
 
+    if (!first_win) {
+        // dS, the angle-gradient carry and the bias sums go to the previous window
+        float *rs = ba.rst + bh * rstf;
+        for (int e = tid; e < N * P; e += NT) rs[e] = dSl[(e / P) * PS + e % P];
+        for (int i = tid; i < HALF; i += NT) rs[N * P + i] = rcar[i];
+#pragma unroll
+        for (int r = 0; r < R; ++r) rs[N * P + HALF + r * NT + tid] = sbacc[r * NT + tid];
+        return;
+    }
     // the chain's bias sums: lane group lg of wave w holds component lg of row tile
     // rt over channel 16 nt0 + lr (+ 64 for the high halves)
     {
@@ -1517,16 +1581,23 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_mfma_kernel(BwdArgs b
 //   d Braw = rs w dB - Braw rs^3 / N * sum_n(Braw w dB),   rs = 1 / sqrt(mean(Braw^2) + eps)
 // and the gain term Braw rs dB is kept per row for the column sums. The previous
 // token's rows (prev) read the per-head fold rows instead and have no C part.
+// Rows of the sequence are those of tokens tbase .. tbase + nt - 1 of every batch (all
+// tokens in one pass, a window's under the low-memory schedule); the per-head rows are
+// the window's (ba.Lb per batch), the raw rows and the outputs the sequence's.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void bwd_group_kernel(BwdArgs ba, bool prev, int64_t nrows, float *gWB,
-                                                             float *gWC, float *dBraw_out, float *dCraw_out) {
+__global__ __launch_bounds__(kThreads) void bwd_group_kernel(BwdArgs ba, bool prev, int64_t nrows, int64_t nt,
+                                                             float *gWB, float *gWC, float *dBraw_out,
+                                                             float *dCraw_out) {
     const ScanArgs &a = ba.f;
     const int N = (int)a.N;
     const int64_t R = a.R, H = a.H, G = a.G, hpg = H / G;
-    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (row >= nrows) return;  // a whole wave; the kernel has no barrier
+    const int64_t wrow = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (wrow >= nrows) return;  // a whole wave; the kernel has no barrier
     const int l = threadIdx.x & 63;
-    const int64_t r = row % R, bg = row / R, g = bg % G, bt = bg / G;
+    const int64_t r = wrow % R, bg = wrow / R, g = bg % G, btw = bg / G;
+    // (batch, token) of the per-head rows and of the sequence
+    const int64_t bt = prev ? btw : (btw / nt) * ba.Lb + btw % nt;
+    const int64_t row = prev ? wrow : (((btw / nt) * a.L + ba.tbase + btw % nt) * G + g) * R + r;
     const int n = 2 * l;
     const bool on = n < N;  // N is even
     const int nc = on ? n : 0;
@@ -1586,13 +1657,16 @@ __global__ __launch_bounds__(kThreads) void bwd_group_kernel(BwdArgs ba, bool pr
     }
 }
 
-// d theta[b,t,g,i] = sum over the heads of group g of the per-head terms
-__global__ __launch_bounds__(kThreads) void bwd_theta_kernel(BwdArgs ba, float *dtheta) {
+// d theta[b,t,g,i] = sum over the heads of group g of the per-head terms, for tokens
+// tbase .. tbase + nt - 1 of every batch (per-head rows as in bwd_group_kernel)
+__global__ __launch_bounds__(kThreads) void bwd_theta_kernel(BwdArgs ba, int64_t nt, float *dtheta) {
     const ScanArgs &a = ba.f;
     const int64_t half = a.N / 2, H = a.H, G = a.G, hpg = H / G;
-    const int64_t total = a.b * a.L * G * half;
+    const int64_t total = a.b * nt * G * half;
     for (int64_t e = blockIdx.x * (int64_t)kThreads + threadIdx.x; e < total; e += (int64_t)gridDim.x * kThreads) {
-        const int64_t i = e % half, g = (e / half) % G, bt = e / (half * G);
+        const int64_t i = e % half, g = (e / half) % G, btw = e / (half * G);
+        const int64_t bt = (btw / nt) * ba.Lb + btw % nt;
+        const int64_t out = ((((btw / nt) * a.L + ba.tbase + btw % nt) * G + g) * half) + i;
         const float *src = ba.gth + (bt * H + g * hpg) * half + i;
         float s = 0.f;
         int64_t h = 0;
@@ -1604,7 +1678,7 @@ __global__ __launch_bounds__(kThreads) void bwd_theta_kernel(BwdArgs ba, float *
             for (int k = 0; k < 8; ++k) s += v[k];
         }
         for (; h < hpg; ++h) s += src[h * half];
-        dtheta[e] = s;
+        dtheta[out] = s;
     }
 }
 
@@ -1719,34 +1793,75 @@ hipError_t launch_chain(const BwdArgs &ba, int64_t chains, size_t smem, hipStrea
 
 }  // namespace
 
-size_t scan_bwd_workspace_bytes(const ScanArgs &a, int64_t *nsplit_out) {
+// Workspace layout, in one pass or under the low-memory schedule (lowmem: the
+// matrix-core chain shapes only). The window of the low-memory schedule, k chunks,
+// minimises nch/k checkpoints plus k recomputed states plus k chunks of per-head
+// partials: k = sqrt(nch S / (S + Pc)) with S the bytes of one checkpoint of every
+// chain and Pc those of one chunk's partials.
+struct BwdLayout {
+    int wchunks = 0, nwin = 1;
+    int64_t Lw = 0;  // tokens per batch of the per-head partial rows
+    size_t chk = 0, chkw = 0, rst = 0, gB = 0, gC = 0, gth = 0, tok = 0, gBp = 0, fold = 0, bpart = 0, gWB = 0,
+           gWC = 0, part = 0, total = 0;
+    int64_t nsplit = 64;
+};
+
+static BwdLayout bwd_layout(const ScanArgs &a, bool lowmem) {
     const BwdDims d = bwd_dims(a.L, a.N, a.P, a.R);
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const int64_t chains = a.b * a.H;
     const int64_t rowsBC = a.b * a.L * a.G * a.R;  // raw B / C rows
     const int64_t rows_prev = a.b * a.G * a.R;
     const int64_t cols_max = (a.H * a.R * a.N > a.N) ? a.H * a.R * a.N : a.N;
-    const int64_t nsplit = 64;
-    if (nsplit_out) *nsplit_out = nsplit;
-    size_t s = 0;
-    s += al(sizeof(float) * chains * (d.nch + 1) * d.slot);      // checkpoints
-    s += 2 * al(sizeof(float) * a.b * a.L * a.H * a.R * a.N);    // gB, gC
-    s += al(sizeof(float) * a.b * a.L * a.H * (a.N / 2));        // gth
-    s += al(sizeof(float) * a.b * a.L * a.H * 4);                // tok
-    s += al(sizeof(float) * chains * a.R * a.N);                 // gBp
-    s += al(sizeof(float) * chains);                             // fold
-    s += al(sizeof(float) * chains * 2 * a.R * 2 * a.N);         // bpart
-    s += 2 * al(sizeof(float) * (rowsBC + rows_prev) * a.N);     // gWB, gWC
-    s += al(sizeof(float) * nsplit * cols_max);                  // column-sum partials
-    return s;
+    BwdLayout y;
+    y.Lw = a.L;
+    int64_t nslots = d.nch + 1;
+    if (lowmem && d.nch > 0) {
+        const double S = 4.0 * chains * d.slot;
+        const double Pc = 4.0 * a.b * d.Cb * a.H * (2.0 * a.R * a.N + a.N / 2);
+        int64_t k = (int64_t)(sqrt((double)d.nch * S / (S + Pc)) + 0.5);
+        k = k < 1 ? 1 : (k > d.nch ? d.nch : k);
+        y.wchunks = (int)k;
+        y.nwin = (int)((d.nch + k - 1) / k);
+        y.Lw = k * d.Cb < a.L ? k * d.Cb : a.L;
+        nslots = y.nwin + 1;
+    }
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += al(bytes);
+        return o;
+    };
+    y.chk = take(sizeof(float) * chains * nslots * d.slot);  // checkpoints
+    if (y.wchunks > 0) {
+        y.chkw = take(sizeof(float) * chains * (y.wchunks + 1) * d.slot);          // a window's states
+        y.rst = take(sizeof(float) * chains * (a.N * a.P + a.N / 2 + 4 * kChainThreads));  // between windows
+    }
+    y.gB = take(sizeof(float) * a.b * y.Lw * a.H * a.R * a.N);
+    y.gC = take(sizeof(float) * a.b * y.Lw * a.H * a.R * a.N);
+    y.gth = take(sizeof(float) * a.b * y.Lw * a.H * (a.N / 2));
+    y.tok = take(sizeof(float) * a.b * a.L * a.H * 4);
+    y.gBp = take(sizeof(float) * chains * a.R * a.N);
+    y.fold = take(sizeof(float) * chains);
+    y.bpart = take(sizeof(float) * chains * 2 * a.R * 2 * a.N);
+    y.gWB = take(sizeof(float) * (rowsBC + rows_prev) * a.N);
+    y.gWC = take(sizeof(float) * (rowsBC + rows_prev) * a.N);
+    y.part = take(sizeof(float) * y.nsplit * cols_max);  // column-sum partials
+    y.total = off;
+    return y;
 }
 
-hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, hipStream_t st) {
+bool scan_bwd_lowmem_ok(const ScanArgs &a) { return a.N == 128 && a.P == 64 && (a.R == 1 || a.R == 2 || a.R == 4); }
+
+size_t scan_bwd_workspace_bytes(const ScanArgs &a, bool lowmem) { return bwd_layout(a, lowmem).total; }
+
+int scan_bwd_windows(const ScanArgs &a, bool lowmem) { return bwd_layout(a, lowmem).nwin; }
+
+hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, bool lowmem, hipStream_t st) {
     if (a.b * a.H == 0) return hipSuccess;
     const BwdDims d = bwd_dims(a.L, a.N, a.P, a.R);
-    int64_t nsplit = 0;
-    scan_bwd_workspace_bytes(a, &nsplit);
-    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const BwdLayout y = bwd_layout(a, lowmem);
+    const int64_t nsplit = y.nsplit;
     const int64_t chains = a.b * a.H;
     const int64_t rowsBC = a.b * a.L * a.G * a.R;
     const int64_t rows_prev = a.b * a.G * a.R;
@@ -1758,60 +1873,86 @@ hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, hipStre
     ba.dx = io.dx;
     ba.dh0 = io.dh0;
     ba.dx_prev = io.dx_prev;
-    ba.chk = reinterpret_cast<float *>(p);
-    p += al(sizeof(float) * chains * (d.nch + 1) * d.slot);
-    ba.gB = reinterpret_cast<float *>(p);
-    p += al(sizeof(float) * a.b * a.L * a.H * a.R * a.N);
-    ba.gC = reinterpret_cast<float *>(p);
-    p += al(sizeof(float) * a.b * a.L * a.H * a.R * a.N);
-    ba.gth = reinterpret_cast<float *>(p);
-    p += al(sizeof(float) * a.b * a.L * a.H * (a.N / 2));
-    ba.tok = reinterpret_cast<float *>(p);
-    p += al(sizeof(float) * a.b * a.L * a.H * 4);
-    ba.gBp = reinterpret_cast<float *>(p);
-    p += al(sizeof(float) * chains * a.R * a.N);
-    ba.fold = reinterpret_cast<float *>(p);
-    p += al(sizeof(float) * chains);
-    ba.bpart = reinterpret_cast<float *>(p);
-    p += al(sizeof(float) * chains * 2 * a.R * 2 * a.N);
-    float *gWB = reinterpret_cast<float *>(p);
-    p += al(sizeof(float) * (rowsBC + rows_prev) * a.N);
-    float *gWC = reinterpret_cast<float *>(p);
-    p += al(sizeof(float) * (rowsBC + rows_prev) * a.N);
-    float *part = reinterpret_cast<float *>(p);
+    ba.chk = reinterpret_cast<float *>(p + y.chk);
+    ba.chkw = y.wchunks > 0 ? reinterpret_cast<float *>(p + y.chkw) : nullptr;
+    ba.rst = y.wchunks > 0 ? reinterpret_cast<float *>(p + y.rst) : nullptr;
+    ba.gB = reinterpret_cast<float *>(p + y.gB);
+    ba.gC = reinterpret_cast<float *>(p + y.gC);
+    ba.gth = reinterpret_cast<float *>(p + y.gth);
+    ba.tok = reinterpret_cast<float *>(p + y.tok);
+    ba.gBp = reinterpret_cast<float *>(p + y.gBp);
+    ba.fold = reinterpret_cast<float *>(p + y.fold);
+    ba.bpart = reinterpret_cast<float *>(p + y.bpart);
+    float *gWB = reinterpret_cast<float *>(p + y.gWB);
+    float *gWC = reinterpret_cast<float *>(p + y.gWC);
+    float *part = reinterpret_cast<float *>(p + y.part);
+    ba.Lb = y.Lw;
+    ba.tbase = 0;
+    ba.wchunks = y.wchunks;
+    ba.win = -1;
 
     hipError_t e;
-    const size_t smem = sizeof(float) * chain_smem_floats(d);
-    switch (a.R) {
-        case 1: e = launch_chain<1>(ba, chains, smem, st); break;
-        case 2: e = launch_chain<2>(ba, chains, smem, st); break;
-        case 3: e = launch_chain<3>(ba, chains, smem, st); break;
-        case 4: e = launch_chain<4>(ba, chains, smem, st); break;
-        default: e = hipErrorInvalidValue;
-    }
-    if (e != hipSuccess) return e;
-
-    auto group = [&](bool prv, int64_t rows, float *wb, float *wc, float *ob, float *oc) -> hipError_t {
+    auto group = [&](bool prv, int64_t rows, int64_t nt, float *wb, float *wc, float *ob, float *oc) -> hipError_t {
         if (rows == 0) return hipSuccess;
         const unsigned nb = (unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64));
         if (a.bf16)
-            hipLaunchKernelGGL(bwd_group_kernel<true>, dim3(nb), dim3(kThreads), 0, st, ba, prv, rows, wb, wc, ob, oc);
+            hipLaunchKernelGGL(bwd_group_kernel<true>, dim3(nb), dim3(kThreads), 0, st, ba, prv, rows, nt, wb, wc,
+                               ob, oc);
         else
-            hipLaunchKernelGGL(bwd_group_kernel<false>, dim3(nb), dim3(kThreads), 0, st, ba, prv, rows, wb, wc, ob, oc);
+            hipLaunchKernelGGL(bwd_group_kernel<false>, dim3(nb), dim3(kThreads), 0, st, ba, prv, rows, nt, wb, wc,
+                               ob, oc);
         return hipGetLastError();
     };
-    if ((e = group(false, rowsBC, gWB, gWC, io.dBraw, io.dCraw)) != hipSuccess) return e;
-    float *gWBp = gWB + rowsBC * a.N;
-    if (a.has_prev && a.L > 0 && (e = group(true, rows_prev, gWBp, nullptr, io.dBraw_prev, nullptr)) != hipSuccess)
-        return e;
-    {
-        const int64_t tot = a.b * a.L * a.G * (a.N / 2);
+    // the per-head sums of the tokens tbase .. tbase + nt - 1 (every batch)
+    auto reduce_tokens = [&](int64_t nt) -> hipError_t {
+        hipError_t e2 = group(false, a.b * nt * a.G * a.R, nt, gWB, gWC, io.dBraw, io.dCraw);
+        if (e2 != hipSuccess) return e2;
+        const int64_t tot = a.b * nt * a.G * (a.N / 2);
         const unsigned nb = (unsigned)((tot + kThreads - 1) / kThreads < 65536 ? (tot + kThreads - 1) / kThreads : 65536);
         if (tot > 0) {
-            hipLaunchKernelGGL(bwd_theta_kernel, dim3(nb), dim3(kThreads), 0, st, ba, io.dtheta);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(bwd_theta_kernel, dim3(nb), dim3(kThreads), 0, st, ba, nt, io.dtheta);
+            return hipGetLastError();
         }
+        return hipSuccess;
+    };
+    if (y.wchunks == 0) {
+        const size_t smem = sizeof(float) * chain_smem_floats(d);
+        switch (a.R) {
+            case 1: e = launch_chain<1>(ba, chains, smem, st); break;
+            case 2: e = launch_chain<2>(ba, chains, smem, st); break;
+            case 3: e = launch_chain<3>(ba, chains, smem, st); break;
+            case 4: e = launch_chain<4>(ba, chains, smem, st); break;
+            default: e = hipErrorInvalidValue;
+        }
+        if (e != hipSuccess) return e;
+        if ((e = reduce_tokens(a.L)) != hipSuccess) return e;
+    } else {
+        // low-memory schedule: the forward sweep keeps a checkpoint every wchunks chunks;
+        // then, last window first, each window's states are recomputed, its reverse sweep
+        // run and its per-head sums reduced before the next window reuses the buffers
+        auto chain = [&]() -> hipError_t {
+            switch (a.R) {
+                case 1: return launch_chain_mfma<1>(ba, chains, st);
+                case 2: return launch_chain_mfma<2>(ba, chains, st);
+                case 4: return launch_chain_mfma<4>(ba, chains, st);
+                default: return hipErrorInvalidValue;
+            }
+        };
+        ba.win = -1;
+        if ((e = chain()) != hipSuccess) return e;
+        for (int wdx = y.nwin - 1; wdx >= 0; --wdx) {
+            ba.win = wdx;
+            ba.tbase = (int64_t)wdx * y.wchunks * d.Cb;
+            const int64_t nt = a.L - ba.tbase < y.Lw ? a.L - ba.tbase : y.Lw;
+            if ((e = chain()) != hipSuccess) return e;
+            if ((e = reduce_tokens(nt)) != hipSuccess) return e;
+        }
+        ba.win = 0;
+        ba.tbase = 0;
     }
+    float *gWBp = gWB + rowsBC * a.N;
+    if (a.has_prev && a.L > 0 && (e = group(true, rows_prev, 1, gWBp, nullptr, io.dBraw_prev, nullptr)) != hipSuccess)
+        return e;
     // column sums: biases over (b, t) rows (plus the previous token's rows), gains over every raw row
     auto colsum = [&](const float *src, int64_t rows, const float *src2, int64_t rows2, int64_t cols,
                       float *dst) -> hipError_t {

@@ -76,7 +76,7 @@ def gpu_decode_fused(inp, shape, bf16_state=False, **kw):
     return o.float().cpu().numpy().astype(np.float64), h.float().cpu().numpy().astype(np.float64)
 
 
-def gpu_scan_bwd(inp, shape, dy, dh_final=None):
+def gpu_scan_bwd(inp, shape, dy, dh_final=None, **kw):
     """Prefill backward on the GPU; returns a dict of float64 arrays keyed like the inputs."""
     from state_space_sequence_amd import m3
     d = m3.to_device(inp, shape.io)
@@ -86,6 +86,6 @@ def gpu_scan_bwd(inp, shape, dy, dh_final=None):
     dhf = None if dh_final is None else torch.from_numpy(np.ascontiguousarray(dh_final, dtype=np.float32)).cuda()
     g = m3.scan_bwd(d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"], d["B_bias"],
                     d["C_bias"], dyt, eps=shape.eps, B_normw=d.get("B_normw"), C_normw=d.get("C_normw"),
-                    h0=d.get("h0"), x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"), dh_final=dhf)
+                    h0=d.get("h0"), x_prev=d.get("x_prev"), Braw_prev=d.get("Braw_prev"), dh_final=dhf, **kw)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy().astype(np.float64) for k, v in g.items()}

@@ -368,3 +368,21 @@ def test_shapes_beyond_one_launch_grid_are_refused(m3):
     assert m3.lib.m3_scan_fwd(ctypes.byref(toks), ctypes.byref(_fake_io(m3)), None, 0, None) == -2
     assert m3.lib.m3_expand_ranks(ctypes.byref(_shape(m3, batch=1 << 20, seqlen=1 << 21, rank=4)), 0x1000, 0x2000,
                                   0x3000, None) == -2
+
+
+def test_backward_low_memory_flag(m3):
+    LOW = m3.M3_FLAG_BWD_LOW_MEMORY
+    for R, C, cap in ((1, 64, 1.0e9), (4, 16, 1.4e9)):
+        full = m3.scan_bwd_workspace_bytes(_shape(m3, batch=8, nheads=64, seqlen=4096, rank=R, chunk=C))
+        low = m3.scan_bwd_workspace_bytes(_shape(m3, batch=8, nheads=64, seqlen=4096, rank=R, chunk=C, flags=LOW))
+        assert 0 < low < cap < full, (R, low, full)
+    # matrix-core chain shapes only
+    assert m3.scan_bwd_workspace_bytes(_shape(m3, dstate=64, headdim=32, flags=LOW)) == 0
+    io = _fake_io(m3)
+    assert _bwd(m3, _shape(m3, dstate=64, headdim=32, flags=LOW), io, _fake_grads(m3, io)) == -2
+    # a backward flag: the forward and its plan refuse it
+    s = _shape(m3, flags=LOW)
+    assert m3.lib.m3_scan_fwd(ctypes.byref(s), ctypes.byref(_fake_io(m3)), None, 0, None) == -1
+    assert m3.lib.m3_scan_workspace_bytes(ctypes.byref(s)) == 0
+    # still validated like the one-pass call: the workspace is checked
+    assert _bwd(m3, _shape(m3, rank=2, chunk=32, flags=LOW), io, _fake_grads(m3, io)) == -4

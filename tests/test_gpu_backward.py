@@ -101,3 +101,62 @@ def test_backward_prefill_1p5b_sampled(name, b, h):
         e = relerr(v, ref[k])
         say("  chain (%d,%d) d%-4s err %.2e" % (b, h, k, e))
         assert e < TOL_BWD, k
+
+
+LOWMEM = [
+    # (b, L, H, G, R, io, prev, h0, normw, dh_final, slow)
+    (2, 700, 3, 1, 1, "bf16", True, True, True, True, True),    # 22 chunks: several windows, ragged tail
+    (1, 301, 2, 1, 4, "f32", True, False, False, True, True),   # R = 4: 38 chunks of 8 tokens
+    (2, 77, 2, 1, 2, "f32", False, True, True, False, False),
+    (1, 5, 2, 1, 4, "bf16", True, True, False, True, False),     # one chunk, one window
+]
+
+
+@pytest.mark.parametrize("case", LOWMEM)
+def test_backward_low_memory_is_bit_identical(case):
+    """The windowed low-memory schedule (M3_FLAG_BWD_LOW_MEMORY) recomputes each
+    window's states from a checkpoint of the exact fp32 state and keeps every sum in
+    the same order: every gradient equals the one-pass result bit for bit."""
+    from state_space_sequence_amd import m3
+    b, L, H, G, R, io, prev, h0, normw, dhf, slow = case
+    shape = Shape(b, L, H, G, 64, 128, R, max(1, 64 // R), io)
+    say("low-memory backward", case)
+    inp = make_scan_inputs(shape, seed=57, slow_decay=slow, with_h0=h0, with_prev=prev, with_normw=normw)
+    dy, dh = upstream(shape, 58, dhf, io)
+    g1 = gpu_scan_bwd(inp, shape, dy, dh)
+    g2 = gpu_scan_bwd(inp, shape, dy, dh, low_memory=True)
+    s0 = m3.make_shape(b, L, H, G, 64, 128, R, max(1, 64 // R), m3.M3_BF16 if io == "bf16" else m3.M3_F32)
+    s1 = m3.make_shape(b, L, H, G, 64, 128, R, max(1, 64 // R), m3.M3_BF16 if io == "bf16" else m3.M3_F32,
+                       flags=m3.M3_FLAG_BWD_LOW_MEMORY)
+    say("  workspace %d -> %d bytes" % (m3.scan_bwd_workspace_bytes(s0), m3.scan_bwd_workspace_bytes(s1)))
+    assert set(g1) == set(g2)
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k
+
+
+def test_backward_low_memory_mimo4_1p5b_bit_identical():
+    """The full MIMO rank-4 b8 L4096 H64 backward, one pass and windowed (32 windows
+    of 16 chunks), compared bit for bit on the GPU; the windowed workspace is
+    about 1.3 GB against 18 GB."""
+    import torch
+    from state_space_sequence_amd import m3
+    from state_space_sequence_amd.inputs import WORKLOADS
+    shape = WORKLOADS["mimo4_prefill_1p5b"]
+    inp = make_scan_inputs(shape, seed=59)
+    d = m3.to_device(inp, shape.io)
+    del inp
+    dy, _ = upstream(shape, 60, False, "bf16")
+    dyt = torch.from_numpy(dy).cuda().to(torch.bfloat16)
+    del dy
+    args = (d["x"], d["Braw"], d["Craw"], d["dt"], d["A"], d["lam"], d["theta"], d["B_bias"], d["C_bias"], dyt)
+    g1 = m3.scan_bwd(*args, eps=shape.eps)
+    g2 = m3.scan_bwd(*args, eps=shape.eps, low_memory=True)
+    torch.cuda.synchronize()
+    s1 = m3.make_shape(shape.batch, shape.seqlen, shape.nheads, shape.ngroups, shape.headdim, shape.dstate,
+                       shape.rank, shape.chunk, m3.M3_BF16, flags=m3.M3_FLAG_BWD_LOW_MEMORY)
+    ws = m3.scan_bwd_workspace_bytes(s1)
+    say("windowed workspace %.2f GB" % (ws / 1e9))
+    assert ws < 1.5e9
+    for k in g1:
+        assert torch.isfinite(g1[k]).all(), k
+        assert torch.equal(g1[k], g2[k]), k
