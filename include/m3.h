@@ -91,10 +91,13 @@ typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
                                       from its checkpoint, its reverse sweep run and its
                                       per-head dB, dC, d theta sums reduced before the next
                                       window reuses the buffers. k minimises the workspace
-                                      (about sqrt of the chunk count). Same results, bit
+                                      (about sqrt of the chunk count); shape->nsegments > 0
+                                      asks for that many windows instead (fewer: less
+                                      launch overhead, more memory). Same results, bit
                                       for bit, for about one more forward sweep of time;
                                       m3_scan_bwd_workspace_bytes gives the smaller size
-                                      for a shape with this flag. */
+                                      for a shape with this flag. Without the flag the
+                                      backward ignores nsegments. */
 
 typedef struct {
     int64_t batch;     /* b >= 0 */

@@ -328,7 +328,7 @@ size_t m3_scan_bwd_workspace_bytes(const m3_shape *shape) {
     const bool lowmem = (shape->flags & M3_FLAG_BWD_LOW_MEMORY) != 0;
     if (shape->flags & ~(M3_FLAG_FORCE_GENERIC | M3_FLAG_BWD_LOW_MEMORY)) return 0;
     if (lowmem && !scan_bwd_lowmem_ok(a)) return 0;
-    return scan_bwd_workspace_bytes(a, lowmem);
+    return scan_bwd_workspace_bytes(a, lowmem, lowmem ? (int)shape->nsegments : 0);
 }
 
 m3_status m3_scan_bwd(const m3_shape *shape, const m3_scan_io *io, const m3_scan_grads *gr, void *workspace,
@@ -381,14 +381,15 @@ m3_status m3_scan_bwd(const m3_shape *shape, const m3_scan_io *io, const m3_scan
         return M3_OK;
     }
     if (lowmem && !scan_bwd_lowmem_ok(a)) return M3_ERR_UNSUPPORTED;
-    const size_t need = scan_bwd_workspace_bytes(a, lowmem);
+    const int windows = lowmem ? (int)s.nsegments : 0;
+    const size_t need = scan_bwd_workspace_bytes(a, lowmem, windows);
     if (workspace == nullptr || ws_bytes < need) return M3_ERR_WORKSPACE_TOO_SMALL;
     BwdIO bio{};
     bio.dy = gr->dy; bio.dh_final = gr->dh_final; bio.dx = gr->dx; bio.dBraw = gr->dBraw; bio.dCraw = gr->dCraw;
     bio.ddt = gr->ddt; bio.dA = gr->dA; bio.dlam = gr->dlam; bio.dtheta = gr->dtheta; bio.dB_bias = gr->dB_bias;
     bio.dC_bias = gr->dC_bias; bio.dB_normw = gr->dB_normw; bio.dC_normw = gr->dC_normw; bio.dh0 = gr->dh0;
     bio.dx_prev = gr->dx_prev; bio.dBraw_prev = gr->dBraw_prev;
-    e = launch_scan_bwd(a, bio, workspace, lowmem, hs);
+    e = launch_scan_bwd(a, bio, workspace, lowmem, windows, hs);
     return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 

@@ -73,11 +73,12 @@ struct BwdIO {
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
-hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, bool lowmem, hipStream_t s);
-// lowmem: the windowed low-memory schedule (shapes with scan_bwd_lowmem_ok only)
-size_t scan_bwd_workspace_bytes(const ScanArgs &a, bool lowmem);
+// lowmem: the windowed low-memory schedule (shapes with scan_bwd_lowmem_ok only), with
+// `windows` windows (0: the count that minimises the workspace)
+hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, bool lowmem, int windows, hipStream_t s);
+size_t scan_bwd_workspace_bytes(const ScanArgs &a, bool lowmem, int windows);
 bool scan_bwd_lowmem_ok(const ScanArgs &a);
-int scan_bwd_windows(const ScanArgs &a, bool lowmem);
+int scan_bwd_windows(const ScanArgs &a, bool lowmem, int windows);
 size_t scan_bwd_smem_bytes(const ScanArgs &a);
 hipError_t launch_scan_generic(const ScanArgs &a, hipStream_t s);
 hipError_t launch_scan_mfma(const ScanArgs &a, const SplitPlan &sp, hipStream_t s);

@@ -1806,7 +1806,7 @@ struct BwdLayout {
     int64_t nsplit = 64;
 };
 
-static BwdLayout bwd_layout(const ScanArgs &a, bool lowmem) {
+static BwdLayout bwd_layout(const ScanArgs &a, bool lowmem, int windows) {
     const BwdDims d = bwd_dims(a.L, a.N, a.P, a.R);
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const int64_t chains = a.b * a.H;
@@ -1820,6 +1820,7 @@ static BwdLayout bwd_layout(const ScanArgs &a, bool lowmem) {
         const double S = 4.0 * chains * d.slot;
         const double Pc = 4.0 * a.b * d.Cb * a.H * (2.0 * a.R * a.N + a.N / 2);
         int64_t k = (int64_t)(sqrt((double)d.nch * S / (S + Pc)) + 0.5);
+        if (windows > 0) k = (d.nch + windows - 1) / windows;  // the caller's window count
         k = k < 1 ? 1 : (k > d.nch ? d.nch : k);
         y.wchunks = (int)k;
         y.nwin = (int)((d.nch + k - 1) / k);
@@ -1853,14 +1854,16 @@ static BwdLayout bwd_layout(const ScanArgs &a, bool lowmem) {
 
 bool scan_bwd_lowmem_ok(const ScanArgs &a) { return a.N == 128 && a.P == 64 && (a.R == 1 || a.R == 2 || a.R == 4); }
 
-size_t scan_bwd_workspace_bytes(const ScanArgs &a, bool lowmem) { return bwd_layout(a, lowmem).total; }
+size_t scan_bwd_workspace_bytes(const ScanArgs &a, bool lowmem, int windows) {
+    return bwd_layout(a, lowmem, windows).total;
+}
 
-int scan_bwd_windows(const ScanArgs &a, bool lowmem) { return bwd_layout(a, lowmem).nwin; }
+int scan_bwd_windows(const ScanArgs &a, bool lowmem, int windows) { return bwd_layout(a, lowmem, windows).nwin; }
 
-hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, bool lowmem, hipStream_t st) {
+hipError_t launch_scan_bwd(const ScanArgs &a, const BwdIO &io, void *ws, bool lowmem, int windows, hipStream_t st) {
     if (a.b * a.H == 0) return hipSuccess;
     const BwdDims d = bwd_dims(a.L, a.N, a.P, a.R);
-    const BwdLayout y = bwd_layout(a, lowmem);
+    const BwdLayout y = bwd_layout(a, lowmem, windows);
     const int64_t nsplit = y.nsplit;
     const int64_t chains = a.b * a.H;
     const int64_t rowsBC = a.b * a.L * a.G * a.R;

@@ -359,12 +359,13 @@ def scan_bwd_workspace_bytes(shape: Shape) -> int:
 
 def scan_bwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, dy, *, eps=1e-5, B_normw=None,
              C_normw=None, h0=None, x_prev=None, Braw_prev=None, dh_final=None, want_dh0=True,
-             workspace=None, grads=None, low_memory=False, stream=None):
+             workspace=None, grads=None, low_memory=False, windows=0, stream=None):
     """Prefill backward (m3_scan_bwd): gradients of <dy, y> + <dh_final, h_final> with
     respect to the forward inputs (same tensors as scan_fwd). Returns a dict of fp32
     tensors named like the inputs (x, Braw, ..., h0, x_prev, Braw_prev when present).
     low_memory: the windowed schedule (M3_FLAG_BWD_LOW_MEMORY), same results in a
-    smaller workspace for about one more forward sweep of time."""
+    smaller workspace for about one more forward sweep of time; windows > 0 sets the
+    number of windows (0: the count that minimises the workspace)."""
     b, L, H, R, P = _dims5("x", x, 5)
     _, _, G, _, N = _dims5("Braw", Braw, 5)
     iot = _io_dtype(x)
@@ -375,7 +376,7 @@ def scan_bwd(x, Braw, Craw, dt, A, lam, theta, B_bias, C_bias, dy, *, eps=1e-5, 
                 x.get_device())
     _need("dy", dy)
     shape = make_shape(b, L, H, G, P, N, R, max(1, 64 // R), iot, eps,
-                       M3_FLAG_BWD_LOW_MEMORY if low_memory else 0)
+                       M3_FLAG_BWD_LOW_MEMORY if low_memory else 0, windows if low_memory else 0)
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
     if grads is None:

@@ -134,6 +134,19 @@ def test_backward_low_memory_is_bit_identical(case):
         assert np.array_equal(g1[k], g2[k]), k
 
 
+@pytest.mark.parametrize("windows", [1, 3, 22])
+def test_backward_low_memory_window_count(windows):
+    """A caller-chosen window count (shape nsegments with the flag): 22 chunks in 1,
+    3 (8 + 8 + 6 chunks) or 22 windows, all bit-identical to the one-pass result."""
+    shape = Shape(2, 700, 2, 1, 64, 128, 1, 64, "bf16")
+    inp = make_scan_inputs(shape, seed=61, slow_decay=True, with_h0=True, with_prev=True, with_normw=True)
+    dy, dh = upstream(shape, 62, True, "bf16")
+    g1 = gpu_scan_bwd(inp, shape, dy, dh)
+    g2 = gpu_scan_bwd(inp, shape, dy, dh, low_memory=True, windows=windows)
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k
+
+
 def test_backward_low_memory_mimo4_1p5b_bit_identical():
     """The full MIMO rank-4 b8 L4096 H64 backward, one pass and windowed (32 windows
     of 16 chunks), compared bit for bit on the GPU; the windowed workspace is
