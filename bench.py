@@ -628,26 +628,33 @@ def main():
             grads = m3.scan_bwd(*bargs, eps=sb.eps)
             shp = m3.make_shape(sb.batch, sb.seqlen, sb.nheads, sb.ngroups, sb.headdim, sb.dstate, sb.rank,
                                 sb.chunk, m3.M3_BF16, sb.eps)
-            wsb = m3.scan_bwd_workspace_bytes(shp)
-            wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
-            for _ in range(5):
-                m3.scan_bwd(*bargs, eps=sb.eps, grads=grads, workspace=wsp)
-            torch.cuda.synchronize()
-            reps = 15
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-            evs[0].record()
-            for k in range(reps):
-                m3.scan_bwd(*bargs, eps=sb.eps, grads=grads, workspace=wsp)
-                evs[k + 1].record()
-            torch.cuda.synchronize()
-            ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(reps))[reps // 2]
             bb = bwd_bytes(sb)
-            ent = {"tokens_per_s": round(sb.batch * sb.seqlen / (ms * 1e-3), 1), "ms": round(ms, 3),
-                   "hbm_frac": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bb,
-                   "workspace_bytes": wsb}
-            log(nm + "_backward", ent)
-            extra[nm + "_backward"] = ent
-            del db, dyb, grads, wsp
+            # one pass, then the windowed low-memory schedule (same gradients, bit for bit)
+            for low in (False, True):
+                shp = m3.make_shape(sb.batch, sb.seqlen, sb.nheads, sb.ngroups, sb.headdim, sb.dstate, sb.rank,
+                                    sb.chunk, m3.M3_BF16, sb.eps, m3.M3_FLAG_BWD_LOW_MEMORY if low else 0)
+                wsb = m3.scan_bwd_workspace_bytes(shp)
+                wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
+                for _ in range(5):
+                    m3.scan_bwd(*bargs, eps=sb.eps, grads=grads, workspace=wsp, low_memory=low)
+                torch.cuda.synchronize()
+                reps = 15
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+                evs[0].record()
+                for k in range(reps):
+                    m3.scan_bwd(*bargs, eps=sb.eps, grads=grads, workspace=wsp, low_memory=low)
+                    evs[k + 1].record()
+                torch.cuda.synchronize()
+                ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(reps))[reps // 2]
+                ent = {"tokens_per_s": round(sb.batch * sb.seqlen / (ms * 1e-3), 1), "ms": round(ms, 3),
+                       "hbm_frac": round(bb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes": bb,
+                       "workspace_bytes": wsb}
+                key = nm + ("_backward_low_memory" if low else "_backward")
+                log(key, ent)
+                extra[key] = ent
+                del wsp
+                torch.cuda.empty_cache()
+            del db, dyb, grads
             torch.cuda.empty_cache()
 
     cpu = None
