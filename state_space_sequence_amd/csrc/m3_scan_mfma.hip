@@ -115,6 +115,15 @@ __device__ __forceinline__ float sum_over_rows(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// A quad permute whose result is an operand rather than an addend: every lane has a
+// source, so no "old" value is materialised (an update with old = 0 costs a zeroing
+// move where the permute is not folded into an add).
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float x) {
+    static_assert(CTRL <= 0xFF, "quad permutes only");
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ float lane_value(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
@@ -764,12 +773,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                 float t;
                 // every lane of a group of R takes lane (group base + ro)
                 if constexpr (R == 4) {
-                    if (ro == 0) t = dpp_mov<0x00>(v);
-                    else if (ro == 1) t = dpp_mov<0x55>(v);
-                    else if (ro == 2) t = dpp_mov<0xAA>(v);
-                    else t = dpp_mov<0xFF>(v);
+                    if (ro == 0) t = quad_perm<0x00>(v);
+                    else if (ro == 1) t = quad_perm<0x55>(v);
+                    else if (ro == 2) t = quad_perm<0xAA>(v);
+                    else t = quad_perm<0xFF>(v);
                 } else {  // R == 2: quad_perm [ro, ro, 2 + ro, 2 + ro]
-                    t = ro == 0 ? dpp_mov<0xA0>(v) : dpp_mov<0xF5>(v);
+                    t = ro == 0 ? quad_perm<0xA0>(v) : quad_perm<0xF5>(v);
                 }
                 return __builtin_bit_cast(h2, __float_as_uint(t));
             }
