@@ -953,6 +953,9 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             // W_O Y SiLU(W_Z Z'); every lane of the token ends with the sum
             auto gate_block = [&](int pb, const f32x4 &yv) -> f32x4 {
                 if constexpr (FUSED) {
+                    // (no contraction: fused into the product, each rank-sum step took a
+                    // zeroed register, a DPP move and an FMA instead of one DPP add)
+#pragma clang fp contract(off)
                     const f32x4 wz = *reinterpret_cast<const f32x4 *>(&sm.fw[1][r_row][16 * pb + 4 * lg]);
                     const f32x4 wo = *reinterpret_cast<const f32x4 *>(&sm.fw[2][r_row][16 * pb + 4 * lg]);
                     f32x4 ov;
