@@ -629,10 +629,22 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             xf[0] = cr.xf[0];
             xf[1] = cr.xf[1];
         }
-        bf16x4 zf[4];
-        if constexpr (FUSED) {
+        // fused gate factor W_O SiLU(W_Z Z') of the row's token and rank at the lane's
+        // output columns (App. C), formed here, off the output stage's critical path
+        f32x4 gz[4];
+        if constexpr (FUSED && MODE != kPass1) {
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) zf[pb] = cr.zf[pb];
+            for (int pb = 0; pb < 4; ++pb) {
+                const f32x4 wz = *reinterpret_cast<const f32x4 *>(&sm.fw[1][r_row][16 * pb + 4 * lg]);
+                const f32x4 wo = *reinterpret_cast<const f32x4 *>(&sm.fw[2][r_row][16 * pb + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float zz = wz[j] * (float)cr.zf[pb][j];
+                    float gv = wo[j] * (zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz)));
+                    asm volatile("" : "+v"(gv));  // formed here, not sunk to its use
+                    gz[pb][j] = gv;
+                }
+            }
         }
         if constexpr (FUSED && MODE != kCorrect) {
             // rank expansion X = W_X (.) X' for this lane's rank (App. C), rounded
@@ -956,15 +968,9 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                     // (no contraction: fused into the product, each rank-sum step took a
                     // zeroed register, a DPP move and an FMA instead of one DPP add)
 #pragma clang fp contract(off)
-                    const f32x4 wz = *reinterpret_cast<const f32x4 *>(&sm.fw[1][r_row][16 * pb + 4 * lg]);
-                    const f32x4 wo = *reinterpret_cast<const f32x4 *>(&sm.fw[2][r_row][16 * pb + 4 * lg]);
                     f32x4 ov;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float zz = wz[j] * (float)zf[pb][j];
-                        const float silu = zz * __builtin_amdgcn_rcpf(1.f + __expf(-zz));
-                        ov[j] = group_sum<R>(wo[j] * yv[j] * silu);
-                    }
+                    for (int j = 0; j < 4; ++j) ov[j] = group_sum<R>(yv[j] * gz[pb][j]);
                     return ov;
                 } else {
                     return yv;
