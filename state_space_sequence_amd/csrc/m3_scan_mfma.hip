@@ -881,6 +881,10 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 
         __builtin_amdgcn_s_setprio(3);
         if constexpr (MODE != kPass1) {
+            // the stage with the wave index as a constant: the causal block structure
+            // is then straight-line code for each wave
+            auto stage_m = [&](auto wc) __attribute__((always_inline)) {
+                constexpr int w = decltype(wc)::value;
             // the correction pass has no input term: only the carried-state output
             bf16x8 pfr[2];
             if constexpr (MODE != kCorrect) {
@@ -1030,6 +1034,13 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 #pragma unroll
                     for (int pb = 0; pb < 4; ++pb) store_block(pb, v4[pb]);
                 }
+            }
+            };
+            switch (w) {
+                case 0: stage_m(std::integral_constant<int, 0>{}); break;
+                case 1: stage_m(std::integral_constant<int, 1>{}); break;
+                case 2: stage_m(std::integral_constant<int, 2>{}); break;
+                default: stage_m(std::integral_constant<int, 3>{}); break;
             }
             __syncthreads();  // B3: St and Bb reads done
             __builtin_amdgcn_s_setprio(0);
