@@ -587,6 +587,21 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
                                    G, H, cr);
     }
 
+    // lane constants of the diagonal mask block (lane: row t = 16w + lr, columns s = 16w + 4lg + j):
+    // 1 where s's token precedes t's, 1 where it is t's token, and the skip D on t's own entry.
+    // Kept across the loop: recomputed per chunk they cost a compare and a select each.
+    f32x4 mbef, msame, mskip;
+    {
+        const int lr0 = tid & 15, lg0 = (tid & 63) >> 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int sj = (4 * lg0 + j) / R, tj = lr0 / R;  // tokens relative to 16w / R
+            mbef[j] = sj < tj ? 1.f : 0.f;
+            msame[j] = sj == tj ? 1.f : 0.f;
+            mskip[j] = (4 * lg0 + j == lr0) ? dsk : 0.f;
+        }
+    }
+
     for (int64_t c = pos.c_begin; c < pos.c_end; ++c) {
         // Wave priorities by phase: the two workgroups of a CU share each SIMD and
         // are rarely in the same phase. Favouring the rotation (2) and the score,
@@ -904,7 +919,6 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             }
             // ---- mask: lane holds S^T[s = 16sb + 4lg + j][t = 16w + lr]
             // (all table reads first, no LDS wait inside the uniform branches below)
-            const int ttok = row / R;
             const float l2t = sm.l2cs[row], gmt = sm.gam[row], ft = sm.ftab[row];
             const f32x4 l2s = *reinterpret_cast<const f32x4 *>(&sm.l2cs[16 * w + 4 * lg]);
             const f32x4 ws = *reinterpret_cast<const f32x4 *>(&sm.wgt[16 * w + 4 * lg]);
@@ -913,14 +927,12 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             for (int sb = 0; sb < 3; ++sb)
                 tws[sb] = *reinterpret_cast<const f32x4 *>(&sm.tw[w > 0 ? w - 1 : 0][16 * sb + 4 * lg]);
             // diagonal block w: exp(cs_t - cs_s) w_s below the diagonal, gamma on it
-            f32x4 mdiag, dadd;
+            f32x4 mdiag;
+            const f32x4 dadd = mskip;  // the row's own entry
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int stok = (16 * w + 4 * lg + j) / R;
                 const float e = __builtin_amdgcn_exp2f(fminf(l2t - l2s[j], 0.f)) * ws[j];
-                const float before = (stok < ttok) ? 1.f : 0.f, same = (stok == ttok) ? 1.f : 0.f;
-                mdiag[j] = before * e + same * gmt;
-                dadd[j] = (4 * lg + j == lr) ? dsk : 0.f;  // the row's own entry
+                mdiag[j] = mbef[j] * e + msame[j] * gmt;
             }
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
