@@ -55,6 +55,12 @@ constexpr int kN = 128, kP = 64, kRows = 64, kHalf = 64;
 // one 16-byte fragment read touches on 8 different bank groups
 constexpr int kLdN = kN + 8;     // tiles with 128 columns (B_bar, state)
 constexpr int kLdR = kRows + 8;  // tiles with 64 columns (B_bar^T, X^T)
+
+// Column order of the B_bar^T and X^T tiles: rows 32m + 16h + 4g + j (h, j < 2, 4) sit at slot
+// 32m + 8g + 4h + j. A lane's K-slots of a 16x16x32 product against the score accumulators (rows
+// 32m + 4g + j and 32m + 16 + 4g + j) are then one 16-byte read; the state update reads the same
+// slots from both of its operands, so its K order only changes with the slot order.
+__device__ __forceinline__ constexpr int row_slot(int w, int lg) { return 32 * (w >> 1) + 8 * lg + 4 * (w & 1); }
 constexpr int kThreads = 256;
 constexpr int kCUs = 256;  // MI355X compute units: 2 resident workgroups each
 constexpr float kLog2e = 1.4426950408889634f;
@@ -177,8 +183,8 @@ __device__ __forceinline__ int exp_ceil(float m) {
 
 struct alignas(16) Smem {
     alignas(16) __bf16 Bb[kRows * kLdN];  // B_bar [row][n]
-    alignas(16) __bf16 Bt[kN * kLdR];     // B_bar * cst, [n][row]
-    alignas(16) __bf16 Xt[kP * kLdR];     // X, [p][row]
+    alignas(16) __bf16 Bt[kN * kLdR];     // B_bar * cst, [n][row slot] (row slots: row_slot())
+    alignas(16) __bf16 Xt[kP * kLdR];     // X, [p][row slot]
     alignas(16) __bf16 St[kP * kLdN];     // bf16 state, [p][n]
     alignas(16) float l2cs[kRows];        // per row: log2(e) * chunk-local cumulative log decay
     alignas(16) float wgt[kRows];         // per row: folded weight w of the row's token
@@ -751,7 +757,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             for (int pb = 0; pb < 4; ++pb) {
                 const f32x4 t = mfma(xf[pb >> 1], (pb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f});
                 const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
-                *reinterpret_cast<bf16x4 *>(&sm.Xt[(16 * pb + lr) * kLdR + 16 * w + 4 * lg]) = v;
+                *reinterpret_cast<bf16x4 *>(&sm.Xt[(16 * pb + lr) * kLdR + row_slot(w, lg)]) = v;
             }
         }
 
@@ -877,7 +883,7 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             for (int nb = 0; nb < 8; ++nb) {
                 const f32x4 t = mfma(bfr[nb >> 1], (nb & 1) ? e1 : e0, f32x4{0.f, 0.f, 0.f, 0.f}) * cs4;
                 const bf16x4 v = {(__bf16)t[0], (__bf16)t[1], (__bf16)t[2], (__bf16)t[3]};
-                *reinterpret_cast<bf16x4 *>(&sm.Bt[(16 * nb + lr) * kLdR + 16 * w + 4 * lg]) = v;
+                *reinterpret_cast<bf16x4 *>(&sm.Bt[(16 * nb + lr) * kLdR + row_slot(w, lg)]) = v;
             }
         }
         // the next chunk's token scalars (every wave read this chunk's before B1)
@@ -969,9 +975,8 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 #pragma unroll
                 for (int m2 = 0; m2 < 2; ++m2) {
                     if (2 * m2 <= w) {
-                        const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(&sm.Xt[p * kLdR + 32 * m2 + 4 * lg]);
-                        const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(&sm.Xt[p * kLdR + 32 * m2 + 16 + 4 * lg]);
-                        const bf16x8 xv = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                        // rows 32m2 + 4lg + j and 32m2 + 16 + 4lg + j: one read (row_slot)
+                        const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(&sm.Xt[p * kLdR + 32 * m2 + 8 * lg]);
                         yv = mfma(xv, pfr[m2], yv);
                     }
                 }
