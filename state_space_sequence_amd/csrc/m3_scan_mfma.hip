@@ -991,7 +991,13 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 #pragma clang fp contract(off)
                     f32x4 ov;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ov[j] = group_sum<R>(yv[j] * gz[pb][j]);
+                    for (int j = 0; j < 4; ++j) {
+                        // formed here by every lane: sunk into the writer's branch, the last
+                        // step had become a zeroed register, a DPP move and a separate add
+                        float t = group_sum<R>(yv[j] * gz[pb][j]);
+                        if constexpr (R > 1) asm volatile("" : "+v"(t));
+                        ov[j] = t;
+                    }
                     return ov;
                 } else {
                     return yv;
