@@ -168,6 +168,9 @@ __device__ __forceinline__ float lane_partner(float x) {
 // low bits go first, so every mirror pairing meets lanes that already hold equal sums
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
+    // No contraction: a caller's product fused into the first step had become a
+    // zeroed register, a DPP move and an FMA instead of one DPP add.
+#pragma clang fp contract(off)
     if constexpr (G >= 2) x += lane_partner<0>(x);
     if constexpr (G >= 4) x += lane_partner<1>(x);
     if constexpr (G >= 8) x += lane_partner<2>(x);
