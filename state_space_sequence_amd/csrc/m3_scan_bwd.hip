@@ -716,21 +716,29 @@ template <int K>
 __device__ __forceinline__ float shr(float v) {  // row_shr:K (lanes without a source in their row read 0)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + K, 0xf, 0xf, false));
 }
-// inclusive prefix sum over aligned groups of G lanes (G in {8, 16, 32}); ln = lane index
+// inclusive prefix sum over aligned groups of G lanes (G in {8, 16, 32}); ln = lane index.
+// A row shift gives 0 to the lanes without a source in their 16-lane row, so groups of
+// 16 or 32 need no mask and each step is one DPP add; groups of 8 mask the lanes whose
+// source lies in the other half of the row. (No contraction: a caller's product fused
+// into the first step would take that add apart.)
 template <int G>
 __device__ __forceinline__ float group_scan(float v, int ln) {
+#pragma clang fp contract(off)
     static_assert(G == 8 || G == 16 || G == 32, "groups of 8, 16 or 32 lanes");
-    const int q = ln & (G - 1);
-    float s;
-    s = shr<1>(v);
-    v += (q >= 1) ? s : 0.f;
-    s = shr<2>(v);
-    v += (q >= 2) ? s : 0.f;
-    s = shr<4>(v);
-    v += (q >= 4) ? s : 0.f;
     if constexpr (G >= 16) {
-        s = shr<8>(v);
-        v += (q >= 8) ? s : 0.f;
+        v += shr<1>(v);
+        v += shr<2>(v);
+        v += shr<4>(v);
+        v += shr<8>(v);
+    } else {
+        const int q = ln & (G - 1);
+        float s;
+        s = shr<1>(v);
+        v += (q >= 1) ? s : 0.f;
+        s = shr<2>(v);
+        v += (q >= 2) ? s : 0.f;
+        s = shr<4>(v);
+        v += (q >= 4) ? s : 0.f;
     }
     if constexpr (G >= 32)  // row_bcast:15 into rows 1 and 3
         v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
