@@ -687,12 +687,17 @@ __device__ __forceinline__ f4 mfma4(f4 a, f4 b, f4 c) {
 __device__ __forceinline__ f4 ld_str(const float *p, int stride) {
     return f4{p[0], p[stride], p[2 * stride], p[3 * stride]};
 }
-// sum over the 16 lanes of a DPP row; lane 15 of each row ends with the total
+// sum over the 16 lanes of a DPP row; lane 15 of each row ends with the total. Every
+// step is one DPP add: no contraction (a caller's product fused into the first step
+// took it apart), and the total is formed by every lane (callers keep lane 15's inside
+// a branch, into which the last add had been sunk as a move and a separate add).
 __device__ __forceinline__ float row_sum16(float v) {
+#pragma clang fp contract(off)
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
+    asm volatile("" : "+v"(v));
     return v;
 }
 
