@@ -238,6 +238,7 @@ __device__ __forceinline__ ChainPos chain_of_block(const ScanArgs &a, const Spli
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: Hillis-Steele
 // inside each 16-lane row, then the row totals carried by row broadcasts.
 __device__ __forceinline__ float wave_incl_scan(float v) {
+#pragma clang fp contract(off)  // a caller's product fused into the first step takes its DPP add apart
     v += dpp_row_shr(v, 1);
     v += dpp_row_shr(v, 2);
     v += dpp_row_shr(v, 4);
@@ -760,6 +761,10 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
             for (int sh = R; sh < 16; sh <<= 1)
 #pragma unroll
                 for (int k = 0; k < 4 * NB; ++k) ph[k] += dpp_row_shr(ph[k], sh);
+            // formed here by every lane: the last step had been placed in the join of the
+            // branch below, as a zeroed register, a DPP move and a separate add
+#pragma unroll
+            for (int k = 0; k < 4 * NB; ++k) asm volatile("" : "+v"(ph[k]));
         }
         if (lr >= 16 - R) {  // the wave's last token: its rank lanes hold every block
 #pragma unroll
