@@ -1252,7 +1252,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
 // (token, group, rank) row instead of once per head that reads it:
 // u = x / sqrt(mean(x^2) + eps) times the gain, scaled by 2^-eg with
 // max |g| <= 2^eg, stored as f16 pairs (n, n + N/2) -- the rotation's operand
-// layout. 16 lanes per row, lane k taking pairs 4k..4k+3; blockIdx.y is 0 for B
+// layout. 16 lanes per row, lane k taking pairs 4k..4k+3, 4 rows per pass; blockIdx.y is 0 for B
 // and 1 for C. Every row of both outputs is written.
 __global__ __launch_bounds__(256) void bcnorm_pairs_kernel(const __bf16 *Bm, const __bf16 *Cm, const float *gB,
                                                            const float *gC, float eps, int64_t rows, unsigned *qB,
@@ -1275,24 +1275,34 @@ __global__ __launch_bounds__(256) void bcnorm_pairs_kernel(const __bf16 *Bm, con
     const float sc = ldexpf(1.f, -max(0, exp_ceil(m)));
     gl *= sc;
     gh *= sc;
-    for (int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); r < rows; r += (int64_t)gridDim.x * 16) {
-        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(src + r * kN + 4 * k);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(src + r * kN + kHalf + 4 * k);
-        float ss = 0.f;
+    // 4 rows per 16-lane group and pass: their loads go out together (indices clamped
+    // into the rows; a row past the end is computed and not stored)
+    constexpr int RP = 4;
+    for (int64_t r0 = (int64_t)blockIdx.x * 16 * RP + (threadIdx.x >> 4); r0 < rows; r0 += (int64_t)gridDim.x * 16 * RP) {
+        bf16x4 lo[RP], hi[RP];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float a = (float)lo[j], b = (float)hi[j];
-            ss = __builtin_fmaf(a, a, __builtin_fmaf(b, b, ss));
+        for (int q = 0; q < RP; ++q) {
+            const int64_t r = r0 + 16 * q < rows ? r0 + 16 * q : rows - 1;
+            lo[q] = *reinterpret_cast<const bf16x4 *>(src + r * kN + 4 * k);
+            hi[q] = *reinterpret_cast<const bf16x4 *>(src + r * kN + kHalf + 4 * k);
         }
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 16);
-        const float rs = __builtin_amdgcn_rsqf(ss * (1.f / kN) + eps);
-        u32x4 out;
+        for (int q = 0; q < RP; ++q) {
+            float ss = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            out[j] = __builtin_bit_cast(
-                unsigned, h2{(_Float16)((float)lo[j] * rs * gl[j]), (_Float16)((float)hi[j] * rs * gh[j])});
-        *reinterpret_cast<u32x4 *>(dst + r * kHalf + 4 * k) = out;
+            for (int j = 0; j < 4; ++j) {
+                const float a = (float)lo[q][j], b = (float)hi[q][j];
+                ss = __builtin_fmaf(a, a, __builtin_fmaf(b, b, ss));
+            }
+            ss = group_sum<16>(ss);  // the row's 16 lanes (DPP)
+            const float rs = __builtin_amdgcn_rsqf(ss * (1.f / kN) + eps);
+            u32x4 out;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                out[j] = __builtin_bit_cast(
+                    unsigned, h2{(_Float16)((float)lo[q][j] * rs * gl[j]), (_Float16)((float)hi[q][j] * rs * gh[j])});
+            if (r0 + 16 * q < rows) *reinterpret_cast<u32x4 *>(dst + (r0 + 16 * q) * kHalf + 4 * k) = out;
+        }
     }
 }
 
@@ -1408,7 +1418,7 @@ hipError_t launch_scan_mfma(const ScanArgs &a, const SplitPlan &sp, hipStream_t 
     if (a.b * a.H == 0) return hipSuccess;
     const int64_t rows = a.b * a.L * a.G * a.R;
     if (rows > 0) {
-        const int64_t nb = (rows + 15) / 16;
+        const int64_t nb = (rows + 63) / 64;  // 64 rows per block of 256 (16 lanes a row, 4 rows each)
         hipLaunchKernelGGL(bcnorm_pairs_kernel, dim3((unsigned)(nb < 16384 ? nb : 16384), 2), dim3(256), 0, s,
                            static_cast<const __bf16 *>(a.Braw), static_cast<const __bf16 *>(a.Craw), a.B_normw,
                            a.C_normw, a.eps, rows, a.Bq, a.Cq);
