@@ -1182,17 +1182,28 @@ __global__ __launch_bounds__(kThreads, 2) void scan_mfma_kernel(ScanArgs a, Spli
 // Chain the segment end states: H_in[0] = h0 (+ fold of the previous token);
 // H_in[k+1] = exp(D_k) R(Phi_k) H_in[k] + E_k. Overwrites E_k with H_in[k]; with
 // write_final, H_in[nseg] (the state after the last token) goes to h_final.
+// kCombineSplit workgroups per chain, each kCombineRows rows p of the N x P state (a
+// thread two channel pairs); the end states of kCombineBurst segments are loaded at
+// once, since only the stores depend on the carried state. (One workgroup per chain
+// walking the segments one load round trip at a time had taken 34 us for 48 chains
+// of 21 segments.)
+constexpr int kCombineSplit = 8;
+constexpr int kCombineRows = kP / kCombineSplit;
+constexpr int kCombineBurst = 8;
 template <int R, bool FUSED>
 __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan sp, bool write_final) {
+    constexpr int KE = kCombineRows * kHalf / kThreads;  // channel pairs per thread
+    static_assert(KE * kThreads == kCombineRows * kHalf, "the rows of a part fill the workgroup");
     __shared__ float rsp[4];
     const int tid = threadIdx.x;
-    const int64_t chain = blockIdx.x;
+    const int64_t chain = blockIdx.x / kCombineSplit;
+    const int p0 = (int)(blockIdx.x % kCombineSplit) * kCombineRows;
     const int64_t bi = chain / a.H, hi = chain % a.H, g = hi / (a.H / a.G);
     const int i = tid % kHalf;  // this thread's rotation channel
-    float lo[16], hiv[16];
+    float lo[KE], hiv[KE];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int p = (tid + kThreads * k) / kHalf;
+    for (int k = 0; k < KE; ++k) {
+        const int p = p0 + (tid + kThreads * k) / kHalf;
         lo[k] = a.h0 ? a.h0[(chain * kP + p) * kN + i] : 0.f;
         hiv[k] = a.h0 ? a.h0[(chain * kP + p) * kN + i + kHalf] : 0.f;
     }
@@ -1210,8 +1221,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
         const float *bb = a.B_bias + (hi * R) * kN;
         const float wl = a.B_normw ? a.B_normw[i] : 1.f, wh = a.B_normw ? a.B_normw[i + kHalf] : 1.f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int p = (tid + kThreads * k) / kHalf;
+        for (int k = 0; k < KE; ++k) {
+            const int p = p0 + (tid + kThreads * k) / kHalf;
             float sl = 0.f, sh = 0.f;
             for (int r = 0; r < R; ++r) {
                 const float xv = prev_x<R, FUSED>(a, bi, hi, r, p);
@@ -1222,26 +1233,46 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(ScanArgs a, SplitPlan
             hiv[k] += f * sh;
         }
     }
-    for (int s = 0; s < sp.nseg; ++s) {
-        float *E = sp.seg_state + (chain * sp.nseg + s) * (kP * kN);
-        const float dec = __expf(sp.seg_decay[chain * sp.nseg + s]);
-        float sn, cn;
-        sincos_rev(sp.seg_angle[(chain * sp.nseg + s) * kHalf + i], sn, cn);
+    float *const E0 = sp.seg_state + chain * sp.nseg * (int64_t)(kP * kN);
+    for (int s0 = 0; s0 < sp.nseg; s0 += kCombineBurst) {
+        // the burst's end states, decays and angles (indices clamped into the segments)
+        float el[kCombineBurst][KE], eh[kCombineBurst][KE], dec[kCombineBurst], ang[kCombineBurst];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int p = (tid + kThreads * k) / kHalf;
-            const float el = E[p * kN + i], eh = E[p * kN + i + kHalf];
-            E[p * kN + i] = lo[k];
-            E[p * kN + i + kHalf] = hiv[k];
-            const float u = lo[k], v = hiv[k];
-            lo[k] = dec * (cn * u - sn * v) + el;
-            hiv[k] = dec * (sn * u + cn * v) + eh;
+        for (int j = 0; j < kCombineBurst; ++j) {
+            const int sc = s0 + j < sp.nseg ? s0 + j : sp.nseg - 1;
+            const float *E = E0 + sc * (int64_t)(kP * kN);
+#pragma unroll
+            for (int k = 0; k < KE; ++k) {
+                const int p = p0 + (tid + kThreads * k) / kHalf;
+                el[j][k] = E[p * kN + i];
+                eh[j][k] = E[p * kN + i + kHalf];
+            }
+            dec[j] = sp.seg_decay[chain * sp.nseg + sc];
+            ang[j] = sp.seg_angle[(chain * sp.nseg + sc) * kHalf + i];
+        }
+#pragma unroll
+        for (int j = 0; j < kCombineBurst; ++j) {
+            if (s0 + j < sp.nseg) {
+                float *E = E0 + (s0 + j) * (int64_t)(kP * kN);
+                const float dc = __expf(dec[j]);
+                float sn, cn;
+                sincos_rev(ang[j], sn, cn);
+#pragma unroll
+                for (int k = 0; k < KE; ++k) {
+                    const int p = p0 + (tid + kThreads * k) / kHalf;
+                    E[p * kN + i] = lo[k];
+                    E[p * kN + i + kHalf] = hiv[k];
+                    const float u = lo[k], v = hiv[k];
+                    lo[k] = dc * (cn * u - sn * v) + el[j][k];
+                    hiv[k] = dc * (sn * u + cn * v) + eh[j][k];
+                }
+            }
         }
     }
     if (write_final && a.h_final) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int p = (tid + kThreads * k) / kHalf;
+        for (int k = 0; k < KE; ++k) {
+            const int p = p0 + (tid + kThreads * k) / kHalf;
             a.h_final[(chain * kP + p) * kN + i] = lo[k];
             a.h_final[(chain * kP + p) * kN + i + kHalf] = hiv[k];
         }
@@ -1322,7 +1353,8 @@ hipError_t launch_rw(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
                            sp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp, true);
+        hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)(chains * kCombineSplit)), dim3(kThreads), 0, s, a,
+                           sp, true);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((scan_mfma_kernel<kCorrect, R, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a,
@@ -1334,7 +1366,8 @@ hipError_t launch_rw(const ScanArgs &a, const SplitPlan &sp, hipStream_t s) {
     hipLaunchKernelGGL((scan_mfma_kernel<kPass1, R, FUSED, false>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)chains), dim3(kThreads), 0, s, a, sp, false);
+    hipLaunchKernelGGL((combine_kernel<R, FUSED>), dim3((unsigned)(chains * kCombineSplit)), dim3(kThreads), 0, s, a, sp,
+                       false);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((scan_mfma_kernel<kPass2, R, FUSED, ONORM>), dim3(nblk), dim3(kThreads), 0, s, a, sp);
