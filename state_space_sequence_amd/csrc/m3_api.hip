@@ -422,6 +422,7 @@ m3_status m3_decode_step(const m3_shape *shape, const m3_decode_io *io, void *st
     if (s.batch == 0) return M3_OK;
     DecodeArgs a{};
     a.b = s.batch; a.H = s.nheads; a.G = s.ngroups; a.P = s.headdim; a.N = s.dstate; a.R = s.rank;
+    a.hpg = s.nheads / s.ngroups;
     a.eps = s.eps; a.bf16 = (s.io_dtype == M3_BF16); a.has_prev = io->x_prev != nullptr;
     a.x = io->x; a.Braw = io->Braw; a.Craw = io->Craw; a.dt = io->dt; a.A = io->A; a.lam = io->lam;
     a.theta = io->theta; a.B_bias = io->B_bias; a.C_bias = io->C_bias; a.B_normw = io->B_normw;

@@ -195,9 +195,12 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     float *srn = sy + R * a.P;   // [R]      output norm: 1/rms per row
 
     const int tid = threadIdx.x;
-    const int64_t bh = blockIdx.x;
-    const int64_t bi = bh / a.H, hi = bh % a.H;
-    const int64_t g = hi / (a.H / a.G);
+    // 32-bit index arithmetic (the launcher keeps b H below 2^31): a 64-bit
+    // division by a run-time value is a long scalar sequence at the top of the kernel
+    const unsigned bhu = blockIdx.x, Hu = (unsigned)a.H;
+    const unsigned biu = bhu / Hu, hiu = bhu - biu * Hu;
+    const int64_t bh = bhu, bi = biu, hi = hiu;
+    const int64_t g = hiu / (unsigned)a.hpg;
     const int P = (int)a.P;
     const int q = tid % NQ;
     const int n0 = V * q;
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < N / SG; ++i) ss += spart[(j * R + r) * 4 + i];
-        return 1.0f / sqrtf(ss / (float)N + a.eps);
+        return __builtin_amdgcn_rsqf(ss * (1.0f / (float)N) + a.eps);  // v_rsq_f32, ~1 ulp
     };
 #pragma unroll
     for (int k = 0; k < EBC; ++k) {

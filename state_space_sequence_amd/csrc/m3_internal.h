@@ -53,6 +53,7 @@ struct DecodeArgs {
     void *o;
     const float *D, *out_normw;
     bool onorm, norm_after_gate;
+    int64_t hpg;  // heads per group, H / G
 };
 
 // Segment-split bookkeeping for the matrix-core prefill (state passing).
