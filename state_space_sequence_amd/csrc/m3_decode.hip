@@ -166,6 +166,38 @@ __device__ __forceinline__ typename StateT<BS, V>::type pack_state(const float *
     }
 }
 
+// io element i of a uniform base, and loads / stores at a 32-bit offset from it:
+// with the base in scalar registers and an unsigned offset the compiler can use
+// the scalar-base addressing form instead of a 64-bit vector add per access
+template <bool BF16>
+__device__ __forceinline__ const void *io_at(const void *p, int64_t i) {
+    if constexpr (BF16)
+        return static_cast<const uint16_t *>(p) + i;
+    else
+        return static_cast<const float *>(p) + i;
+}
+template <bool BF16>
+__device__ __forceinline__ void *io_at(void *p, int64_t i) {
+    if constexpr (BF16)
+        return static_cast<uint16_t *>(p) + i;
+    else
+        return static_cast<float *>(p) + i;
+}
+template <bool BF16>
+__device__ __forceinline__ float ld_io_u(const void *p, unsigned i) {
+    if constexpr (BF16)
+        return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+    else
+        return static_cast<const float *>(p)[i];
+}
+template <bool BF16>
+__device__ __forceinline__ void st_io_u(void *p, unsigned i, float v) {
+    if constexpr (BF16)
+        static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(v);
+    else
+        static_cast<float *>(p)[i] = v;
+}
+
 template <bool BF16, bool BS, int N, int R, int V, int KBATCH, bool ONORM>
 __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(DecodeArgs a) {
     constexpr int HALF = N / 2;
@@ -230,16 +262,18 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     const int64_t rowP = (bi * a.H + hi) * P;
     const bool hp = a.has_prev;
     const void *srcBp = hp ? a.Braw_prev : a.Braw;
+    const void *gB = io_at<BF16>(a.Braw, rowBC), *gC = io_at<BF16>(a.Craw, rowBC), *gBp = io_at<BF16>(srcBp, rowBC);
+    const float *gbb = a.B_bias + hi * R * N, *gcb = a.C_bias + hi * R * N;
     float rB[EBC], rC[EBC], rBp[EBC], rbb[EBC], rcb[EBC];
 #pragma unroll
     for (int k = 0; k < EBC; ++k) {
-        int e = tid + k * kThreads;
+        unsigned e = tid + k * kThreads;
         e = e < R * N ? e : R * N - 1;
-        rB[k] = ld_io<BF16>(a.Braw, rowBC + e);
-        rC[k] = ld_io<BF16>(a.Craw, rowBC + e);
-        rBp[k] = ld_io<BF16>(srcBp, rowBC + e);
-        rbb[k] = a.B_bias[hi * R * N + e];
-        rcb[k] = a.C_bias[hi * R * N + e];
+        rB[k] = ld_io_u<BF16>(gB, e);
+        rC[k] = ld_io_u<BF16>(gC, e);
+        rBp[k] = ld_io_u<BF16>(gBp, e);
+        rbb[k] = gbb[e];
+        rcb[k] = gcb[e];
     }
     const int en = tid < N ? tid : N - 1, ei = tid < HALF ? tid : HALF - 1;
     const float *pwb = a.B_normw ? a.B_normw : a.B_bias, *pwc = a.C_normw ? a.C_normw : a.C_bias;
@@ -251,35 +285,39 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     const int EXN = R * P;
     const int ex0 = tid < EXN ? tid : EXN - 1, ex1 = tid + kThreads < EXN ? tid + kThreads : EXN - 1;
     const void *srcXp = hp ? a.x_prev : a.x;
+    const void *gx = io_at<BF16>(a.x, a.fused ? rowP : rowX), *gxp = io_at<BF16>(srcXp, a.fused ? rowP : rowX);
     if (!a.fused) {
+        // the tables are stored rank-minor, [p][r], so one row's ranks are
+        // adjacent: thread element e of a table is x[r = e % R][p = e / R]
         float rx[2], rxp[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int e = k == 0 ? ex0 : ex1;
-            rx[k] = ld_io<BF16>(a.x, rowX + e);
-            rxp[k] = ld_io<BF16>(srcXp, rowX + e);
+            const unsigned e = k == 0 ? ex0 : ex1;
+            const unsigned src = (e % R) * P + e / R;
+            rx[k] = ld_io_u<BF16>(gx, src);
+            rxp[k] = ld_io_u<BF16>(gxp, src);
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int e = tid + k * kThreads;
             if (e < EXN) {
-                // stored rank-minor, [p][r], so one row's ranks are adjacent
-                const int r = e / P, pp = e % P;
-                sx[pp * R + r] = rx[k];
-                sxp[pp * R + r] = hp ? rxp[k] : 0.f;
+                sx[e] = rx[k];
+                sxp[e] = hp ? rxp[k] : 0.f;
             }
         }
     } else {
+        const void *gz = io_at<BF16>(a.z, rowP);
+        const float *gwx = a.W_X + hi * R * P, *gwz = a.W_Z + hi * R * P, *gwo = a.W_O + hi * R * P;
         float rx[2], rxp[2], rz[2], rwx[2], rwz[2], rwo[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int e = k == 0 ? ex0 : ex1, pp = e / R;
-            rx[k] = ld_io<BF16>(a.x, rowP + pp);
-            rxp[k] = ld_io<BF16>(srcXp, rowP + pp);
-            rz[k] = ld_io<BF16>(a.z, rowP + pp);
-            rwx[k] = a.W_X[hi * R * P + e];
-            rwz[k] = a.W_Z[hi * R * P + e];
-            rwo[k] = a.W_O[hi * R * P + e];
+            const unsigned e = k == 0 ? ex0 : ex1, pp = e / R;
+            rx[k] = ld_io_u<BF16>(gx, pp);
+            rxp[k] = ld_io_u<BF16>(gxp, pp);
+            rz[k] = ld_io_u<BF16>(gz, pp);
+            rwx[k] = gwx[e];
+            rwz[k] = gwz[e];
+            rwo[k] = gwo[e];
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -315,9 +353,9 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     // x elements past the first 2 * kThreads (R P > 512: large heads only)
     for (int e = tid + 2 * kThreads; e < EXN; e += kThreads) {
         if (!a.fused) {
-            const int r = e / P, pp = e % P;
-            sx[pp * R + r] = ld_io<BF16>(a.x, rowX + e);
-            sxp[pp * R + r] = a.has_prev ? ld_io<BF16>(a.x_prev, rowX + e) : 0.f;
+            const unsigned src = (e % R) * P + e / R;
+            sx[e] = ld_io_u<BF16>(gx, src);
+            sxp[e] = a.has_prev ? ld_io_u<BF16>(gxp, src) : 0.f;
         } else {
             const int pp = e / R;
             const float wx = a.W_X[hi * R * P + e];
@@ -386,6 +424,8 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
 
     // ---- stream the state rows
     const int64_t ybase = rowX;  // y has the x layout
+    void *gy = a.fused ? nullptr : io_at<BF16>(a.y, ybase);
+    void *go = a.fused ? io_at<BF16>(a.o, rowP) : nullptr;
     for (int kb = 0; kb < passes; kb += KB) {
         if (kb > 0) {
 #pragma unroll
@@ -454,7 +494,7 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
                     if (stage_o)
                         sy[p] = v;
                     else
-                        st_io<BF16>(a.o, (bi * a.H + hi) * P + p, v);
+                        st_io_u<BF16>(go, p, v);
                 }
             } else if constexpr (R == 2 || R == 4) {
                 // reduce-scatter over the NQ lanes of the row: at the top log2(R)
@@ -472,13 +512,13 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
                 if constexpr (LR == 2) scatter_step<LNQ - 2, 1>(vals, q);
                 const float v = tree_sum_low<LNQ - LR>(vals[0]);
                 const int rk = q / (NQ / R);
-                if (q % (NQ / R) == 0) st_io<BF16>(a.y, ybase + rk * P + p, v);
+                if (q % (NQ / R) == 0) st_io_u<BF16>(gy, rk * P + p, v);
             } else {
 #pragma unroll
                 for (int r = 0; r < R; ++r) yacc[r] = group_sum<NQ>(yacc[r]);
                 if (q == 0) {
 #pragma unroll
-                    for (int r = 0; r < R; ++r) st_io<BF16>(a.y, ybase + r * P + p, yacc[r]);
+                    for (int r = 0; r < R; ++r) st_io_u<BF16>(gy, r * P + p, yacc[r]);
                 }
             }
         }
