@@ -421,6 +421,23 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
         unpack<V>(*reinterpret_cast<const vec *>(sBp + r * N + n0), pl[r]);
         unpack<V>(*reinterpret_cast<const vec *>(sBp + r * N + HALF + n0), ph[r]);
     }
+    // R_t is linear, so R_t (alpha H + beta B_prev x_prev^T) = (alpha R_t) H +
+    // (R_t beta B_prev) x_prev^T: the rotation is folded into alpha (acs, asn) and
+    // into the beta B_prev columns once here, not applied per state element
+    float acs[V], asn[V];
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+        acs[c] = alpha * cs[c];
+        asn[c] = alpha * sn[c];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float u = pl[r][c], v = ph[r][c];
+            pl[r][c] = cs[c] * u - sn[c] * v;
+            ph[r][c] = sn[c] * u + cs[c] * v;
+        }
+    }
+    // the skip term D x enters the partial sums of each row's first lane only
+    const float dq = (q == 0) ? dsk : 0.f;
 
     // ---- stream the state rows
     const int64_t ybase = rowX;  // y has the x layout
@@ -456,24 +473,26 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
             // reduction below carries it
             float yacc[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) yacc[r] = (q == 0) ? dsk * xv[r] : 0.f;
+            for (int r = 0; r < R; ++r) yacc[r] = dq * xv[r];
 #pragma unroll
             for (int c = 0; c < V; ++c) {
-                float u = alpha * l[c], v = alpha * h[c];
-                float gu = 0.f, gv = 0.f;
+                // (l, h) <- alpha R_t (l, h) + (R_t beta B_prev) x_prev + gamma B x
+                float nu = acs[c] * l[c] - asn[c] * h[c];
+                float nv = asn[c] * l[c] + acs[c] * h[c];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    u += pl[r][c] * xpv[r];
-                    v += ph[r][c] * xpv[r];
-                    gu += bl[r][c] * xv[r];
-                    gv += bhc[r][c] * xv[r];
+                    nu += pl[r][c] * xpv[r];
+                    nv += ph[r][c] * xpv[r];
+                    nu += bl[r][c] * xv[r];
+                    nv += bhc[r][c] * xv[r];
                 }
-                const float nu = cs[c] * u - sn[c] * v + gu;
-                const float nv = sn[c] * u + cs[c] * v + gv;
                 l[c] = nu;
                 h[c] = nv;
 #pragma unroll
-                for (int r = 0; r < R; ++r) yacc[r] += cl[r][c] * nu + ch[r][c] * nv;
+                for (int r = 0; r < R; ++r) {
+                    yacc[r] += cl[r][c] * nu;
+                    yacc[r] += ch[r][c] * nv;
+                }
             }
             __builtin_nontemporal_store(pack_state<BS, V>(l), reinterpret_cast<svec *>(hbase + (int64_t)p * N + n0));
             __builtin_nontemporal_store(pack_state<BS, V>(h), reinterpret_cast<svec *>(hbase + (int64_t)p * N + HALF + n0));
