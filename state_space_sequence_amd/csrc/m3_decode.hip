@@ -215,12 +215,9 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     float *sB = sm;              // [R][N]   gamma * normalised B_t (+ bias)
     float *sC = sB + R * N;      // [R][N]   normalised C_t (+ bias)
     float *sBp = sC + R * N;     // [R][N]   beta * normalised B_{t-1} (+ bias)
-    float *swb = sBp + R * N;    // [N]      B gain (ones when absent)
-    float *swc = swb + N;        // [N]      C gain
-    float *scs = swc + N;        // [HALF]   cos
+    float *scs = sBp + R * N;    // [HALF]   cos
     float *ssn = scs + HALF;     // [HALF]   sin
-    float *spart = ssn + HALF;   // [3][R][4] BCNorm: sums of squares of row segments (B, C, B_prev)
-    float *sx = spart + 12 * R;  // [P][R]
+    float *sx = ssn + HALF;      // [P][R]
     float *sxp = sx + R * a.P;   // [P][R]
     float *sgt = sxp + R * a.P;  // [P][R]   fused: W_O SiLU(W_Z Z')
     float *sy = sgt + (a.fused ? R * a.P : 0);  // [R][P] output norm: rows before the norm
@@ -256,7 +253,12 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     // pointer (the value is masked afterwards), so that no load sits in a branch:
     // the compiler ends such a branch by waiting for its loads, and a load-then-
     // store loop per input had cost one memory round trip each.
-    constexpr int EBC = (R * N + kThreads - 1) / kThreads;  // B, C, bias elements per thread
+    // raw row r of B, C and B_prev (and the head's bias rows) belongs to wave r
+    // (R <= 4 waves), NE elements per lane, so BCNorm's sums are wave sums
+    constexpr int NE = (N + 63) / 64;
+    static_assert(R <= kThreads / 64, "one wave per rank row");
+    const int wv = tid / 64, ln = tid % 64;
+    const int rr = wv < R ? wv : 0;  // waves past R load row 0 and store nothing
     const int64_t rowBC = (bi * a.G + g) * R * N;
     const int64_t rowX = (bi * a.H + hi) * R * P;
     const int64_t rowP = (bi * a.H + hi) * P;
@@ -264,20 +266,21 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     const void *srcBp = hp ? a.Braw_prev : a.Braw;
     const void *gB = io_at<BF16>(a.Braw, rowBC), *gC = io_at<BF16>(a.Craw, rowBC), *gBp = io_at<BF16>(srcBp, rowBC);
     const float *gbb = a.B_bias + hi * R * N, *gcb = a.C_bias + hi * R * N;
-    float rB[EBC], rC[EBC], rBp[EBC], rbb[EBC], rcb[EBC];
-#pragma unroll
-    for (int k = 0; k < EBC; ++k) {
-        unsigned e = tid + k * kThreads;
-        e = e < R * N ? e : R * N - 1;
-        rB[k] = ld_io_u<BF16>(gB, e);
-        rC[k] = ld_io_u<BF16>(gC, e);
-        rBp[k] = ld_io_u<BF16>(gBp, e);
-        rbb[k] = gbb[e];
-        rcb[k] = gcb[e];
-    }
-    const int en = tid < N ? tid : N - 1, ei = tid < HALF ? tid : HALF - 1;
     const float *pwb = a.B_normw ? a.B_normw : a.B_bias, *pwc = a.C_normw ? a.C_normw : a.C_bias;
-    const float rwb0 = pwb[en], rwc0 = pwc[en];
+    float rB[NE], rC[NE], rBp[NE], rbb[NE], rcb[NE], rwb[NE], rwc[NE];
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+        const unsigned n = ln + 64 * j < N ? ln + 64 * j : N - 1;
+        const unsigned e = rr * N + n;
+        rB[j] = ld_io_u<BF16>(gB, e);
+        rC[j] = ld_io_u<BF16>(gC, e);
+        rBp[j] = ld_io_u<BF16>(gBp, e);
+        rbb[j] = gbb[e];
+        rcb[j] = gcb[e];
+        rwb[j] = pwb[n];
+        rwc[j] = pwc[n];
+    }
+    const int ei = tid < HALF ? tid : HALF - 1;
     const float rth = a.theta[(bi * a.G + g) * HALF + ei];
     const float d = a.dt[bh], Av = a.A[bh], lm = a.lam[bh];
     // x and x_prev, first 2 * kThreads of the R P elements (with the fused
@@ -331,23 +334,36 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
             }
         }
     }
-    const float rwb = a.B_normw ? rwb0 : 1.f, rwc = a.C_normw ? rwc0 : 1.f;
 
-    // ---- BCNorm sums of squares straight from the registers: row r holds the
-    // elements [rN, (r+1)N), and a segment of SG = min(N, 64) consecutive elements
-    // lies in one wave, so an SG-lane group sum is that segment's total
-    constexpr int SG = N < 64 ? N : 64;
+    // ---- BCNorm of the wave's rows: 1/rms from wave sums of the registers, then the
+    // per-column coefficients sB = gamma B_t, sBp = beta B_{t-1}, sC = C_t (all
+    // normalised, with gain and bias)
+    const float alpha = expf(d * Av);
+    const float beta = a.has_prev ? (1.0f - lm) * d * alpha : 0.f;
+    const float gamma = lm * d;
+    {
+        float qb = 0.f, qc = 0.f, qp = 0.f;
 #pragma unroll
-    for (int k = 0; k < EBC; ++k) {
-        const int e = tid + k * kThreads;
-        const bool ok = e < R * N;  // whole SG-lane groups (R N is a multiple of SG)
-        const float vb = ok ? rB[k] : 0.f, vc = ok ? rC[k] : 0.f, vp = ok ? rBp[k] : 0.f;
-        const float qb = group_sum<SG>(vb * vb), qc = group_sum<SG>(vc * vc), qp = group_sum<SG>(vp * vp);
-        if (ok && e % SG == 0) {
-            const int r = e / N, seg = (e % N) / SG;
-            spart[r * 4 + seg] = qb;
-            spart[(R + r) * 4 + seg] = qc;
-            spart[(2 * R + r) * 4 + seg] = qp;
+        for (int j = 0; j < NE; ++j) {
+            const bool ok = ln + 64 * j < N;
+            qb += ok ? rB[j] * rB[j] : 0.f;
+            qc += ok ? rC[j] * rC[j] : 0.f;
+            qp += ok ? rBp[j] * rBp[j] : 0.f;
+        }
+        const float rsb = __builtin_amdgcn_rsqf(wave_sum(qb) * (1.0f / (float)N) + a.eps);  // v_rsq_f32, ~1 ulp
+        const float rsc = __builtin_amdgcn_rsqf(wave_sum(qc) * (1.0f / (float)N) + a.eps);
+        const float rsp = __builtin_amdgcn_rsqf(wave_sum(qp) * (1.0f / (float)N) + a.eps);
+        if (wv < R) {
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const int n = ln + 64 * j;
+                if (n < N) {
+                    const float wb = a.B_normw ? rwb[j] : 1.f, wc = a.C_normw ? rwc[j] : 1.f;
+                    sB[wv * N + n] = gamma * (rB[j] * rsb * wb + rbb[j]);
+                    sC[wv * N + n] = rC[j] * rsc * wc + rcb[j];
+                    sBp[wv * N + n] = hp ? beta * (rBp[j] * rsp * wb + rbb[j]) : 0.f;
+                }
+            }
         }
     }
     // x elements past the first 2 * kThreads (R P > 512: large heads only)
@@ -365,10 +381,6 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
             sgt[e] = a.W_O[hi * R * P + e] * (zz / (1.f + expf(-zz)));
         }
     }
-    if (tid < N) {
-        swb[tid] = rwb;
-        swc[tid] = rwc;
-    }
     if (tid < HALF) {
         // the hardware sine and cosine take revolutions; reduce to [0, 1) first
         const float rev = __builtin_amdgcn_fractf(d * rth * 0.15915494309189535f);
@@ -383,29 +395,6 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
     // gate), or the gated and contracted O' (after the gate)
     const bool stage_ranks = ONORM && !(a.fused && a.norm_after_gate);
     const bool stage_o = ONORM && a.fused && a.norm_after_gate;
-    const float alpha = expf(d * Av);
-    const float beta = a.has_prev ? (1.0f - lm) * d * alpha : 0.f;
-    const float gamma = lm * d;
-
-    // ---- per-column coefficients, once per workgroup, from the registers:
-    // sB = gamma * B_t, sBp = beta * B_{t-1}, sC = C_t (all normalised + bias)
-    auto rs_of = [&](int j, int r) {  // 1/rms of row r of B (j = 0), C (1), B_prev (2)
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < N / SG; ++i) ss += spart[(j * R + r) * 4 + i];
-        return __builtin_amdgcn_rsqf(ss * (1.0f / (float)N) + a.eps);  // v_rsq_f32, ~1 ulp
-    };
-#pragma unroll
-    for (int k = 0; k < EBC; ++k) {
-        const int e = tid + k * kThreads;
-        if (e < R * N) {
-            const int r = e / N, n = e % N;
-            sB[e] = gamma * (rB[k] * rs_of(0, r) * swb[n] + rbb[k]);
-            sC[e] = rC[k] * rs_of(1, r) * swc[n] + rcb[k];
-            sBp[e] = hp ? beta * (rBp[k] * rs_of(2, r) * swb[n] + rbb[k]) : 0.f;
-        }
-    }
-    __syncthreads();
 
     // ---- this thread's columns: coefficients in registers
     float bl[R][V], bhc[R][V], cl[R][V], ch[R][V], pl[R][V], ph[R][V];
@@ -576,7 +565,7 @@ __global__ __launch_bounds__(kThreads, (R == 1 ? 7 : 5)) void decode_kernel(Deco
 
 template <bool BF16, bool BS, int N, bool ONORM>
 hipError_t launch_nn(const DecodeArgs &a, hipStream_t s) {
-    const size_t smem = sizeof(float) * (3 * a.R * N + 3 * N + 12 * a.R + (a.fused ? 3 : 2) * a.R * a.P +
+    const size_t smem = sizeof(float) * (3 * a.R * N + N + (a.fused ? 3 : 2) * a.R * a.P +
                                          (a.onorm ? a.R * a.P + a.R : 0));
     dim3 grid((unsigned)(a.b * a.H)), block(kThreads);
     switch (a.R) {
